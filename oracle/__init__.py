@@ -1,0 +1,173 @@
+"""CPU oracle for the TN GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` import this package.  The product library (``dense_gemm_tn_amd``)
+never imports it and shares no code with it: the arithmetic lives in
+``oracle.c`` (plain C, binary64, k ascending), built with gcc into
+``liboracle.so`` next to this file.
+
+Definitions followed (page, section):
+  * "hello-gpu, chapter 11 (GEMM-like)", section 11.1: C[m,n] = sum_k A[m,k] B[k,n]
+    with the partial sum starting at zero and k ascending (Fig. 11.1); no scaling,
+    transpose or addend.
+  * "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", section "What we compute":
+    A row-major M x K, B column-major (K contiguous per column), C column-major.
+  * FP8 inputs carry per-tensor scales; the oracle applies scale_a * scale_b to
+    the exact binary64 sum.
+
+Every function here has at least one pin in ``tests/test_oracle_pins.py`` that
+does not come from this code (the worked example of section 11.1, the rank-1
+partial sums of section 11.2, closed forms, exact rational sums, and library
+codecs).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+FMT_F16 = 0
+FMT_E4M3FN = 1
+FMT_BF16 = 2
+
+_ITEMSIZE = {FMT_F16: 2, FMT_BF16: 2, FMT_E4M3FN: 1}
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` with gcc into ``liboracle.so`` (no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(
+            ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-o", tmp, _SRC, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        i64 = ctypes.c_int64
+        vp = ctypes.c_void_p
+        lib.oracle_decode.argtypes = [ctypes.c_int, vp, vp, i64]
+        lib.oracle_encode.argtypes = [ctypes.c_int, vp, vp, i64]
+        lib.oracle_gemm_tn.argtypes = [ctypes.c_int, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                       ctypes.c_double, ctypes.c_int]
+        lib.oracle_gemm_tn_entries.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, vp, i64,
+                                               ctypes.c_double, vp]
+        for f in (lib.oracle_decode, lib.oracle_encode, lib.oracle_gemm_tn,
+                  lib.oracle_gemm_tn_entries):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _raw(arr: np.ndarray, fmt: int) -> np.ndarray:
+    """View an array of element codes as contiguous raw storage for ``fmt``."""
+    a = np.ascontiguousarray(arr)
+    want = np.uint8 if _ITEMSIZE[fmt] == 1 else np.uint16
+    if a.dtype == np.float16 and fmt == FMT_F16:
+        return a.view(np.uint16)
+    if a.dtype != want:
+        raise TypeError("fmt %d expects %s codes, got %s" % (fmt, want, a.dtype))
+    return a
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def decode(codes: np.ndarray, fmt: int) -> np.ndarray:
+    """Exact binary64 value of every element code."""
+    raw = _raw(codes, fmt)
+    out = np.empty(raw.shape, dtype=np.float64)
+    rc = _load().oracle_decode(fmt, _ptr(raw), _ptr(out), raw.size)
+    if rc:
+        raise ValueError("oracle_decode: bad format %d" % fmt)
+    return out
+
+
+def encode(values: np.ndarray, fmt: int) -> np.ndarray:
+    """Round binary64 values to ``fmt`` (nearest, ties to even); returns the codes."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint8 if _ITEMSIZE[fmt] == 1 else np.uint16)
+    rc = _load().oracle_encode(fmt, _ptr(v), _ptr(out), v.size)
+    if rc:
+        raise ValueError("oracle_encode: bad format %d" % fmt)
+    return out
+
+
+def gemm_tn(A: np.ndarray, B: np.ndarray, fmt: int, M: int, N: int, K: int,
+            lda: int | None = None, ldb: int | None = None, scale: float = 1.0,
+            nthreads: int | None = None) -> np.ndarray:
+    """binary64 C (column-major, returned as an [N, M] array: row n is column n of C).
+
+    A holds M rows of lda codes (row-major), B holds N columns of ldb codes
+    (column-major, i.e. K contiguous per column), both flat or shaped.
+    """
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ra = _raw(A, fmt).reshape(-1)
+    rb = _raw(B, fmt).reshape(-1)
+    if M and K and ra.size < (M - 1) * lda + K:
+        raise ValueError("A is too small for M, K, lda")
+    if N and K and rb.size < (N - 1) * ldb + K:
+        raise ValueError("B is too small for N, K, ldb")
+    C = np.zeros((N, M), dtype=np.float64)
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    rc = _load().oracle_gemm_tn(fmt, _ptr(ra), _ptr(rb), _ptr(C), M, N, K, lda, ldb, M,
+                                float(scale), int(nthreads))
+    if rc:
+        raise RuntimeError("oracle_gemm_tn failed with %d" % rc)
+    return C
+
+
+def gemm_tn_entries(A: np.ndarray, B: np.ndarray, fmt: int, K: int, ms, ns,
+                    lda: int | None = None, ldb: int | None = None,
+                    scale: float = 1.0) -> np.ndarray:
+    """binary64 values C[ms[i], ns[i]] of the same product, one by one."""
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ra = _raw(A, fmt).reshape(-1)
+    rb = _raw(B, fmt).reshape(-1)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    if ms.shape != ns.shape:
+        raise ValueError("ms and ns differ in shape")
+    if ms.size and (ms.min() < 0 or ns.min() < 0 or
+                    (ms.max() * lda + K) > ra.size or (ns.max() * ldb + K) > rb.size):
+        raise ValueError("entry index out of range")
+    out = np.empty(ms.shape, dtype=np.float64)
+    rc = _load().oracle_gemm_tn_entries(fmt, _ptr(ra), _ptr(rb), K, lda, ldb, _ptr(ms),
+                                        _ptr(ns), ms.size, float(scale), _ptr(out))
+    if rc:
+        raise RuntimeError("oracle_gemm_tn_entries failed with %d" % rc)
+    return out
+
+
+def batched_qkt(Q: np.ndarray, Kmat: np.ndarray, batch: int, M: int, N: int, D: int,
+                nthreads: int | None = None) -> np.ndarray:
+    """binary64 S_h = Q_h K_h^T per head, returned as [batch, N, M] (column-major S_h).
+
+    Q is [batch, M, D] and Kmat is [batch, N, D] fp16 (packed); K_h row-major N x D is
+    the K-contiguous B of the TN product, so S_h(i, j) = sum_d Q_h[i, d] K_h[j, d].
+    Source: the QK^T sketch on the mlqm.cn TileLang attention page (K = head dim).
+    """
+    q = np.ascontiguousarray(Q).reshape(batch, M * D)
+    k = np.ascontiguousarray(Kmat).reshape(batch, N * D)
+    out = np.empty((batch, N, M), dtype=np.float64)
+    for h in range(batch):
+        out[h] = gemm_tn(q[h], k[h], FMT_F16, M, N, D, nthreads=nthreads)
+    return out
