@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 TN GEMM on synthetic inputs resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME ...] [--no-cpu]
+
+A step is one launch of the GEMM over one set of inputs (A, B -> C).  Inputs
+are generated on the host with fixed seeds, copied to HBM before timing, and
+rotated over R buffer sets so the working set exceeds the 256 MB last-level
+cache (the method of the MI355X FP8 GEMM page: warm-up runs, timed runs,
+normally distributed data, rotating buffers).  W untimed steps, then exactly K
+timed steps bracketed by torch.cuda.synchronize(); HIP events recorded on the
+launch stream give the average kernel duration.  Throughput = 2*M*N*K per
+step / time (section 11.1 of the hello-gpu chapter counts a multiply-add as
+two flops).
+
+Prints ONE JSON line.  The headline `value` is the FP16 TN 4096^3 workload; the
+FP8 8192^3 workload (and any other requested one) is reported under
+"workloads" in the same line.  `roofline` is for the FP16 kernel; `traffic`
+comes from a stored rocprofv3 counter summary and is null when the kernel
+source changed after the counters were taken.  `cpu_baseline` times the CPU
+oracle on a bounded column sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s and % of dense MFMA peak: FP16 TN 4096^3, FP8 e4m3 8192^3"
+# Published MI355X dense peaks: 256 CUs x 2.4 GHz x 4096 (fp16) / 8192 (fp8) flop/clk/CU.
+PEAK_TFLOPS = {"f16": 2516.6, "qkt": 2516.6, "f8": 5033.2}
+HBM_PEAK_GBS = 8000.0
+KERNEL_NAME = {"f16": "gemm_tn_kernel<0>", "qkt": "gemm_tn_kernel<0>", "f8": "gemm_tn_kernel<1>"}
+SRC = os.path.join(ROOT, "dense_gemm_tn_amd", "csrc", "gemm_tn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def source_hash() -> str:
+    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(w) -> int:
+    """Read A and B once, write C once (the ideal-traffic model of section 11.6 of
+    the hello-gpu chapter, with 2-byte fp16 / 1-byte fp8 inputs and 2-byte outputs)."""
+    es = 1 if w.kind == "f8" else 2
+    return w.batch * ((w.M * w.K + w.N * w.K) * es + w.M * w.N * 2)
+
+
+def rotation_sets(w) -> int:
+    per_set = algorithmic_bytes(w)
+    return max(1, min(8, -(-512 * 2 ** 20 // per_set)))
+
+
+def make_launcher(w, dev):
+    """Inputs for R rotating sets and a function launching step i on the current stream."""
+    import numpy as np
+    import torch
+
+    import dense_gemm_tn_amd as dg
+    from dense_gemm_tn_amd import inputs
+
+    x = inputs.make(w)
+    R = rotation_sets(w)
+    sets = []
+    for r in range(R):
+        if w.kind == "qkt":
+            q = torch.from_numpy(x["Q"]).to(dev)
+            k = torch.from_numpy(x["K"]).to(dev)
+            s = torch.empty((w.batch, w.N, w.M), dtype=torch.float16, device=dev)
+            sets.append((q, k, s))
+        else:
+            a = torch.from_numpy(np.ascontiguousarray(x["A"])).to(dev)
+            b = torch.from_numpy(np.ascontiguousarray(x["B"])).to(dev)
+            cdt = torch.float16 if w.kind == "f16" else torch.bfloat16
+            c = torch.empty((w.N, w.M), dtype=cdt, device=dev)
+            sets.append((a, b, c))
+
+    def launch(i):
+        a, b, c = sets[i % R]
+        if w.kind == "f16":
+            dg.gemm_f16_tn(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M)
+        elif w.kind == "f8":
+            dg.gemm_f8_tn(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M, x["scale_a"], x["scale_b"])
+        else:
+            dg.gemm_batched_qkt(a, b, c, w.batch, w.M, w.N, w.K, w.K, w.K, w.M,
+                                w.M * w.K, w.N * w.K, w.M * w.N)
+
+    return x, sets, launch, R
+
+
+def time_workload(w, steps, warmup, dev):
+    import torch
+
+    x, sets, launch, R = make_launcher(w, dev)
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        launch(i)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = start.elapsed_time(stop)
+    kernel_s = ev_ms / 1e3 / steps
+    tflops = w.flops / kernel_s / 1e12
+    res = {
+        "M": w.M, "N": w.N, "K": w.K, "batch": w.batch, "kind": w.kind, "seed": w.seed,
+        "dist": w.dist, "rotating_sets": R,
+        "ms_per_step": ev_ms / steps,
+        "wall_ms_per_step": wall * 1e3 / steps,
+        "tflops": tflops,
+        "frac_of_peak": tflops / PEAK_TFLOPS[w.kind],
+        "hbm_gbs_algorithmic": algorithmic_bytes(w) / kernel_s / 1e9,
+    }
+    return res, x, sets
+
+
+def traffic_for(name, w, kernel_s):
+    """HBM bytes per launch from stored counter runs, if taken on this kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except ValueError:
+        return None
+    ent = t.get("workloads", {}).get(name)
+    if not ent or t.get("source_sha256_16") != source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, sets, target_s=12.0):
+    """The CPU oracle on a bounded sample: all M rows, full K, the first Ns columns
+    (Ns sized from a short probe so the timed run takes about target_s seconds).
+    Also reports the GPU's normwise error on that sample."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        threads = min(threads, int(env))
+    fmt = oracle.FMT_E4M3FN if w.kind == "f8" else oracle.FMT_F16
+    scale = float(x["scale_a"]) * float(x["scale_b"]) if w.kind == "f8" else 1.0
+    A = x["A"] if w.kind != "qkt" else x["Q"][0]
+    B = x["B"] if w.kind != "qkt" else x["K"][0]
+    probe_n = max(threads, 16)
+    t0 = time.perf_counter()
+    oracle.gemm_tn(A, B[:probe_n], fmt, w.M, probe_n, w.K, scale=scale, nthreads=threads)
+    dt = time.perf_counter() - t0
+    ns = int(min(w.N, max(probe_n, probe_n * target_s / max(dt, 1e-6))))
+    t0 = time.perf_counter()
+    ref = oracle.gemm_tn(A, B[:ns], fmt, w.M, ns, w.K, scale=scale, nthreads=threads)
+    dt = time.perf_counter() - t0
+    c = sets[0][2] if w.kind != "qkt" else sets[0][2][0]
+    got_codes = c[:ns].view(torch.int16).cpu().numpy().view(np.uint16)
+    got = oracle.decode(got_codes, oracle.FMT_BF16 if w.kind == "f8" else oracle.FMT_F16)
+    err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {
+        "value": 2.0 * w.M * ns * w.K / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%s: all %d rows x first %d of %d columns, full K=%d (%.1f%% of the work)%s; "
+                  "%.1f s" % (w.name, w.M, ns, w.N, w.K, 100.0 * ns / w.N,
+                              ", head 0 of %d" % w.batch if w.kind == "qkt" else "", dt),
+        "cpu_model": model,
+        "gpu_max_rel_err_on_sample": err,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", action="append", default=None,
+                    help="workload names (default: f16_4096 and f8_8192)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this GEMM build runs on a single MI355X; "
+              "--gpus %d is not supported (a multi-GPU run would shard N across GPUs with no "
+              "exchange, see the design notes)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from dense_gemm_tn_amd import inputs
+
+    dev = torch.device("cuda:0")
+    names = args.workload or ["f16_4096", "f8_8192"]
+    head = "f16_4096" if "f16_4096" in names else names[0]
+    results = {}
+    keep = {}
+    for name in names:
+        w = inputs.WORKLOADS[name]
+        res, x, sets = time_workload(w, args.steps, args.warmup, dev)
+        kernel_s = res["ms_per_step"] / 1e3
+        tb = traffic_for(name, w, kernel_s)
+        res["roofline"] = {
+            "bound": "hbm" if w.kind == "qkt" else "mfma",
+            "achieved": res["hbm_gbs_algorithmic"] if w.kind == "qkt" else res["tflops"],
+            "peak": HBM_PEAK_GBS if w.kind == "qkt" else PEAK_TFLOPS[w.kind],
+            "unit": "GB/s" if w.kind == "qkt" else "TFLOP/s",
+            "traffic": tb,
+            "kernel": KERNEL_NAME[w.kind],
+        }
+        r = res["roofline"]
+        r["frac"] = r["achieved"] / r["peak"]
+        results[name] = res
+        if name == head:
+            keep = {"w": w, "x": x, "sets": sets}
+        else:
+            del sets, x
+        torch.cuda.empty_cache()
+
+    hw = inputs.WORKLOADS[head]
+    hr = results[head]
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(keep["w"], keep["x"], keep["sets"])
+    line = {
+        "metric": METRIC,
+        "value": hr["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": hr["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if hw.kind != "f8" else "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": head, "M": hw.M, "N": hw.N, "K": hw.K, "batch": hw.batch,
+                   "layout": "TN (A row-major, B K-contiguous, C column-major ld=M)",
+                   "accumulate": "fp32", "inputs": hw.dist, "seed": hw.seed},
+        "frac_of_peak": hr["frac_of_peak"],
+        "roofline": {k: hr["roofline"][k] for k in
+                     ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "cpu_baseline": cpu,
+        "workloads": results,
+        "kernel_source_sha256_16": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

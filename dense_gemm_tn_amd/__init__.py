@@ -1,0 +1,175 @@
+"""Python binding of libdense_gemm_tn.so (gfx950 TN GEMM).
+
+Argument marshalling only: every step of the GEMM runs in the HIP kernels of
+``csrc/gemm_tn.hip`` behind the C ABI declared in ``include/dense_gemm_tn.h``.
+PyTorch supplies device memory and the current HIP stream.  If the library has
+not been built, every call raises -- there is no other code path.
+
+Layouts (TN, "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", section "What we
+compute"): A is row-major M x K (a [M, lda] tensor), B is column-major K x N,
+i.e. a [N, ldb] tensor whose row n is column n of B, and C is column-major
+M x N, i.e. a [N, ldc] tensor whose row n is column n of C.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdense_gemm_tn.so")
+
+DG_OK = 0
+DG_ERR_INVALID_ARGUMENT = 1
+DG_ERR_UNSUPPORTED = 2
+DG_ERR_HIP = 3
+
+EXPORTS = (
+    "gemm_f16_tn",
+    "gemm_f8_tn",
+    "gemm_batched_qkt",
+    "gemm_status_string",
+    "gemm_tile_order",
+    "gemm_block_tile",
+)
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (fn, status_string(status), status))
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libdense_gemm_tn.so is not built; run `python -m dense_gemm_tn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+        L.gemm_f16_tn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+        L.gemm_f8_tn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, vp]
+        L.gemm_batched_qkt.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                       i64, vp]
+        L.gemm_status_string.argtypes = [ctypes.c_int]
+        L.gemm_status_string.restype = ctypes.c_char_p
+        L.gemm_tile_order.argtypes = [i64, i64, i64, vp]
+        L.gemm_block_tile.argtypes = []
+        for f in (L.gemm_f16_tn, L.gemm_f8_tn, L.gemm_batched_qkt, L.gemm_tile_order,
+                  L.gemm_block_tile):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().gemm_status_string(int(status)).decode()
+
+
+def _ptr(x) -> int | None:
+    """Device address of a tensor, or an integer address passed through."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != DG_OK:
+        raise GemmError(fn, status)
+
+
+def gemm_f16_tn(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
+                stream=None) -> None:
+    """C[m + n*ldc] = sum_k A[m*lda + k] * B[n*ldb + k]   (fp16 in/out, fp32 accumulate)."""
+    _check("gemm_f16_tn", lib().gemm_f16_tn(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                                            _stream(stream)))
+
+
+def gemm_f8_tn(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
+               scale_a: float, scale_b: float, stream=None) -> None:
+    """C = bf16(fp32(scale_a*scale_b) * A x B) with E4M3FN A, B and fp32 accumulation."""
+    _check("gemm_f8_tn", lib().gemm_f8_tn(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                                          float(scale_a), float(scale_b), _stream(stream)))
+
+
+def gemm_batched_qkt(Q, Kmat, S, batch: int, M: int, N: int, D: int, ldq: int, ldk: int,
+                     lds: int, stride_q: int, stride_k: int, stride_s: int,
+                     stream=None) -> None:
+    """S_h[i + j*lds] = sum_d Q_h[i*ldq + d] * K_h[j*ldk + d] for every head h."""
+    _check("gemm_batched_qkt",
+           lib().gemm_batched_qkt(_ptr(Q), _ptr(Kmat), _ptr(S), batch, M, N, D, ldq, ldk, lds,
+                                  stride_q, stride_k, stride_s, _stream(stream)))
+
+
+def tile_order(tiles_m: int, tiles_n: int, batch: int = 1):
+    """(head, tile_m, tile_n) for every hardware block id, as a [G, 3] int64 numpy array."""
+    import numpy as np
+
+    out = np.empty((tiles_m * tiles_n * batch, 3), dtype=np.int64)
+    _check("gemm_tile_order", lib().gemm_tile_order(tiles_m, tiles_n, batch, out.ctypes.data))
+    return out
+
+
+def block_tile() -> int:
+    return lib().gemm_block_tile()
+
+
+# ----------------------------------------------------------- tensor helpers
+
+def matmul_tn_f16(a, b, out=None, stream=None):
+    """a: [M, K] fp16 (row-major A), b: [N, K] fp16 (column-major B) -> C as [N, M] fp16."""
+    import torch
+
+    M, K = a.shape
+    N, Kb = b.shape
+    if K != Kb or a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise ValueError("matmul_tn_f16 expects fp16 [M, K] and [N, K]")
+    if out is None:
+        out = torch.empty((N, M), dtype=torch.float16, device=a.device)
+    gemm_f16_tn(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), stream)
+    return out
+
+
+def matmul_tn_f8(a, b, scale_a: float, scale_b: float, out=None, stream=None):
+    """a: [M, K] uint8 E4M3FN codes, b: [N, K] codes -> C as [N, M] bf16."""
+    import torch
+
+    M, K = a.shape
+    N, Kb = b.shape
+    if K != Kb or a.element_size() != 1 or b.element_size() != 1:
+        raise ValueError("matmul_tn_f8 expects 1-byte [M, K] and [N, K]")
+    if out is None:
+        out = torch.empty((N, M), dtype=torch.bfloat16, device=a.device)
+    gemm_f8_tn(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), scale_a, scale_b,
+               stream)
+    return out
+
+
+def qkt(q, k, out=None, stream=None):
+    """q: [H, M, D], k: [H, N, D] fp16 -> S as [H, N, M] fp16 (S_h column-major)."""
+    import torch
+
+    H, M, D = q.shape
+    Hk, N, Dk = k.shape
+    if H != Hk or D != Dk:
+        raise ValueError("qkt expects [H, M, D] and [H, N, D]")
+    if out is None:
+        out = torch.empty((H, N, M), dtype=torch.float16, device=q.device)
+    gemm_batched_qkt(q, k, out, H, M, N, D, q.stride(1), k.stride(1), out.stride(1),
+                     q.stride(0), k.stride(0), out.stride(0), stream)
+    return out

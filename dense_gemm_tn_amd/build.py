@@ -1,0 +1,47 @@
+"""Build step for the gfx950 library: one hipcc call, in-tree output.
+
+    python -m dense_gemm_tn_amd.build
+
+compiles ``csrc/gemm_tn.hip`` into ``libdense_gemm_tn.so`` next to this file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "csrc", "gemm_tn.hip")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libdense_gemm_tn.so")
+
+HIPCC_FLAGS = [
+    "-O3",
+    "-std=c++17",
+    "--offload-arch=gfx950",
+    "-fPIC",
+    "-shared",
+    # Keep the compiler from forming packed fp32 instructions.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cand = os.path.join(rocm, "bin", "hipcc")
+    return cand if os.path.exists(cand) else "hipcc"
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)

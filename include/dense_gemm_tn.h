@@ -1,0 +1,124 @@
+/*
+ * dense_gemm_tn.h -- C ABI of libdense_gemm_tn.so, the gfx950 TN GEMM library.
+ *
+ * The operation (cited by page and section):
+ *   "hello-gpu, chapter 11 (GEMM-like)", section 11.1: C = A x B with
+ *   C[m,n] = sum over k of A[m,k] * B[k,n]; no scaling, transpose or addend.
+ *   "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", section "What we compute":
+ *   the TN pairing -- A is row-major M x K, B is column-major K x N (so both
+ *   operands are contiguous along K), and C is column-major.
+ *
+ * Storage, in elements (es = bytes per element):
+ *   A[m*lda + k]   m < M, k < K    (row-major, row stride lda >= K)
+ *   B[n*ldb + k]   n < N, k < K    (column n of B is K contiguous elements)
+ *   C[m + n*ldc]   m < M, n < N    (column-major, ldc >= M)
+ * Elements of A and B outside those index ranges are never read, and C is
+ * written only at those M*N positions: ldc padding and memory around C are
+ * left untouched (the tail rules of section 11.4 of the hello-gpu chapter:
+ * out-of-range operand elements contribute zero, out-of-range C is not written).
+ *
+ * Ownership and ordering:
+ *   All matrix pointers are DEVICE pointers on the current HIP device; the
+ *   caller allocates and owns them.  `stream` is a hipStream_t (NULL = the
+ *   default stream).  Each call validates its arguments on the host, enqueues
+ *   exactly one kernel on `stream` and returns without synchronising; results
+ *   are visible after the caller synchronises with the stream.  The library
+ *   allocates nothing, keeps no per-call state and is safe to call from
+ *   several host threads.  C must not overlap A or B.
+ *
+ * Errors (returned; nothing aborts):
+ *   DG_ERR_INVALID_ARGUMENT  null pointer with M, N > 0; negative size;
+ *                            lda or ldb < K; ldc < M; C overlapping A or B.
+ *   DG_ERR_UNSUPPORTED       K, lda or ldb not a multiple of the 16-byte
+ *                            vector (8 fp16 or 16 fp8 elements); A, B or C
+ *                            not 16-byte aligned; one 256-row operand strip
+ *                            spanning 2^31 bytes or more; more than 2^31-1
+ *                            tiles in the launch.
+ *   DG_ERR_HIP               the launch itself failed (hipGetLastError).
+ *   M == 0 or N == 0 is a successful no-op; K == 0 writes C := 0, the empty sum.
+ *   A fault inside the kernel surfaces at the caller's next synchronisation.
+ */
+#ifndef DENSE_GEMM_TN_H
+#define DENSE_GEMM_TN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DG_OK = 0,
+  DG_ERR_INVALID_ARGUMENT = 1,
+  DG_ERR_UNSUPPORTED = 2,
+  DG_ERR_HIP = 3
+} dg_status;
+
+/*
+ * FP16 TN GEMM: A, B and C are IEEE binary16.  Products are accumulated in
+ * fp32 on the matrix cores and each C element is rounded once, to nearest
+ * even, from the fp32 sum.
+ * Source: the FP16 GEMM of "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4",
+ * section "What we compute" (TN layouts).
+ */
+int gemm_f16_tn(const void *A, const void *B, void *C,
+                int64_t M, int64_t N, int64_t K,
+                int64_t lda, int64_t ldb, int64_t ldc,
+                void *stream);
+
+/*
+ * FP8 TN GEMM: A and B are OCP FP8 E4M3FN codes (one byte each) carrying the
+ * per-tensor fp32 scales scale_a and scale_b; C is bfloat16.
+ *   C[m + n*ldc] = bf16_rne( fp32(scale_a * scale_b) * sum_k a(m,k) * b(k,n) )
+ * with the sum accumulated in fp32 on the matrix cores.
+ * Source: the FP8 GEMM of "AMD ROCm 4-wave interleave FP8 GEMM for Instinct
+ * MI355X (CDNA 4)", sections "why 4 waves" and "interleave".
+ */
+int gemm_f8_tn(const void *A, const void *B, void *C,
+               int64_t M, int64_t N, int64_t K,
+               int64_t lda, int64_t ldb, int64_t ldc,
+               float scale_a, float scale_b,
+               void *stream);
+
+/*
+ * Strided-batched Q K^T (fp16 in, fp16 out, fp32 accumulate): for each head
+ * h < batch,
+ *   S[h*stride_s + j*lds + i] = sum_d Q[h*stride_q + i*ldq + d] * Kmat[h*stride_k + j*ldk + d]
+ * for i < M (query rows), j < N (key rows), d < D (head dim).  Q_h is the
+ * row-major A and K_h, row-major N x D, is exactly the K-contiguous B of the TN
+ * product, so S_h is column-major with leading dimension lds (>= M): seen as a
+ * row-major [N][lds] array it holds S_h transposed.  Swapping Q and Kmat (and
+ * M and N) gives the row-major S_h.
+ * Source: the QK^T kernel sketch of the mlqm.cn TileLang attention page
+ * (K dimension = head dim 128).  Strides are in elements; ldq, ldk >= D,
+ * lds >= M; the per-head regions of S must not overlap (stride_s >= lds*N
+ * when batch > 1), otherwise DG_ERR_INVALID_ARGUMENT.
+ */
+int gemm_batched_qkt(const void *Q, const void *Kmat, void *S,
+                     int64_t batch, int64_t M, int64_t N, int64_t D,
+                     int64_t ldq, int64_t ldk, int64_t lds,
+                     int64_t stride_q, int64_t stride_k, int64_t stride_s,
+                     void *stream);
+
+/* Static, NUL-terminated name of a dg_status value ("unknown status" otherwise). */
+const char *gemm_status_string(int status);
+
+/*
+ * Host-side view of the block -> tile order used by every kernel above (the
+ * grouped order of "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", Step 6,
+ * composed with the chiplet-aware remap of the MI355X FP8 GEMM page).  For a
+ * launch over `batch` heads of tiles_m x tiles_n tiles, writes for every
+ * hardware block id b the triple (head, tile_m, tile_n) to out[3*b .. 3*b+2].
+ * `out` is a HOST buffer of 3*batch*tiles_m*tiles_n int64 values.  Returns
+ * DG_ERR_INVALID_ARGUMENT for a null `out` or non-positive sizes.
+ */
+int gemm_tile_order(int64_t tiles_m, int64_t tiles_n, int64_t batch, int64_t *out);
+
+/* Output tile edge (rows and columns of C per block) used by the kernels. */
+int gemm_block_tile(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DENSE_GEMM_TN_H */

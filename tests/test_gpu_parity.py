@@ -1,0 +1,287 @@
+"""GPU path vs CPU oracle, element by element (gfx950, through the C ABI).
+
+Bars:
+  * +-1 inputs: bit-exact.  Every partial sum is an integer of magnitude <= K, so
+    the fp32 accumulation is exact in any order and the single rounding to the
+    output format is the oracle's ("FP16 GEMM optimisation on AMD RDNA 3 and
+    RDNA 4", section "What we compute", exact comparison on +-1 inputs).
+  * normal inputs: max|C - C_ref| / max|C_ref| <= 4e-3 for fp16 output and
+    <= 1e-2 for bf16 output (FP8 path), C_ref the unrounded binary64 oracle.
+  * memory around C and in the ldc padding is never written (section 11.4 of the
+    hello-gpu chapter: invalid C is not written).
+Shapes: the edge shapes of section 11.4 (K rounded up to the 16-byte vector),
+multi-tile ragged shapes, K tails, and the full-size workloads on sampled
+entries plus size-independent invariants.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_tn_amd as dg
+import oracle
+from dense_gemm_tn_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+CANARY16 = 0x7BCD  # a finite fp16 / bf16 pattern no kernel writes by accident
+F16_TOL = 4e-3
+BF16_TOL = 1e-2
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def _padded(src: np.ndarray, ld: int) -> np.ndarray:
+    """Rows of src placed in a wider row stride ld; the padding holds a nonzero
+    value (7.0 or the E4M3FN code of 1.0) that must never enter the sum."""
+    rows, cols = src.shape
+    fill = np.float16(7.0) if src.dtype == np.float16 else np.uint8(0x38)
+    out = np.full((rows, ld), fill, dtype=src.dtype)
+    out[:, :cols] = src
+    return out
+
+
+def run_gemm(kind, x, M, N, K, lda=None, ldb=None, ldc=None, guard=64):
+    """Launch through the C ABI with C inside a canary-filled allocation.
+
+    Returns (C as [N, M] uint16 codes, canary_ok)."""
+    lda = K if lda is None else lda
+    ldb = K if ldb is None else ldb
+    ldc = M if ldc is None else ldc
+    A = x["A"] if lda == K else _padded(x["A"], lda)
+    B = x["B"] if ldb == K else _padded(x["B"], ldb)
+    a = _dev(A.view(np.int16) if A.dtype == np.float16 else A)
+    b = _dev(B.view(np.int16) if B.dtype == np.float16 else B)
+    total = guard * 2 + max(N * ldc, 1)
+    c = torch.full((total,), CANARY16, dtype=torch.int32, device=DEV).to(torch.int16)
+    cptr = c.data_ptr() + guard * 2
+    if kind == "f16":
+        dg.gemm_f16_tn(a, b, cptr, M, N, K, lda, ldb, ldc)
+    else:
+        dg.gemm_f8_tn(a, b, cptr, M, N, K, lda, ldb, ldc, x["scale_a"], x["scale_b"])
+    torch.cuda.synchronize()
+    host = c.cpu().numpy().view(np.uint16)
+    body = host[guard:guard + N * ldc].reshape(N, ldc) if N else np.zeros((0, ldc), np.uint16)
+    ok = (np.all(host[:guard] == CANARY16) and np.all(host[guard + N * ldc:] == CANARY16)
+          and np.all(body[:, M:] == CANARY16))
+    return np.ascontiguousarray(body[:, :M]), ok
+
+
+def out_fmt(kind):
+    return oracle.FMT_F16 if kind in ("f16", "qkt") else oracle.FMT_BF16
+
+
+def in_fmt(kind):
+    return oracle.FMT_F16 if kind in ("f16", "qkt") else oracle.FMT_E4M3FN
+
+
+def reference(kind, x, M, N, K):
+    scale = float(x["scale_a"]) * float(x["scale_b"]) if kind == "f8" else 1.0
+    return oracle.gemm_tn(x["A"], x["B"], in_fmt(kind), M, N, K, scale=scale)
+
+
+def assert_exact(kind, got_codes, ref):
+    got = oracle.decode(got_codes, out_fmt(kind))
+    want = oracle.decode(oracle.encode(ref, out_fmt(kind)), out_fmt(kind))
+    bad = got != want
+    assert not bad.any(), "%d of %d elements differ; first at [n,m]=%s: got %r want %r" % (
+        bad.sum(), bad.size, np.argwhere(bad)[0], got[bad][0], want[bad][0])
+
+
+def normwise_error(kind, got_codes, ref):
+    got = oracle.decode(got_codes, out_fmt(kind))
+    assert np.all(np.isfinite(got))
+    denom = np.max(np.abs(ref))
+    return float(np.max(np.abs(got - ref)) / denom) if denom > 0 else float(np.max(np.abs(got)))
+
+
+# Edge shapes of section 11.4 (1x1x1, 3x5x7, 15x17x19, 17x19x23, 31x33x29) with K
+# rounded up to the 16-byte vector, plus multi-tile ragged shapes and K tails.
+EDGE = [(1, 1, 8), (3, 5, 8), (15, 17, 24), (17, 19, 24), (31, 33, 32)]
+EDGE8 = [(1, 1, 16), (3, 5, 16), (15, 17, 32), (17, 19, 32), (31, 33, 32)]
+RAGGED = [(256, 256, 256), (300, 290, 200), (257, 255, 72), (513, 260, 136), (64, 700, 64),
+          (700, 64, 1000), (1000, 1000, 8)]
+RAGGED8 = [(256, 256, 256), (300, 290, 208), (257, 255, 144), (513, 260, 112), (64, 700, 64),
+           (700, 64, 1008), (1000, 1000, 16)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE + RAGGED)
+@pytest.mark.parametrize("dist", ["pm1", "normal"])
+def test_f16_shapes(M, N, K, dist):
+    x = inputs.make_shape("f16", M, N, K, dist=dist, seed=M + N + K)
+    got, canary = run_gemm("f16", x, M, N, K)
+    assert canary
+    ref = reference("f16", x, M, N, K)
+    if dist == "pm1":
+        assert_exact("f16", got, ref)
+    else:
+        assert normwise_error("f16", got, ref) <= F16_TOL
+
+
+@pytest.mark.parametrize("M,N,K", EDGE8 + RAGGED8)
+@pytest.mark.parametrize("dist", ["pm1", "normal"])
+def test_f8_shapes(M, N, K, dist):
+    x = inputs.make_shape("f8", M, N, K, dist=dist, seed=M + N + K)
+    got, canary = run_gemm("f8", x, M, N, K)
+    assert canary
+    ref = reference("f8", x, M, N, K)
+    if dist == "pm1":
+        assert_exact("f8", got, ref)
+    else:
+        assert normwise_error("f8", got, ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("kind", ["f16", "f8"])
+def test_padded_leading_dimensions(kind):
+    M, N, K = 270, 300, 160
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=9)
+    got, canary = run_gemm(kind, x, M, N, K, lda=K + 32, ldb=K + 64, ldc=M + 10)
+    assert canary
+    assert_exact(kind, got, reference(kind, x, M, N, K))
+
+
+@pytest.mark.parametrize("kind", ["f16", "f8"])
+def test_odd_ldc_uses_narrow_stores(kind):
+    M, N, K = 37, 41, 64
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=10)
+    got, canary = run_gemm(kind, x, M, N, K, ldc=M + 3)
+    assert canary
+    assert_exact(kind, got, reference(kind, x, M, N, K))
+
+
+@pytest.mark.parametrize("kind", ["f16", "f8"])
+def test_k_zero_writes_zeros(kind):
+    M, N = 40, 30
+    x = {"A": np.zeros((M, 0), np.float16 if kind == "f16" else np.uint8),
+         "B": np.zeros((N, 0), np.float16 if kind == "f16" else np.uint8),
+         "scale_a": 1.0, "scale_b": 1.0}
+    got, canary = run_gemm(kind, x, M, N, 0, lda=16, ldb=16)
+    assert canary
+    assert np.all(oracle.decode(got, out_fmt(kind)) == 0)
+
+
+def test_identity_gives_exact_copy():
+    """A = I: C holds B exactly; B = I: C holds A transposed (special cases of 11.1)."""
+    n = 320
+    I = np.eye(n, dtype=np.float16)
+    rng = np.random.default_rng(0)
+    Bm = rng.standard_normal((300, n)).astype(np.float16)
+    got, ok = run_gemm("f16", {"A": I, "B": Bm}, n, 300, n)
+    assert ok and np.array_equal(got, Bm.view(np.uint16))
+    got, ok = run_gemm("f16", {"A": Bm, "B": I}, 300, n, n)
+    assert ok and np.array_equal(got, np.ascontiguousarray(Bm.T).view(np.uint16))
+
+
+def test_batched_qkt_small():
+    H, M, N, D = 3, 100, 70, 128
+    x = inputs.make_shape("qkt", M, N, D, dist="normal", seed=4, batch=H, std=128 ** -0.5)
+    q = _dev(x["Q"])
+    k = _dev(x["K"])
+    s = dg.qkt(q, k)
+    torch.cuda.synchronize()
+    ref = oracle.batched_qkt(x["Q"], x["K"], H, M, N, D)
+    got = s.view(torch.int16).cpu().numpy().view(np.uint16)
+    for h in range(H):
+        assert normwise_error("qkt", got[h], ref[h]) <= F16_TOL
+    # +-1 exact, and the swapped call gives the transposed (row-major) result
+    x = inputs.make_shape("qkt", M, N, D, dist="pm1", seed=5, batch=H)
+    q, k = _dev(x["Q"]), _dev(x["K"])
+    s = dg.qkt(q, k)
+    st = dg.qkt(k, q)
+    torch.cuda.synchronize()
+    ref = oracle.batched_qkt(x["Q"], x["K"], H, M, N, D)
+    got = s.view(torch.int16).cpu().numpy().view(np.uint16)
+    gott = st.view(torch.int16).cpu().numpy().view(np.uint16)
+    for h in range(H):
+        assert_exact("qkt", got[h], ref[h])
+        assert np.array_equal(gott[h], got[h].T)
+
+
+# ------------------------------------------------------------- full-size workloads
+
+def sample_entries(M, N, count, seed):
+    """Corners, tile edges and random entries of an M x N output."""
+    rng = np.random.default_rng(seed)
+    edges_m = sorted({0, 1, 15, 16, 127, 128, 255, 256, M // 2, M - 2, M - 1} & set(range(M)))
+    edges_n = sorted({0, 1, 15, 16, 127, 128, 255, 256, N // 2, N - 2, N - 1} & set(range(N)))
+    ms = [m for m in edges_m for _ in edges_n]
+    ns = [n for _ in edges_m for n in edges_n]
+    ms += list(rng.integers(0, M, count))
+    ns += list(rng.integers(0, N, count))
+    return np.asarray(ms, np.int64), np.asarray(ns, np.int64)
+
+
+def _full_size(name, dist=None, samples=3000):
+    w = inputs.WORKLOADS[name]
+    x = inputs.make(w, dist=dist)
+    got, canary = run_gemm(w.kind, x, w.M, w.N, w.K)
+    assert canary
+    ms, ns = sample_entries(w.M, w.N, samples, seed=1)
+    scale = float(x["scale_a"]) * float(x["scale_b"]) if w.kind == "f8" else 1.0
+    ref = oracle.gemm_tn_entries(x["A"], x["B"], in_fmt(w.kind), w.K, ms, ns, scale=scale)
+    return w, x, got, ms, ns, ref
+
+
+def test_c1_f16_256_pm1_exact_full():
+    w = inputs.WORKLOADS["f16_256_pm1"]
+    x = inputs.make(w)
+    got, canary = run_gemm("f16", x, w.M, w.N, w.K)
+    assert canary
+    assert_exact("f16", got, reference("f16", x, w.M, w.N, w.K))
+
+
+def test_c2_f16_4096_normal():
+    w, x, got, ms, ns, ref = _full_size("f16_4096")
+    g = oracle.decode(got[ns, ms], oracle.FMT_F16)
+    assert np.max(np.abs(g - ref)) / np.max(np.abs(ref)) <= F16_TOL
+    assert np.all(np.isfinite(oracle.decode(got, oracle.FMT_F16)))
+
+
+def test_c2_f16_4096_pm1_exact():
+    w, x, got, ms, ns, ref = _full_size("f16_4096", dist="pm1")
+    assert_exact("f16", got[ns, ms], ref)
+    vals = oracle.decode(got, oracle.FMT_F16)
+    assert np.all(np.abs(vals) <= w.K) and np.all((vals - w.K) % 2 == 0)
+
+
+def test_c3_f16_wide_ragged_normal():
+    w, x, got, ms, ns, ref = _full_size("f16_1920x13900x4096")
+    g = oracle.decode(got[ns, ms], oracle.FMT_F16)
+    assert np.max(np.abs(g - ref)) / np.max(np.abs(ref)) <= F16_TOL
+
+
+def test_c3_f16_wide_ragged_pm1_exact():
+    w, x, got, ms, ns, ref = _full_size("f16_1920x13900x4096_pm1")
+    assert_exact("f16", got[ns, ms], ref)
+    vals = oracle.decode(got, oracle.FMT_F16)
+    assert np.all(np.abs(vals) <= w.K) and np.all((vals - w.K) % 2 == 0)
+
+
+def test_c4_f8_8192_normal():
+    w, x, got, ms, ns, ref = _full_size("f8_8192", samples=1500)
+    g = oracle.decode(got[ns, ms], oracle.FMT_BF16)
+    assert np.max(np.abs(g - ref)) / np.max(np.abs(ref)) <= BF16_TOL
+
+
+def test_c4_f8_8192_pm1_exact():
+    w, x, got, ms, ns, ref = _full_size("f8_8192", dist="pm1", samples=1500)
+    assert_exact("f8", got[ns, ms], ref)
+
+
+def test_c5_batched_qkt_full():
+    w = inputs.WORKLOADS["qkt_64x4096x4096x128"]
+    x = inputs.make(w)
+    q, k = _dev(x["Q"]), _dev(x["K"])
+    s = dg.qkt(q, k)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    for h in sorted({0, 1, 31, 63} | set(rng.integers(0, w.batch, 4).tolist())):
+        ms, ns = sample_entries(w.M, w.N, 500, seed=h)
+        ref = oracle.gemm_tn_entries(x["Q"][h], x["K"][h], oracle.FMT_F16, w.K, ms, ns)
+        got = s[h].view(torch.int16).cpu().numpy().view(np.uint16)
+        g = oracle.decode(got[ns, ms], oracle.FMT_F16)
+        assert np.max(np.abs(g - ref)) / np.max(np.abs(ref)) <= F16_TOL
+    del s
+    torch.cuda.empty_cache()
