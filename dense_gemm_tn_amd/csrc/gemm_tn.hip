@@ -7,8 +7,12 @@
 //
 // Kernel design (one family, fp16 and fp8 instantiations, optional head index):
 //   * 256 x 256 output tile per workgroup, 4 waves (one per SIMD), each wave owns
-//     a 128 x 128 quarter held as 8 x 8 MFMA 16x16 accumulator tiles -- the
-//     4-wave layout of the MI355X FP8 GEMM page, section "why 4 waves".
+//     a 128 x 128 quarter held as 4 x 4 MFMA 32x32 accumulator tiles (256
+//     accumulator registers per lane) -- the 4-wave layout of the MI355X FP8
+//     GEMM page, section "why 4 waves".  The matrix-core shapes are
+//     v_mfma_f32_32x32x16_f16 and v_mfma_f32_32x32x64_f8f6f4: on gfx950 the
+//     32x32x16 fp16 shape retires twice the flops per cycle of 16x16x32 (measured
+//     with a register-only probe), and the fp8 shapes run at the same rate.
 //   * A K-step moves 128 bytes of K per row (64 fp16 or 128 fp8 elements):
 //     256 rows x 128 B of A and of B per stage, two stages in LDS (128 KiB).
 //   * Global -> LDS copies are buffer loads that write LDS directly (no VGPR
@@ -20,6 +24,11 @@
 //     c ^ ((r >> 1) & 7), the XOR swizzle of the MI355X FP8 GEMM page (section
 //     "XOR swizzle"), so the 16 rows read by one ds_read_b128 phase hit 16
 //     distinct 16-byte bank groups of the 256-byte bank period.
+//   * Fragments are software-pipelined in registers (the prefetch interleaving
+//     of "FP16 GEMM optimisation ...", Step 7, and the MFMA / ds_read
+//     interleave of the MI355X FP8 GEMM page): A fragments in a ring read two
+//     MFMA groups ahead, B fragments double-buffered per substep, one barrier
+//     per K-step placed mid-substep; sched_barrier pins the order.
 //   * Block ids are remapped so each XCD (workgroups are dealt round-robin over
 //     the 8 XCDs) receives a contiguous range of tiles, and that range is walked
 //     in the grouped order of "FP16 GEMM optimisation ...", Step 6 (groups of 8
@@ -36,19 +45,22 @@
 namespace dg {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t_v __attribute__((ext_vector_type(16)));
 typedef int int8_t_v __attribute__((ext_vector_type(8)));
 typedef int int4_t_v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(3))) uint8_t *lds_cptr;
 
 constexpr int kTile = 256;        // rows of A / columns of B per workgroup
-constexpr int kRowBytes = 128;    // bytes of K per row per K-step
+constexpr int kRowBytes = 64;     // bytes of K per row per K-step
+constexpr int kStages = 4;        // LDS ring of K-steps (copies run 3 steps ahead)
 constexpr int kThreads = 256;     // 4 waves of 64
 constexpr int kWaveTile = 128;    // each wave owns kWaveTile x kWaveTile of C
-constexpr int kSub = 8;           // 16x16 MFMA tiles per wave edge (128 / 16)
+constexpr int kMma = 32;          // MFMA output tile edge
+constexpr int kSub = 4;           // MFMA tiles per wave edge (128 / 32)
 constexpr int kXcds = 8;          // chiplets the dispatcher deals blocks over
 constexpr int kGroupM = 8;        // tile rows per group in the grouped order
-constexpr int kStageBytes = kTile * kRowBytes;   // 32 KiB per operand per stage
+constexpr int kStageBytes = kTile * kRowBytes;   // 16 KiB per operand per stage
 constexpr uint32_t kOob = 0x80000000u;           // an offset past every descriptor
 // Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts:
 // 32-bit data format so the hardware range-checks the byte offset.
@@ -59,27 +71,27 @@ enum Kind { kF16 = 0, kF8 = 1 };
 template <int KIND> struct Traits;
 template <> struct Traits<kF16> {
   static constexpr int es = 2;       // bytes per element
-  static constexpr int kstep = 64;   // K elements per K-step (128 B per row)
+  static constexpr int kstep = 32;   // K elements per K-step (64 B per row)
   static constexpr int reads = 1;    // 16-byte LDS reads per lane per MFMA operand
-  static constexpr int subs = 2;     // MFMA K sub-steps per K-step (32 each)
+  static constexpr int subs = 2;     // MFMA K sub-steps per K-step (16 deep each)
   typedef half8_t frag_t;
 };
 template <> struct Traits<kF8> {
   static constexpr int es = 1;
-  static constexpr int kstep = 128;
+  static constexpr int kstep = 64;
   static constexpr int reads = 2;    // 32 bytes of K per lane
-  static constexpr int subs = 1;     // one 16x16x128 MFMA covers the K-step
+  static constexpr int subs = 1;     // one 32x32x64 MFMA depth per K-step
   typedef int8_t_v frag_t;
 };
 
-__device__ __forceinline__ float4_t mma(const half8_t &a, const half8_t &b, float4_t c) {
-  // v_mfma_f32_16x16x32_f16: fp16 products, fp32 accumulate.
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ float16_t_v mma(const half8_t &a, const half8_t &b, float16_t_v c) {
+  // v_mfma_f32_32x32x16_f16: fp16 products, fp32 accumulate.
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ float4_t mma(const int8_t_v &a, const int8_t_v &b, float4_t c) {
-  // v_mfma_f32_16x16x128_f8f6f4 with both operand formats = 0 (FP8 E4M3) and
+__device__ __forceinline__ float16_t_v mma(const int8_t_v &a, const int8_t_v &b, float16_t_v c) {
+  // v_mfma_f32_32x32x64_f8f6f4 with both operand formats = 0 (FP8 E4M3) and
   // no block scales; the per-tensor scales are applied in the epilogue.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // Kernel arguments (one struct, passed by value).
@@ -94,6 +106,7 @@ struct Params {
   int32_t tiles_m, tiles_n;
   float scale;           // fp8 only: fp32(scale_a * scale_b)
   int32_t c_vec_ok;      // 8-byte C stores are aligned (ldc % 4 == 0)
+  int32_t c_vec16_ok;    // 16-byte C stores are aligned (ldc % 8 == 0)
 };
 
 // Block id -> (head, tile_m, tile_n).  First the chiplet remap: block b runs on
@@ -124,108 +137,155 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                            (int)kRsrcWord3);
 }
 
-// One K-step's copy of a 256-row operand strip into one LDS stage.  Load q of
-// wave w fills LDS rows 32q + 8w .. +7 (1 KiB, lane-contiguous: lane l writes
-// bytes l*16 .. l*16+15 of that KiB).  Lane l therefore lands in row
-// 32q + 8w + (l >> 3), slot l & 7, and fetches the global chunk that the
-// swizzle stores there.
-template <int ES>
-__device__ __forceinline__ void copy_stage(lds_void_t *stage, __amdgpu_buffer_rsrc_t rsrc,
-                                           uint32_t voff, uint32_t q_stride, bool chunk_valid,
-                                           int wave) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const uint32_t off = chunk_valid ? voff + q * q_stride : kOob;
-    lds_void_t *dst = (lds_void_t *)((__attribute__((address_space(3))) uint8_t *)stage +
-                                     q * 4096 + wave * 1024);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, off, 0, 0, 0);
+// Copies for one K-step: a 256-row x 64-byte strip of A and of B, each as four
+// wave-wide loads per wave.  Load q of wave w fills LDS rows 64q + 16w .. +15
+// of the strip (1 KiB, lane-contiguous: lane l writes bytes l*16 .. l*16+15 of
+// that KiB), so lane l lands in row 64q + 16w + (l >> 2), slot l & 3, and
+// fetches the global 16-byte chunk that the swizzle stores there (see the
+// kernel).  `voff` is the lane's offset for q = 0, or kOob for a K-step (or
+// K-tail chunk) that must read zeros; the host guarantees
+// kOob + 3 * q_stride < 2^32, so a zero-read offset stays out of range.
+struct StepCopy {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t va, vb;                          // lane offsets for q = 0
+  __attribute__((address_space(3))) uint8_t *la, *lb;  // LDS strip bases (+ wave KiB)
+};
+
+// Issue copy d (0..7) of a step: d < 4 is load q = d of A, else load q = d - 4 of B.
+__device__ __forceinline__ void copy_one(const StepCopy &c, int d, uint32_t qs_a, uint32_t qs_b) {
+  if (d < 4) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, (lds_void_t *)(c.la + d * 4096), 16,
+                                             c.va + d * qs_a, 0, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, (lds_void_t *)(c.lb + (d - 4) * 4096), 16,
+                                             c.vb + (d - 4) * qs_b, 0, 0, 0);
   }
 }
 
+// One MFMA operand fragment: 32 rows x (16 fp16 or 64 fp8) of K.  Lane l reads
+// row (l & 31) of the 32-row tile at `tile` and the 16-byte chunk(s) of its K
+// half (l >> 5); `off[s * reads + r]` holds the lane's swizzled byte offsets
+// (stage and wave offsets included) for substep s, read r.
 template <int KIND>
-__device__ __forceinline__ void load_frags(typename Traits<KIND>::frag_t (&f)[kSub],
-                                           const __attribute__((address_space(3))) uint8_t *base,
-                                           const uint32_t (&lane_off)[2], int s) {
-  typedef Traits<KIND> T;
+__device__ __forceinline__ typename Traits<KIND>::frag_t read_frag(lds_cptr tile,
+                                                                  const uint32_t (&off)[2],
+                                                                  int sub) {
+  if constexpr (Traits<KIND>::reads == 1) {
+    return *(const __attribute__((address_space(3))) half8_t *)(tile + off[sub]);
+  } else {
+    const int4_t_v lo = *(const __attribute__((address_space(3))) int4_t_v *)(tile + off[0]);
+    const int4_t_v hi = *(const __attribute__((address_space(3))) int4_t_v *)(tile + off[1]);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// s_waitcnt immediate for "at most n vector-memory operations outstanding"
+// (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at max).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int KIND>
+__device__ __forceinline__ void store_c(const Params &p, uint8_t *Cb,
+                                        const float16_t_v (&acc)[kSub][kSub], int64_t m_base,
+                                        int64_t n_base, int lane) {
+  // Accumulator tile (i, j), element e: lane l holds column (l & 31) and rows
+  // 8*(e >> 2) + 4*(l >> 5) + (e & 3), i.e. four runs of four consecutive
+  // elements of one column of the column-major C.
+  const int64_t m_lane = m_base + 4 * (lane >> 5);
+  const int64_t n_lane = n_base + (lane & 31);
+  const bool full = (m_base + kWaveTile <= p.M) && (n_base + kWaveTile <= p.N) && p.c_vec_ok;
 #pragma unroll
-  for (int i = 0; i < kSub; ++i) {
-    if constexpr (T::reads == 1) {
-      f[i] = *(const __attribute__((address_space(3))) half8_t *)(base + i * 16 * kRowBytes +
-                                                                  lane_off[s]);
-    } else {
-      int4_t_v lo = *(const __attribute__((address_space(3))) int4_t_v *)(base + i * 16 * kRowBytes +
-                                                                          lane_off[0]);
-      int4_t_v hi = *(const __attribute__((address_space(3))) int4_t_v *)(base + i * 16 * kRowBytes +
-                                                                          lane_off[1]);
-      f[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  for (int j = 0; j < kSub; ++j) {
+    const int64_t n = n_lane + kMma * j;
+#pragma unroll
+    for (int i = 0; i < kSub; ++i) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int64_t m = m_lane + kMma * i + 8 * b;
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (KIND == kF16) {
+            h[e] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][4 * b + e]);
+          } else {
+            h[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * b + e] * p.scale));
+          }
+        }
+        uint16_t *dst = (uint16_t *)Cb + (n * p.ldc + m);
+        uint2 w;
+        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        if (full) {
+          *(uint2 *)dst = w;
+        } else if (n < p.N) {
+          if (p.c_vec_ok && m + 3 < p.M) {
+            *(uint2 *)dst = w;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (m + e < p.M) dst[e] = h[e];
+          }
+        }
+      }
     }
   }
 }
 
+// Epilogue through LDS: the wave's 128 x 128 tile is converted to 16-bit
+// values and written column-major into the wave's own 32 KiB of LDS (column n
+// at n * 256 B, its 16-byte chunk c stored in slot c ^ (n & 15)), then read
+// back as 16 contiguous bytes (8 rows) per lane, so each global store
+// instruction writes four full 256-byte column segments of C.  Needs 16-byte
+// aligned columns (ldc % 8 == 0); rows or columns past M, N are masked.
 template <int KIND>
-__device__ __forceinline__ void compute_stage(float4_t (&acc)[kSub][kSub],
-                                              const __attribute__((address_space(3))) uint8_t *sa,
-                                              const __attribute__((address_space(3))) uint8_t *sb,
-                                              const uint32_t (&lane_off)[2]) {
-  typedef Traits<KIND> T;
-#pragma unroll
-  for (int s = 0; s < T::subs; ++s) {
-    typename T::frag_t a[kSub], b[kSub];
-    load_frags<KIND>(a, sa, lane_off, s);
-    load_frags<KIND>(b, sb, lane_off, s);
-#pragma unroll
-    for (int i = 0; i < kSub; ++i)
-#pragma unroll
-      for (int j = 0; j < kSub; ++j) acc[i][j] = mma(a[i], b[j], acc[i][j]);
-  }
-}
-
-template <int KIND>
-__device__ __forceinline__ void store_c(const Params &p, uint8_t *Cb, const float4_t (&acc)[kSub][kSub],
-                                        int64_t m_base, int64_t n_base, int lane) {
-  // Accumulator tile (i, j): lane l holds rows 4*(l >> 4) .. +3 of column (l & 15),
-  // i.e. four consecutive elements of one column of the column-major C.
-  const int64_t m_lane = m_base + 4 * (lane >> 4);
-  const int64_t n_lane = n_base + (lane & 15);
-  const bool full = (m_base + kWaveTile <= p.M) && (n_base + kWaveTile <= p.N) && p.c_vec_ok;
+__device__ __forceinline__ void store_c_lds(const Params &p, uint8_t *Cb,
+                                            const float16_t_v (&acc)[kSub][kSub],
+                                            __attribute__((address_space(3))) uint8_t *buf,
+                                            int64_t m_base, int64_t n_base, int lane) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) u32x2 lds_u2;
+  typedef __attribute__((address_space(3))) u32x4 lds_u4;
 #pragma unroll
   for (int j = 0; j < kSub; ++j) {
-    const int64_t n = n_lane + 16 * j;
+    const int n = kMma * j + (lane & 31);
 #pragma unroll
     for (int i = 0; i < kSub; ++i) {
-      const int64_t m = m_lane + 16 * i;
-      uint16_t h[4];
-      if constexpr (KIND == kF16) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int m = kMma * i + 8 * b + 4 * (lane >> 5);
+        uint16_t h[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          _Float16 v = (_Float16)acc[i][j][e];
-          h[e] = __builtin_bit_cast(uint16_t, v);
+          if constexpr (KIND == kF16) {
+            h[e] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][4 * b + e]);
+          } else {
+            h[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * b + e] * p.scale));
+          }
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          __bf16 v = (__bf16)(acc[i][j][e] * p.scale);
-          h[e] = __builtin_bit_cast(uint16_t, v);
-        }
-      }
-      uint16_t *dst = (uint16_t *)Cb + (n * p.ldc + m);
-      if (full) {
-        uint2 w;
+        u32x2 w;
         w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
         w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-        *(uint2 *)dst = w;
-      } else if (n < p.N) {
-        if (p.c_vec_ok && m + 3 < p.M) {
-          uint2 w;
-          w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-          w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-          *(uint2 *)dst = w;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (m + e < p.M) dst[e] = h[e];
-        }
+        const int chunk = (m >> 3) ^ (n & 15);
+        *(lds_u2 *)(buf + n * 256 + chunk * 16 + (m & 7) * 2) = w;
       }
+    }
+  }
+  // Same wave wrote what it reads next: the LDS counter wait orders them.
+  const bool full = (m_base + kWaveTile <= p.M) && (n_base + kWaveTile <= p.N);
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const int n = 4 * r + (lane >> 4);
+    const int mc = lane & 15;
+    const u32x4 v = *(lds_u4 *)(buf + n * 256 + ((mc ^ (n & 15)) * 16));
+    const int64_t gm = m_base + 8 * mc, gn = n_base + n;
+    uint16_t *dst = (uint16_t *)Cb + (gn * p.ldc + gm);
+    if (full || (gn < p.N && gm + 7 < p.M)) {
+      *(u32x4 *)dst = v;
+    } else if (gn < p.N) {
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gm + e < p.M) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
     }
   }
 }
@@ -233,8 +293,8 @@ __device__ __forceinline__ void store_c(const Params &p, uint8_t *Cb, const floa
 template <int KIND>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   typedef Traits<KIND> T;
-  // Two stages of [A strip | B strip], 64 KiB each.
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * kStageBytes];
+  // kStages stages of [A strip | B strip], 32 KiB each.
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * 2 * kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -253,57 +313,149 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   const uint32_t rec_a = (uint32_t)((rows_a - 1) * p.lda_b) + kbytes;
   const uint32_t rec_b = (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes;
 
+  // LDS layout: row r of a stage strip holds 64 B of K as four 16-byte slots;
+  // chunk c of row r is stored in slot c ^ ((r >> 2) & 3).  A ds_read_b128 phase
+  // (16 lanes, 16 consecutive rows, one chunk) then covers all 16 slots of the
+  // 256-byte bank period: four rows per period, four distinct slots per row
+  // group -- the XOR swizzle of the MI355X FP8 GEMM page for 64-byte rows.
   // Copy geometry of this lane (same for A and B, see copy_stage).
-  const int crow = 8 * wave + (lane >> 3);           // row within a 32-row band
-  const int gchunk = (lane & 7) ^ ((crow >> 1) & 7);  // global 16-B chunk of that row
+  const int crow = 16 * wave + (lane >> 2);           // row within a 64-row band
+  const int gchunk = (lane & 3) ^ ((crow >> 2) & 3);  // global 16-B chunk of that row
   const uint32_t voff_a = (uint32_t)(crow * p.lda_b) + gchunk * 16;
   const uint32_t voff_b = (uint32_t)(crow * p.ldb_b) + gchunk * 16;
-  const uint32_t qs_a = (uint32_t)(32 * p.lda_b), qs_b = (uint32_t)(32 * p.ldb_b);
-  const int kchunk = gchunk * (16 / T::es);          // K offset of the chunk in a step
+  const uint32_t qs_a = (uint32_t)(64 * p.lda_b), qs_b = (uint32_t)(64 * p.ldb_b);
+  const int kchunk = gchunk * (16 / T::es);           // K offset of the chunk in a step
 
-  // Fragment geometry: lane l reads row (l & 15) of each 16-row MFMA tile and the
-  // 16-byte chunk(s) of its K group (l >> 4); slots are swizzled by row.
+  // Fragment geometry: lane l reads row (l & 31) of each 32-row MFMA tile and
+  // the 16-byte chunk(s) of its K half (l >> 5).
   const int wm = wave & 1, wn = wave >> 1;
-  uint32_t lane_off[2];
+  uint32_t a_off[2], b_off[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int chunk = (T::reads == 1) ? (j * 4 + (lane >> 4)) : ((lane >> 4) * 2 + j);
-    lane_off[j] = (uint32_t)((lane & 15) * kRowBytes + ((chunk ^ ((lane & 15) >> 1)) * 16));
+    // fp16: substep j reads chunk 2j + half; fp8: read j of half h is chunk 2h + j.
+    const int chunk = (T::reads == 1) ? (2 * j + (lane >> 5)) : (2 * (lane >> 5) + j);
+    const uint32_t lo = (uint32_t)((lane & 31) * kRowBytes + ((chunk ^ ((lane >> 2) & 3)) * 16));
+    a_off[j] = lo + wm * kWaveTile * kRowBytes;
+    b_off[j] = lo + kStageBytes + wn * kWaveTile * kRowBytes;
   }
-  const int a_wave_off = wm * kWaveTile * kRowBytes;
-  const int b_wave_off = wn * kWaveTile * kRowBytes;
 
-  float4_t acc[kSub][kSub];
+  float16_t_v acc[kSub][kSub];
 #pragma unroll
   for (int i = 0; i < kSub; ++i)
 #pragma unroll
-    for (int j = 0; j < kSub; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kSub; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  // K-step t lives in stage t % kStages; its copies are issued three steps ahead.
+  // One loop iteration runs two MFMA substeps: one K-step for fp16, two for fp8.
+  // For fp8 an odd K-step count gets one leading step whose chunks all read as
+  // zero (adding exact zeros), so the fragment sets alternate at compile time.
+  constexpr int kPerBody = 2 / T::subs;
   const int64_t nk = (p.K + T::kstep - 1) / T::kstep;
-  auto issue = [&](int64_t ks, lds_void_t *da, lds_void_t *db) {
-    const int64_t k0 = ks * T::kstep;
-    const uint32_t kb = (uint32_t)(k0 * T::es);
-    const bool valid = kchunk < p.K - k0;
-    copy_stage<T::es>(da, make_rsrc(Ab + kb, rec_a - kb), voff_a, qs_a, valid, wave);
-    copy_stage<T::es>(db, make_rsrc(Bb + kb, rec_b - kb), voff_b, qs_b, valid, wave);
-  };
-  typedef const __attribute__((address_space(3))) uint8_t *lds_cptr;
-
+  const int64_t pad = (kPerBody == 2) ? (nk & 1) : 0;
+  const int64_t nk2 = nk + pad;
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
-  lds_u8 *const lds = (lds_u8 *)smem;
-  if (nk > 0) issue(0, (lds_void_t *)lds, (lds_void_t *)(lds + kStageBytes));
-  for (int64_t ks = 0; ks < nk; ++ks) {
-    // Stage ks&1 has landed and every wave is done reading the other stage.
-    __syncthreads();
-    const int cur = (int)(ks & 1) * 2 * kStageBytes;
-    const int nxt = 2 * kStageBytes - cur;
-    if (ks + 1 < nk)
-      issue(ks + 1, (lds_void_t *)(lds + nxt), (lds_void_t *)(lds + nxt + kStageBytes));
-    compute_stage<KIND>(acc, (lds_cptr)(lds + cur + a_wave_off),
-                        (lds_cptr)(lds + cur + kStageBytes + b_wave_off), lane_off);
+  auto step_copy = [&](int64_t t) {
+    // Steps outside the matrix (the leading pad step, and the steps past the end
+    // issued unconditionally by the last iterations) read zeros and touch no memory.
+    const int64_t k0 = (t - pad) * T::kstep;
+    const bool inside = (k0 >= 0) && (t < nk2);
+    const uint32_t kb = inside ? (uint32_t)(k0 * T::es) : 0u;
+    const bool valid = inside && (kchunk < p.K - k0);
+    lds_u8 *st = (lds_u8 *)smem + (int)(t % kStages) * 2 * kStageBytes + wave * 1024;
+    StepCopy c;
+    c.ra = make_rsrc(Ab + kb, rec_a - kb);
+    c.rb = make_rsrc(Bb + kb, rec_b - kb);
+    c.va = valid ? voff_a : kOob;
+    c.vb = valid ? voff_b : kOob;
+    c.la = st;
+    c.lb = st + kStageBytes;
+    return c;
+  };
+  auto issue = [&](int64_t t) {
+    const StepCopy c = step_copy(t);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) copy_one(c, d, qs_a, qs_b);
+  };
+
+  // Register pipeline: two fragment sets (A and B, 4 + 4 fragments); set u & 1
+  // feeds substep u while the other set is read for substep u + 1.
+  typedef typename T::frag_t frag_t;
+  frag_t fa[2][kSub], fb[2][kSub];
+
+  if (nk2 > 0) {
+    issue(0);
+    issue(1);
+    issue(2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));  // step 0 landed (steps 1, 2 in flight)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    lds_cptr st0 = (lds_cptr)smem;
+#pragma unroll
+    for (int j = 0; j < kSub; ++j) {
+      fa[0][j] = read_frag<KIND>(st0 + j * kMma * kRowBytes, a_off, 0);
+      fb[0][j] = read_frag<KIND>(st0 + j * kMma * kRowBytes, b_off, 0);
+    }
   }
 
-  store_c<KIND>(p, Cb, acc, m0 + wm * kWaveTile, n0 + wn * kWaveTile, lane);
+  for (int64_t t0 = 0; t0 < nk2; t0 += kPerBody) {
+#pragma unroll
+    for (int h = 0; h < kPerBody; ++h) {
+      const int64_t t = t0 + h;
+      // Step t + 1 has landed for every wave (step t + 2 may still be in flight),
+      // and every wave finished reading stage (t - 1) % kStages during step t - 1:
+      // publish the former, refill the latter with step t + 3.
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const StepCopy cp = step_copy(t + 3);
+      lds_cptr cur = (lds_cptr)smem + (int)(t % kStages) * 2 * kStageBytes;
+      lds_cptr nxt = (lds_cptr)smem + (int)((t + 1) % kStages) * 2 * kStageBytes;
+#pragma unroll
+      for (int s = 0; s < T::subs; ++s) {     // MFMA K sub-steps of this K-step
+        const bool last = (s == T::subs - 1);
+        lds_cptr src = last ? nxt : cur;      // where the next substep's data is
+        const int s_n = last ? 0 : s + 1;
+        const int u = (h * T::subs + s) & 1, v = u ^ 1;  // current / next fragment set
+#pragma unroll
+        for (int g = 0; g < kSub; ++g) {
+#pragma unroll
+          for (int j = 0; j < kSub; ++j) {
+            // Slot (g, j): at most one fragment read for the next substep (groups
+            // 0 and 1 read the eight fragments in the order they are needed:
+            // A0, B0..B3, A1..A3), at most one of the step's eight copies (spread
+            // evenly over the step's MFMAs), then one MFMA.
+            if (g < 2) {
+              const int f = 4 * g + j;
+              if (f == 0) fa[v][0] = read_frag<KIND>(src, a_off, s_n);
+              else if (f <= 4) fb[v][f - 1] = read_frag<KIND>(src + (f - 1) * kMma * kRowBytes, b_off, s_n);
+              else fa[v][f - 4] = read_frag<KIND>(src + (f - 4) * kMma * kRowBytes, a_off, s_n);
+            }
+            constexpr int kSlots = T::subs * kSub * kSub;   // MFMAs per step
+            constexpr int kEvery = kSlots / 8;             // slots between copies
+            const int slot = (s * kSub + g) * kSub + j;
+            if (slot % kEvery == 1 % kEvery) copy_one(cp, slot / kEvery, qs_a, qs_b);
+            acc[g][j] = mma(fa[u][g], fb[u][j], acc[g][j]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+    }
+  }
+
+  // Drain the trailing zero copies; every wave leaves the stages before the
+  // epilogue reuses the LDS.
+  __builtin_amdgcn_s_waitcnt(0);
+  if (p.c_vec16_ok) {
+    __syncthreads();
+    store_c_lds<KIND>(p, Cb, acc, (__attribute__((address_space(3))) uint8_t *)smem + wave * 32768,
+                      m0 + wm * kWaveTile, n0 + wn * kWaveTile, lane);
+  } else {
+    store_c<KIND>(p, Cb, acc, m0 + wm * kWaveTile, n0 + wn * kWaveTile, lane);
+  }
 }
 
 template __global__ void gemm_tn_kernel<kF16>(Params);
@@ -382,6 +534,7 @@ static int launch(const Problem &pr, hipStream_t stream) {
   p.tiles_m = (int32_t)tiles_m; p.tiles_n = (int32_t)tiles_n;
   p.scale = pr.scale;
   p.c_vec_ok = (pr.ldc % 4 == 0) ? 1 : 0;
+  p.c_vec16_ok = (pr.ldc % 8 == 0) ? 1 : 0;
 
   hipLaunchKernelGGL(gemm_tn_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
