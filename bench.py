@@ -197,7 +197,22 @@ def main():
     ap.add_argument("--workload", action="append", default=None,
                     help="workload names (default: f16_4096 and f8_8192)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (a known-size kernel for "
+                         "scaling HBM byte counters), then exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+
+        n = args.calibrate_copy * 2 ** 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n,
+                          "copies": 5}))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this GEMM build runs on a single MI355X; "
               "--gpus %d is not supported (a multi-GPU run would shard N across GPUs with no "
