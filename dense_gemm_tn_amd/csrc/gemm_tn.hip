@@ -39,6 +39,7 @@
 //     outside its M x N logical extent (section 11.4 of the hello-gpu chapter).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "dense_gemm_tn.h"
 
@@ -52,15 +53,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef const __attribute__((address_space(3))) uint8_t *lds_cptr;
 
 constexpr int kTile = 256;        // rows of A / columns of B per workgroup
-constexpr int kRowBytes = 64;     // bytes of K per row per K-step
-constexpr int kStages = 4;        // LDS ring of K-steps (copies run 3 steps ahead)
+constexpr int kRowBytes = 128;    // bytes of K per row per K-step (full 128-byte lines)
+constexpr int kStages = 2;        // LDS stages (double buffer)
 constexpr int kThreads = 256;     // 4 waves of 64
 constexpr int kWaveTile = 128;    // each wave owns kWaveTile x kWaveTile of C
 constexpr int kMma = 32;          // MFMA output tile edge
 constexpr int kSub = 4;           // MFMA tiles per wave edge (128 / 32)
 constexpr int kXcds = 8;          // chiplets the dispatcher deals blocks over
 constexpr int kGroupM = 8;        // tile rows per group in the grouped order
-constexpr int kStageBytes = kTile * kRowBytes;   // 16 KiB per operand per stage
+constexpr int kStageBytes = kTile * kRowBytes;   // 32 KiB per operand per stage
 constexpr uint32_t kOob = 0x80000000u;           // an offset past every descriptor
 // Word 3 of a raw (untyped, stride 0) buffer resource on gfx9-family parts:
 // 32-bit data format so the hardware range-checks the byte offset.
@@ -71,16 +72,16 @@ enum Kind { kF16 = 0, kF8 = 1 };
 template <int KIND> struct Traits;
 template <> struct Traits<kF16> {
   static constexpr int es = 2;       // bytes per element
-  static constexpr int kstep = 32;   // K elements per K-step (64 B per row)
+  static constexpr int kstep = 64;   // K elements per K-step (128 B per row)
   static constexpr int reads = 1;    // 16-byte LDS reads per lane per MFMA operand
-  static constexpr int subs = 2;     // MFMA K sub-steps per K-step (16 deep each)
+  static constexpr int subs = 4;     // MFMA K sub-steps per K-step (16 deep each)
   typedef half8_t frag_t;
 };
 template <> struct Traits<kF8> {
   static constexpr int es = 1;
-  static constexpr int kstep = 64;
+  static constexpr int kstep = 128;
   static constexpr int reads = 2;    // 32 bytes of K per lane
-  static constexpr int subs = 1;     // one 32x32x64 MFMA depth per K-step
+  static constexpr int subs = 2;     // MFMA K sub-steps per K-step (64 deep each)
   typedef int8_t_v frag_t;
 };
 
@@ -137,44 +138,47 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
                                            (int)kRsrcWord3);
 }
 
-// Copies for one K-step: a 256-row x 64-byte strip of A and of B, each as four
-// wave-wide loads per wave.  Load q of wave w fills LDS rows 64q + 16w .. +15
-// of the strip (1 KiB, lane-contiguous: lane l writes bytes l*16 .. l*16+15 of
-// that KiB), so lane l lands in row 64q + 16w + (l >> 2), slot l & 3, and
-// fetches the global 16-byte chunk that the swizzle stores there (see the
-// kernel).  `voff` is the lane's offset for q = 0, or kOob for a K-step (or
-// K-tail chunk) that must read zeros; the host guarantees
-// kOob + 3 * q_stride < 2^32, so a zero-read offset stays out of range.
+// Copies for one K-step: a 256-row x 128-byte strip of A and of B, each as
+// eight wave-wide loads per wave.  Load q of wave w fills LDS rows
+// 32q + 8w .. +7 of the strip (1 KiB, lane-contiguous: lane l writes bytes
+// l*16 .. l*16+15 of that KiB), so lane l lands in row 32q + 8w + (l >> 3),
+// slot l & 7, and fetches the global 16-byte chunk that the swizzle stores
+// there (see the kernel); eight lanes cover one full 128-byte line of a row.
+// `voff` is the lane's offset for q = 0, or kOob for a K-step (or K-tail chunk)
+// that must read zeros; the host guarantees kOob + 7 * q_stride < 2^32, so a
+// zero-read offset stays out of range.
 struct StepCopy {
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t va, vb;                          // lane offsets for q = 0
   __attribute__((address_space(3))) uint8_t *la, *lb;  // LDS strip bases (+ wave KiB)
 };
 
-// Issue copy d (0..7) of a step: d < 4 is load q = d of A, else load q = d - 4 of B.
+// Issue copy d (0..15) of a step: d < 8 is load q = d of A, else load q = d - 8 of B.
 __device__ __forceinline__ void copy_one(const StepCopy &c, int d, uint32_t qs_a, uint32_t qs_b) {
-  if (d < 4) {
+  if (d < 8) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, (lds_void_t *)(c.la + d * 4096), 16,
                                              c.va + d * qs_a, 0, 0, 0);
   } else {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, (lds_void_t *)(c.lb + (d - 4) * 4096), 16,
-                                             c.vb + (d - 4) * qs_b, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, (lds_void_t *)(c.lb + (d - 8) * 4096), 16,
+                                             c.vb + (d - 8) * qs_b, 0, 0, 0);
   }
 }
 
 // One MFMA operand fragment: 32 rows x (16 fp16 or 64 fp8) of K.  Lane l reads
 // row (l & 31) of the 32-row tile at `tile` and the 16-byte chunk(s) of its K
 // half (l >> 5); `off[s * reads + r]` holds the lane's swizzled byte offsets
-// (stage and wave offsets included) for substep s, read r.
+// (wave offset included) for substep s, read r.
 template <int KIND>
 __device__ __forceinline__ typename Traits<KIND>::frag_t read_frag(lds_cptr tile,
-                                                                  const uint32_t (&off)[2],
+                                                                  const uint32_t (&off)[4],
                                                                   int sub) {
   if constexpr (Traits<KIND>::reads == 1) {
     return *(const __attribute__((address_space(3))) half8_t *)(tile + off[sub]);
   } else {
-    const int4_t_v lo = *(const __attribute__((address_space(3))) int4_t_v *)(tile + off[0]);
-    const int4_t_v hi = *(const __attribute__((address_space(3))) int4_t_v *)(tile + off[1]);
+    const int4_t_v lo =
+        *(const __attribute__((address_space(3))) int4_t_v *)(tile + off[2 * sub]);
+    const int4_t_v hi =
+        *(const __attribute__((address_space(3))) int4_t_v *)(tile + off[2 * sub + 1]);
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 }
@@ -293,7 +297,7 @@ __device__ __forceinline__ void store_c_lds(const Params &p, uint8_t *Cb,
 template <int KIND>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   typedef Traits<KIND> T;
-  // kStages stages of [A strip | B strip], 32 KiB each.
+  // Two stages of [A strip | B strip], 64 KiB each.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * 2 * kStageBytes];
 
   const int tid = threadIdx.x;
@@ -313,28 +317,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   const uint32_t rec_a = (uint32_t)((rows_a - 1) * p.lda_b) + kbytes;
   const uint32_t rec_b = (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes;
 
-  // LDS layout: row r of a stage strip holds 64 B of K as four 16-byte slots;
-  // chunk c of row r is stored in slot c ^ ((r >> 2) & 3).  A ds_read_b128 phase
-  // (16 lanes, 16 consecutive rows, one chunk) then covers all 16 slots of the
-  // 256-byte bank period: four rows per period, four distinct slots per row
-  // group -- the XOR swizzle of the MI355X FP8 GEMM page for 64-byte rows.
-  // Copy geometry of this lane (same for A and B, see copy_stage).
-  const int crow = 16 * wave + (lane >> 2);           // row within a 64-row band
-  const int gchunk = (lane & 3) ^ ((crow >> 2) & 3);  // global 16-B chunk of that row
+  // LDS layout: row r of a stage strip holds 128 B of K as eight 16-byte slots;
+  // chunk c of row r is stored in slot c ^ ((r >> 1) & 7), the XOR swizzle of
+  // the MI355X FP8 GEMM page: a ds_read_b128 phase (16 lanes, 16 consecutive
+  // rows, one chunk) covers all 16 slots of the 256-byte bank period.
+  // Copy geometry of this lane (same for A and B, see copy_one).
+  const int crow = 8 * wave + (lane >> 3);            // row within a 32-row band
+  const int gchunk = (lane & 7) ^ ((crow >> 1) & 7);  // global 16-B chunk of that row
   const uint32_t voff_a = (uint32_t)(crow * p.lda_b) + gchunk * 16;
   const uint32_t voff_b = (uint32_t)(crow * p.ldb_b) + gchunk * 16;
-  const uint32_t qs_a = (uint32_t)(64 * p.lda_b), qs_b = (uint32_t)(64 * p.ldb_b);
+  const uint32_t qs_a = (uint32_t)(32 * p.lda_b), qs_b = (uint32_t)(32 * p.ldb_b);
   const int kchunk = gchunk * (16 / T::es);           // K offset of the chunk in a step
 
   // Fragment geometry: lane l reads row (l & 31) of each 32-row MFMA tile and
   // the 16-byte chunk(s) of its K half (l >> 5).
   const int wm = wave & 1, wn = wave >> 1;
-  uint32_t a_off[2], b_off[2];
+  uint32_t a_off[4], b_off[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    // fp16: substep j reads chunk 2j + half; fp8: read j of half h is chunk 2h + j.
-    const int chunk = (T::reads == 1) ? (2 * j + (lane >> 5)) : (2 * (lane >> 5) + j);
-    const uint32_t lo = (uint32_t)((lane & 31) * kRowBytes + ((chunk ^ ((lane >> 2) & 3)) * 16));
+  for (int j = 0; j < 4; ++j) {
+    // fp16: substep j reads chunk 2j + half; fp8: read j&1 of substep j>>1 for
+    // half h is chunk 4(j>>1) + 2h + (j&1).
+    const int chunk = (T::reads == 1) ? (2 * j + (lane >> 5))
+                                      : (4 * (j >> 1) + 2 * (lane >> 5) + (j & 1));
+    const uint32_t lo = (uint32_t)((lane & 31) * kRowBytes + ((chunk ^ ((lane >> 1) & 7)) * 16));
     a_off[j] = lo + wm * kWaveTile * kRowBytes;
     b_off[j] = lo + kStageBytes + wn * kWaveTile * kRowBytes;
   }
@@ -347,13 +352,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // K-step t lives in stage t % kStages; its copies are issued three steps ahead.
-  // One loop iteration runs two MFMA substeps: one K-step for fp16, two for fp8.
-  // For fp8 an odd K-step count gets one leading step whose chunks all read as
-  // zero (adding exact zeros), so the fragment sets alternate at compile time.
-  constexpr int kPerBody = 2 / T::subs;
+  // One loop iteration runs two K-steps, stage 0 then stage 1.  An odd K-step
+  // count gets one leading step whose chunks all read as zero (adding exact
+  // zeros).
   const int64_t nk = (p.K + T::kstep - 1) / T::kstep;
-  const int64_t pad = (kPerBody == 2) ? (nk & 1) : 0;
+  const int64_t pad = nk & 1;
   const int64_t nk2 = nk + pad;
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   auto step_copy = [&](int64_t t) {
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     const bool inside = (k0 >= 0) && (t < nk2);
     const uint32_t kb = inside ? (uint32_t)(k0 * T::es) : 0u;
     const bool valid = inside && (kchunk < p.K - k0);
-    lds_u8 *st = (lds_u8 *)smem + (int)(t % kStages) * 2 * kStageBytes + wave * 1024;
+    lds_u8 *st = (lds_u8 *)smem + (int)(t & 1) * 2 * kStageBytes + wave * 1024;
     StepCopy c;
     c.ra = make_rsrc(Ab + kb, rec_a - kb);
     c.rb = make_rsrc(Bb + kb, rec_b - kb);
@@ -373,22 +376,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     c.lb = st + kStageBytes;
     return c;
   };
-  auto issue = [&](int64_t t) {
-    const StepCopy c = step_copy(t);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) copy_one(c, d, qs_a, qs_b);
-  };
 
-  // Register pipeline: two fragment sets (A and B, 4 + 4 fragments); set u & 1
-  // feeds substep u while the other set is read for substep u + 1.
+  // Per K-step schedule (S substeps x 16 MFMA slots, one MFMA per slot):
+  //  * a substep reads the next substep's eight fragments in its first eight
+  //    slots (A0, B0..B3, A1..A3, in the order they are needed);
+  //  * the last substep instead reaches the barrier after its first eight slots
+  //    (step t+1 has landed everywhere; every wave is done with stage t) and
+  //    then reads step t+1's first fragments from the other stage;
+  //  * step t+2's sixteen copies into the freed stage start right after the
+  //    barrier and are spread over a window of kWin slots (the 8 slots after
+  //    the barrier, then the first kWin - 8 slots of step t+1), at most one per
+  //    slot, so the last one still has part of a step to land before step t+1's
+  //    barrier.  Copy c goes to window position (c * kWin) / 16.
+  constexpr int kSlots = T::subs * kSub * kSub;    // MFMAs per step
+  constexpr int kBar = kSlots - 8;                // barrier before this slot
+  constexpr int kWin = (T::reads == 1) ? 32 : 24;  // copy window (slots)
+  static_assert(kWin >= 16 && kWin - 8 <= kBar, "copy window");
+  // Copies [first_copy(x), first_copy(x + 1)) are issued at window position x.
+  auto first_copy = [](int x) { return (x * 16 + kWin - 1) / kWin; };
+  const int kPost = first_copy(8);                // copies issued after the barrier
+
   typedef typename T::frag_t frag_t;
   frag_t fa[2][kSub], fb[2][kSub];
 
   if (nk2 > 0) {
-    issue(0);
-    issue(1);
-    issue(2);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));  // step 0 landed (steps 1, 2 in flight)
+    const StepCopy c0 = step_copy(0);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) copy_one(c0, d, qs_a, qs_b);
+    const StepCopy c1 = step_copy(1);
+#pragma unroll
+    for (int d = 0; d < 16; ++d)
+      if (d < kPost) copy_one(c1, d, qs_a, qs_b);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));      // steps 0 (and part of 1) landed
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -400,46 +419,49 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     }
   }
 
-  for (int64_t t0 = 0; t0 < nk2; t0 += kPerBody) {
+  for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
 #pragma unroll
-    for (int h = 0; h < kPerBody; ++h) {
+    for (int h = 0; h < 2; ++h) {            // K-step t0 + h lives in stage h
       const int64_t t = t0 + h;
-      // Step t + 1 has landed for every wave (step t + 2 may still be in flight),
-      // and every wave finished reading stage (t - 1) % kStages during step t - 1:
-      // publish the former, refill the latter with step t + 3.
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      const StepCopy cp = step_copy(t + 3);
-      lds_cptr cur = (lds_cptr)smem + (int)(t % kStages) * 2 * kStageBytes;
-      lds_cptr nxt = (lds_cptr)smem + (int)((t + 1) % kStages) * 2 * kStageBytes;
+      const StepCopy cn = step_copy(t + 1);  // remaining copies of step t + 1
+      const StepCopy cnn = step_copy(t + 2); // first copies of step t + 2
+      lds_cptr cur = (lds_cptr)smem + h * 2 * kStageBytes;
+      lds_cptr nxt = (lds_cptr)smem + (1 - h) * 2 * kStageBytes;
 #pragma unroll
-      for (int s = 0; s < T::subs; ++s) {     // MFMA K sub-steps of this K-step
+      for (int s = 0; s < T::subs; ++s) {
         const bool last = (s == T::subs - 1);
-        lds_cptr src = last ? nxt : cur;      // where the next substep's data is
-        const int s_n = last ? 0 : s + 1;
-        const int u = (h * T::subs + s) & 1, v = u ^ 1;  // current / next fragment set
+        const int u = s & 1, v = u ^ 1;      // current / next fragment set
 #pragma unroll
         for (int g = 0; g < kSub; ++g) {
 #pragma unroll
           for (int j = 0; j < kSub; ++j) {
-            // Slot (g, j): at most one fragment read for the next substep (groups
-            // 0 and 1 read the eight fragments in the order they are needed:
-            // A0, B0..B3, A1..A3), at most one of the step's eight copies (spread
-            // evenly over the step's MFMAs), then one MFMA.
-            if (g < 2) {
-              const int f = 4 * g + j;
+            const int slot = (s * kSub + g) * kSub + j;
+            const int f = (slot & 15) - (last ? 8 : 0);  // fragment read in this slot
+            if (f >= 0 && f < 8) {
+              lds_cptr src = last ? nxt : cur;
+              const int s_n = last ? 0 : s + 1;
               if (f == 0) fa[v][0] = read_frag<KIND>(src, a_off, s_n);
               else if (f <= 4) fb[v][f - 1] = read_frag<KIND>(src + (f - 1) * kMma * kRowBytes, b_off, s_n);
               else fa[v][f - 4] = read_frag<KIND>(src + (f - 4) * kMma * kRowBytes, a_off, s_n);
             }
-            constexpr int kSlots = T::subs * kSub * kSub;   // MFMAs per step
-            constexpr int kEvery = kSlots / 8;             // slots between copies
-            const int slot = (s * kSub + g) * kSub + j;
-            if (slot % kEvery == 1 % kEvery) copy_one(cp, slot / kEvery, qs_a, qs_b);
+            if (slot < kWin - 8) {
+              for (int c = first_copy(slot + 8); c < first_copy(slot + 9); ++c)
+                copy_one(cn, c, qs_a, qs_b);
+            } else if (slot >= kBar) {
+              for (int c = first_copy(slot - kBar); c < first_copy(slot - kBar + 1); ++c)
+                copy_one(cnn, c, qs_a, qs_b);
+            }
             acc[g][j] = mma(fa[u][g], fb[u][j], acc[g][j]);
             __builtin_amdgcn_sched_barrier(0);
+            if (slot == kBar - 1) {
+              // Step t+1's copies have landed for this wave and its last reads of
+              // stage h are complete; once every wave is here, stage 1-h is
+              // published and stage h may be refilled.
+              __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & 0xF0FF);  // vmcnt(0), lgkmcnt(0)
+              asm volatile("" ::: "memory");
+              __builtin_amdgcn_s_barrier();
+              asm volatile("" ::: "memory");
+            }
           }
         }
       }
@@ -462,6 +484,7 @@ template __global__ void gemm_tn_kernel<kF16>(Params);
 template __global__ void gemm_tn_kernel<kF8>(Params);
 
 // ------------------------------------------------------------------ host side
+
 
 static bool overlaps(const void *a, uint64_t abytes, const void *b, uint64_t bbytes) {
   if (abytes == 0 || bbytes == 0) return false;
