@@ -110,17 +110,12 @@ struct Params {
   int32_t c_vec16_ok;    // 16-byte C stores are aligned (ldc % 8 == 0)
 };
 
-// Block id -> (head, tile_m, tile_n).  First the chiplet remap: block b runs on
-// XCD b % 8 and is the (b / 8)-th block there; XCD x gets the contiguous logical
-// range starting at x*q + min(x, r) (q = G / 8, r = G % 8), a bijection for any
-// G.  Then the grouped order inside a head: groups of kGroupM tile rows, walked
-// column by column (short last group allowed).
+// Logical tile -> (head, tile_m, tile_n): the grouped order inside a head,
+// groups of kGroupM tile rows walked column by column (short last group
+// allowed), heads one after another.
 template <typename I>
-__host__ __device__ inline void tile_of_block(I b, I G, I tiles_m, I tiles_n, I *head, I *tm,
-                                              I *tn) {
-  const I q = G / kXcds, r = G % kXcds;
-  const I x = b % kXcds, idx = b / kXcds;
-  const I logical = x * q + (x < r ? x : r) + idx;
+__host__ __device__ inline void tile_coords(I logical, I tiles_m, I tiles_n, I *head, I *tm,
+                                            I *tn) {
   const I per_head = tiles_m * tiles_n;
   *head = logical / per_head;
   const I t = logical - *head * per_head;
@@ -131,6 +126,27 @@ __host__ __device__ inline void tile_of_block(I b, I G, I tiles_m, I tiles_n, I 
   const I local = t - group * span;
   *tm = first_m + local % rows;
   *tn = local / rows;
+}
+
+// First logical tile of XCD x when T tiles are split into 8 contiguous ranges
+// (sizes q or q + 1, q = T / 8).
+template <typename I>
+__host__ __device__ inline I xcd_first_tile(I x, I T) {
+  const I q = T / kXcds, r = T % kXcds;
+  return x * q + (x < r ? x : r);
+}
+
+// Block id -> (head, tile_m, tile_n) for a grid of one block per tile.  The
+// dispatcher deals block b to XCD b % 8 as that XCD's (b / 8)-th block, so XCD
+// x is given the contiguous logical range starting at xcd_first_tile(x, G), a
+// bijection for any G; inside it the grouped order keeps the blocks that are
+// resident on one XCD at the same time on a compact patch of tiles, sharing A
+// and B strips in that XCD's L2.
+template <typename I>
+__host__ __device__ inline void tile_of_block(I b, I G, I tiles_m, I tiles_n, I *head, I *tm,
+                                              I *tn) {
+  const I x = b % kXcds, idx = b / kXcds;
+  tile_coords<I>(xcd_first_tile<I>(x, G) + idx, tiles_m, tiles_n, head, tm, tn);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -484,6 +500,183 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
 template __global__ void gemm_tn_kernel<kF16>(Params);
 template __global__ void gemm_tn_kernel<kF8>(Params);
 
+// ----------------------------------------------------------------- skinny K
+// Kernels for K * es <= 256 bytes (the QK^T shape: K = head dim 128): the whole
+// K extent of a 128 x 128 tile's A and B strips fits in LDS at once (2 x 32
+// KiB), so there is no K pipeline; each wave owns 64 x 64 of C (2 x 2 MFMA
+// 32x32 tiles, 64 accumulators).  Writing C bounds these shapes; one tile per
+// block and two blocks per CU let one block's stores drain while the other
+// block copies and computes.
+constexpr int kSkTile = 128;       // rows of A / columns of B per block
+constexpr int kSkRow = 256;        // LDS bytes per row (all of K, zero-filled)
+constexpr int kSkStrip = kSkTile * kSkRow;  // 32 KiB per operand
+constexpr int kSkWave = 64;        // each wave owns 64 x 64 of C
+constexpr int kSkSub = 2;          // MFMA tiles per wave edge
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Copies of one tile's A and B strips (128 rows x 256 B each, rows of 256 B,
+// chunk c of row r in slot c ^ (r & 15), so a 16-row ds_read_b128 phase hits 16
+// distinct slots of the bank period) into `stage`.  Load q (0..7) of wave w
+// fills rows 16q + 4w .. +3 (1 KiB): lane l lands in row 16q + 4w + (l >> 4),
+// slot l & 15.  Chunks at or past K are pointed out of range and read zero.
+template <int KIND>
+__device__ __forceinline__ void sk_copy(const Params &p, lds_u8 *stage, int head, int tm, int tn,
+                                        int wave, int lane) {
+  typedef Traits<KIND> T;
+  const int64_t m0 = (int64_t)tm * kSkTile, n0 = (int64_t)tn * kSkTile;
+  const uint8_t *Ab = p.A + head * p.stride_a_b + m0 * p.lda_b;
+  const uint8_t *Bb = p.B + head * p.stride_b_b + n0 * p.ldb_b;
+  const int64_t rows_a = (p.M - m0) < kSkTile ? (p.M - m0) : kSkTile;
+  const int64_t rows_b = (p.N - n0) < kSkTile ? (p.N - n0) : kSkTile;
+  const uint32_t kbytes = (uint32_t)(p.K * T::es);
+  const int crow = 4 * wave + (lane >> 4);
+  const int gchunk = (lane & 15) ^ (crow & 15);
+  const bool valid = gchunk * 16 < (int)kbytes;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, (uint32_t)((rows_a - 1) * p.lda_b) + kbytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes);
+  const uint32_t va = valid ? (uint32_t)(crow * p.lda_b) + gchunk * 16 : kOob;
+  const uint32_t vb = valid ? (uint32_t)(crow * p.ldb_b) + gchunk * 16 : kOob;
+  lds_u8 *la = stage + wave * 1024;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(la + q * 4096), 16,
+                                             va + q * (uint32_t)(16 * p.lda_b), 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(la + kSkStrip + q * 4096), 16,
+                                             vb + q * (uint32_t)(16 * p.ldb_b), 0, 0, 0);
+  }
+}
+
+// The wave's 64 x 64 block of A x B from a stage (substeps of 32 B of K: one
+// 16-byte chunk per lane half for fp16, two for fp8; fragments double-buffered).
+template <int KIND>
+__device__ __forceinline__ void sk_compute(float16_t_v (&acc)[kSkSub][kSkSub], lds_cptr stage,
+                                           int wm, int wn, int lane) {
+  typedef Traits<KIND> T;
+  constexpr int kSubs = (T::reads == 1) ? 8 : 4;
+  lds_cptr la = stage + (wm * kSkWave + (lane & 31)) * kSkRow;
+  lds_cptr lb = stage + kSkStrip + (wn * kSkWave + (lane & 31)) * kSkRow;
+  const int sw = lane & 15;
+  auto frag = [&](lds_cptr row0, int i, int s) -> typename T::frag_t {
+    lds_cptr r = row0 + i * kMma * kSkRow;
+    if constexpr (T::reads == 1) {
+      const int c = 2 * s + (lane >> 5);
+      return *(const __attribute__((address_space(3))) half8_t *)(r + ((c ^ sw) * 16));
+    } else {
+      const int c = 4 * s + 2 * (lane >> 5);
+      const int4_t_v lo = *(const __attribute__((address_space(3))) int4_t_v *)(r + ((c ^ sw) * 16));
+      const int4_t_v hi =
+          *(const __attribute__((address_space(3))) int4_t_v *)(r + (((c + 1) ^ sw) * 16));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kSkSub; ++i)
+#pragma unroll
+    for (int j = 0; j < kSkSub; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  typename T::frag_t fa[2][kSkSub], fb[2][kSkSub];
+#pragma unroll
+  for (int i = 0; i < kSkSub; ++i) {
+    fa[0][i] = frag(la, i, 0);
+    fb[0][i] = frag(lb, i, 0);
+  }
+#pragma unroll
+  for (int s = 0; s < kSubs; ++s) {
+    const int u = s & 1;
+    if (s + 1 < kSubs) {
+#pragma unroll
+      for (int i = 0; i < kSkSub; ++i) {
+        fa[u ^ 1][i] = frag(la, i, s + 1);
+        fb[u ^ 1][i] = frag(lb, i, s + 1);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kSkSub; ++i)
+#pragma unroll
+      for (int j = 0; j < kSkSub; ++j) acc[i][j] = mma(fa[u][i], fb[u][j], acc[i][j]);
+  }
+}
+
+// Converted accumulators into the wave's 8 KiB transpose buffer: column n at
+// n * 128 B, its 16-byte chunk c in slot c ^ (n & 7).
+template <int KIND>
+__device__ __forceinline__ void sk_to_lds(const Params &p, const float16_t_v (&acc)[kSkSub][kSkSub],
+                                          lds_u8 *buf, int lane) {
+#pragma unroll
+  for (int j = 0; j < kSkSub; ++j) {
+    const int n = kMma * j + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < kSkSub; ++i) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int m = kMma * i + 8 * b + 4 * (lane >> 5);
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (KIND == kF16) {
+            h[e] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][4 * b + e]);
+          } else {
+            h[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * b + e] * p.scale));
+          }
+        }
+        u32x2 w;
+        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        *(__attribute__((address_space(3))) u32x2 *)(buf + n * 128 + (((m >> 3) ^ (n & 7)) * 16) +
+                                                   (m & 7) * 2) = w;
+      }
+    }
+  }
+}
+
+// One tile per block (two blocks per CU).
+template <int KIND>
+__global__ __launch_bounds__(kThreads, 2) void gemm_tn_skinny_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kSkStrip];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int head, tm, tn;
+  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
+  // (K = 0 still copies: every chunk is then out of range and reads zero.)
+  sk_copy<KIND>(p, (lds_u8 *)smem, head, tm, tn, wave, lane);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  const int wm = wave & 1, wn = wave >> 1;
+  float16_t_v acc[kSkSub][kSkSub];
+  sk_compute<KIND>(acc, (lds_cptr)smem, wm, wn, lane);
+  __syncthreads();  // every wave is done reading the strips
+  lds_u8 *buf = (lds_u8 *)smem + wave * 8192;
+  sk_to_lds<KIND>(p, acc, buf, lane);
+  uint8_t *Cb = p.C + head * p.stride_c_b;
+  const int64_t m_base = (int64_t)tm * kSkTile + wm * kSkWave;
+  const int64_t n_base = (int64_t)tn * kSkTile + wn * kSkWave;
+  const bool full = (m_base + kSkWave <= p.M) && (n_base + kSkWave <= p.N) && p.c_vec16_ok;
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int n = 8 * r + (lane >> 3);
+    const int mc = lane & 7;
+    const u32x4 v = *(__attribute__((address_space(3))) u32x4 *)(buf + n * 128 + ((mc ^ (n & 7)) * 16));
+    const int64_t gm = m_base + 8 * mc, gn = n_base + n;
+    uint16_t *dst = (uint16_t *)Cb + (gn * p.ldc + gm);
+    if (full || (p.c_vec16_ok && gn < p.N && gm + 7 < p.M)) {
+      *(u32x4 *)dst = v;
+    } else if (gn < p.N) {
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gm + e < p.M) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+template __global__ void gemm_tn_skinny_kernel<kF16>(Params);
+template __global__ void gemm_tn_skinny_kernel<kF8>(Params);
+
 // ------------------------------------------------------------------ host side
 
 
@@ -543,8 +736,12 @@ static int launch(const Problem &pr, hipStream_t stream) {
       reach_b >= (int64_t)kOob)
     return DG_ERR_UNSUPPORTED;
 
-  const int64_t tiles_m = (pr.M + kTile - 1) / kTile;
-  const int64_t tiles_n = (pr.N + kTile - 1) / kTile;
+  // Skinny contractions (all of K fits one 256-byte LDS row) take the 128 x 128
+  // tile kernel with two blocks per CU; everything else the 256 x 256 pipeline.
+  const bool skinny = pr.K * es <= kSkRow;
+  const int64_t tile = skinny ? kSkTile : kTile;
+  const int64_t tiles_m = (pr.M + tile - 1) / tile;
+  const int64_t tiles_n = (pr.N + tile - 1) / tile;
   const int64_t blocks = tiles_m * tiles_n * pr.batch;
   if (blocks > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;
 
@@ -560,7 +757,11 @@ static int launch(const Problem &pr, hipStream_t stream) {
   p.c_vec_ok = (pr.ldc % 4 == 0) ? 1 : 0;
   p.c_vec16_ok = (pr.ldc % 8 == 0) ? 1 : 0;
 
-  hipLaunchKernelGGL(gemm_tn_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  if (skinny)
+    hipLaunchKernelGGL(gemm_tn_skinny_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL(gemm_tn_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 

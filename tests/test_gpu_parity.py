@@ -99,12 +99,15 @@ def normwise_error(kind, got_codes, ref):
 
 # Edge shapes of section 11.4 (1x1x1, 3x5x7, 15x17x19, 17x19x23, 31x33x29) with K
 # rounded up to the 16-byte vector, plus multi-tile ragged shapes and K tails.
+# K rows of at most 256 bytes take the skinny-K kernel (fp16 K <= 128, fp8
+# K <= 256), longer ones the pipelined 256 x 256 kernel; both are covered.
 EDGE = [(1, 1, 8), (3, 5, 8), (15, 17, 24), (17, 19, 24), (31, 33, 32)]
 EDGE8 = [(1, 1, 16), (3, 5, 16), (15, 17, 32), (17, 19, 32), (31, 33, 32)]
 RAGGED = [(256, 256, 256), (300, 290, 200), (257, 255, 72), (513, 260, 136), (64, 700, 64),
-          (700, 64, 1000), (1000, 1000, 8)]
+          (700, 64, 1000), (1000, 1000, 8), (260, 300, 128), (129, 131, 136), (383, 385, 264)]
 RAGGED8 = [(256, 256, 256), (300, 290, 208), (257, 255, 144), (513, 260, 112), (64, 700, 64),
-           (700, 64, 1008), (1000, 1000, 16)]
+           (700, 64, 1008), (1000, 1000, 16), (300, 290, 272), (513, 260, 400),
+           (256, 256, 512), (129, 131, 528)]
 
 
 @pytest.mark.parametrize("M,N,K", EDGE + RAGGED)
@@ -197,6 +200,24 @@ def test_batched_qkt_small():
     for h in range(H):
         assert_exact("qkt", got[h], ref[h])
         assert np.array_equal(gott[h], got[h].T)
+
+
+@pytest.mark.parametrize("H,M,N,D,pad", [(12, 640, 520, 128, 0), (12, 640, 520, 64, 8),
+                                         (2, 1024, 2048, 128, 0), (3, 136, 264, 32, 16)])
+def test_batched_qkt_many_tiles(H, M, N, D, pad):
+    """More 128 x 128 tiles than CUs (the persistent skinny-K form walks several
+    tiles per block), N tails, a padded lds, and a K shorter than the LDS row."""
+    x = inputs.make_shape("qkt", M, N, D, dist="pm1", seed=H + M + D, batch=H)
+    q, k = _dev(x["Q"]), _dev(x["K"])
+    lds = M + pad
+    s = torch.full((H, N, lds), CANARY16, dtype=torch.int32, device=DEV).to(torch.int16)
+    dg.gemm_batched_qkt(q, k, s, H, M, N, D, D, D, lds, M * D, N * D, N * lds)
+    torch.cuda.synchronize()
+    got = s.cpu().numpy().view(np.uint16)
+    ref = oracle.batched_qkt(x["Q"], x["K"], H, M, N, D)
+    for h in range(H):
+        assert_exact("qkt", np.ascontiguousarray(got[h, :, :M]), ref[h])
+        assert np.all(got[h, :, M:] == CANARY16)
 
 
 # ------------------------------------------------------------- full-size workloads
