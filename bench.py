@@ -36,7 +36,7 @@ METRIC = "TFLOP/s and % of dense MFMA peak: FP16 TN 4096^3, FP8 e4m3 8192^3"
 # Published MI355X dense peaks: 256 CUs x 2.4 GHz x 4096 (fp16) / 8192 (fp8) flop/clk/CU.
 PEAK_TFLOPS = {"f16": 2516.6, "qkt": 2516.6, "f8": 5033.2}
 HBM_PEAK_GBS = 8000.0
-KERNEL_NAME = {"f16": "gemm_tn_kernel<0>", "qkt": "gemm_tn_kernel<0>", "f8": "gemm_tn_kernel<1>"}
+KERNEL_NAME = {"f16": "gemm_tn_kernel<0>", "qkt": "gemm_tn_skinny_kernel<0>", "f8": "gemm_tn_kernel<1>"}
 SRC = os.path.join(ROOT, "dense_gemm_tn_amd", "csrc", "gemm_tn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 

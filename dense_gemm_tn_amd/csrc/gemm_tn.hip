@@ -664,7 +664,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_skinny_kernel(Params p) {
     const int64_t gm = m_base + 8 * mc, gn = n_base + n;
     uint16_t *dst = (uint16_t *)Cb + (gn * p.ldc + gm);
     if (full || (p.c_vec16_ok && gn < p.N && gm + 7 < p.M)) {
-      *(u32x4 *)dst = v;
+      // Non-temporal: C is written once and never read here, and letting it
+      // allocate in L2 evicts the Q and K strips that later tiles re-read.
+      __builtin_nontemporal_store(v, (u32x4 *)dst);
     } else if (gn < p.N) {
       const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
