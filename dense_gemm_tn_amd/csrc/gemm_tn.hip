@@ -47,6 +47,7 @@ namespace dg {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t_v __attribute__((ext_vector_type(16)));
+typedef float float4_t_v __attribute__((ext_vector_type(4)));
 typedef int int8_t_v __attribute__((ext_vector_type(8)));
 typedef int int4_t_v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -57,8 +58,7 @@ constexpr int kRowBytes = 128;    // bytes of K per row per K-step (full 128-byt
 constexpr int kStages = 2;        // LDS stages (double buffer)
 constexpr int kThreads = 256;     // 4 waves of 64
 constexpr int kWaveTile = 128;    // each wave owns kWaveTile x kWaveTile of C
-constexpr int kMma = 32;          // MFMA output tile edge
-constexpr int kSub = 4;           // MFMA tiles per wave edge (128 / 32)
+constexpr int kMma = 32;          // MFMA output tile edge of the skinny-K kernels
 constexpr int kXcds = 8;          // chiplets the dispatcher deals blocks over
 constexpr int kGroupM = 8;        // tile rows per group in the grouped order
 constexpr int kStageBytes = kTile * kRowBytes;   // 32 KiB per operand per stage
@@ -74,20 +74,42 @@ template <> struct Traits<kF16> {
   static constexpr int es = 2;       // bytes per element
   static constexpr int kstep = 64;   // K elements per K-step (128 B per row)
   static constexpr int reads = 1;    // 16-byte LDS reads per lane per MFMA operand
-  static constexpr int subs = 4;     // MFMA K sub-steps per K-step (16 deep each)
+  // 256 x 256 kernel: v_mfma_f32_16x16x32_f16, two 32-deep sub-steps per K-step.
+  static constexpr int mt = 16;      // MFMA output tile edge
+  static constexpr int subs = 2;     // MFMA K sub-steps per K-step
   typedef half8_t frag_t;
+  typedef float4_t_v acc_t;
 };
 template <> struct Traits<kF8> {
   static constexpr int es = 1;
   static constexpr int kstep = 128;
   static constexpr int reads = 2;    // 32 bytes of K per lane
-  static constexpr int subs = 2;     // MFMA K sub-steps per K-step (64 deep each)
+  // 256 x 256 kernel: v_mfma_f32_32x32x64_f8f6f4, two 64-deep sub-steps per K-step.
+  static constexpr int mt = 32;
+  static constexpr int subs = 2;
   typedef int8_t_v frag_t;
+  typedef float16_t_v acc_t;
 };
 
 __device__ __forceinline__ float16_t_v mma(const half8_t &a, const half8_t &b, float16_t_v c) {
   // v_mfma_f32_32x32x16_f16: fp16 products, fp32 accumulate.
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t_v mma(const half8_t &a, const half8_t &b, float4_t_v c) {
+  // v_mfma_f32_16x16x32_f16: fp16 products, fp32 accumulate.  Written as
+  // inline assembly with the accumulator tied in place in AGPRs: with the
+  // builtin, the register allocator rotates the 64 accumulator tiles of the
+  // 256 x 256 kernel through spare registers (hundreds of v_accvgpr moves per
+  // K-step).  The memory clobber keeps the LDS reads and copies in the slots
+  // the schedule gives them.  Callers leave wait states before reading an
+  // accumulator with anything but another MFMA (see mfma_drain).
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
+  return c;
+}
+// Wait states after the last MFMA before its accumulators are read by other
+// instructions (more than the 16x16x32 result latency).
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 __device__ __forceinline__ float16_t_v mma(const int8_t_v &a, const int8_t_v &b, float16_t_v c) {
   // v_mfma_f32_32x32x64_f8f6f4 with both operand formats = 0 (FP8 E4M3) and
@@ -203,43 +225,62 @@ __device__ __forceinline__ typename Traits<KIND>::frag_t read_frag(lds_cptr tile
 // (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at max).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Accumulator layout of the 256 x 256 kernel's MFMA tiles (edge MT = 16 or 32):
+// element 4*b + e of tile (i, j) in lane l is C row MT*i + 8*b + 4*(l / MT) + e,
+// column MT*j + (l % MT), for b < MT*MT/256 -- runs of four consecutive rows of
+// one column of the column-major C.
+template <int KIND> struct AccShape {
+  static constexpr int MT = Traits<KIND>::mt;
+  static constexpr int NT = kWaveTile / MT;        // tiles per wave edge
+  static constexpr int NB = MT * MT / 256;         // runs of four per lane per tile
+  typedef typename Traits<KIND>::acc_t acc_t;
+};
+
+// Four accumulator elements (one run) -> four 16-bit outputs packed in two words.
 template <int KIND>
-__device__ __forceinline__ void store_c(const Params &p, uint8_t *Cb,
-                                        const float16_t_v (&acc)[kSub][kSub], int64_t m_base,
-                                        int64_t n_base, int lane) {
-  // Accumulator tile (i, j), element e: lane l holds column (l & 31) and rows
-  // 8*(e >> 2) + 4*(l >> 5) + (e & 3), i.e. four runs of four consecutive
-  // elements of one column of the column-major C.
-  const int64_t m_lane = m_base + 4 * (lane >> 5);
-  const int64_t n_lane = n_base + (lane & 31);
+__device__ __forceinline__ void pack_run(const Params &p, const typename Traits<KIND>::acc_t &a,
+                                         int first, uint32_t &w0, uint32_t &w1) {
+  uint16_t h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if constexpr (KIND == kF16) {
+      h[e] = __builtin_bit_cast(uint16_t, (_Float16)a[first + e]);
+    } else {
+      h[e] = __builtin_bit_cast(uint16_t, (__bf16)(a[first + e] * p.scale));
+    }
+  }
+  w0 = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+  w1 = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+}
+
+template <int KIND>
+__device__ __forceinline__ void store_c(
+    const Params &p, uint8_t *Cb,
+    const typename AccShape<KIND>::acc_t (&acc)[AccShape<KIND>::NT][AccShape<KIND>::NT],
+    int64_t m_base, int64_t n_base, int lane) {
+  typedef AccShape<KIND> S;
+  const int64_t m_lane = m_base + 4 * (lane / S::MT);
+  const int64_t n_lane = n_base + (lane % S::MT);
   const bool full = (m_base + kWaveTile <= p.M) && (n_base + kWaveTile <= p.N) && p.c_vec_ok;
 #pragma unroll
-  for (int j = 0; j < kSub; ++j) {
-    const int64_t n = n_lane + kMma * j;
+  for (int j = 0; j < S::NT; ++j) {
+    const int64_t n = n_lane + S::MT * j;
 #pragma unroll
-    for (int i = 0; i < kSub; ++i) {
+    for (int i = 0; i < S::NT; ++i) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t m = m_lane + kMma * i + 8 * b;
-        uint16_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (KIND == kF16) {
-            h[e] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][4 * b + e]);
-          } else {
-            h[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * b + e] * p.scale));
-          }
-        }
-        uint16_t *dst = (uint16_t *)Cb + (n * p.ldc + m);
+      for (int b = 0; b < S::NB; ++b) {
+        const int64_t m = m_lane + S::MT * i + 8 * b;
         uint2 w;
-        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        pack_run<KIND>(p, acc[i][j], 4 * b, w.x, w.y);
+        uint16_t *dst = (uint16_t *)Cb + (n * p.ldc + m);
         if (full) {
           *(uint2 *)dst = w;
         } else if (n < p.N) {
           if (p.c_vec_ok && m + 3 < p.M) {
             *(uint2 *)dst = w;
           } else {
+            const uint16_t h[4] = {(uint16_t)w.x, (uint16_t)(w.x >> 16), (uint16_t)w.y,
+                                   (uint16_t)(w.y >> 16)};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               if (m + e < p.M) dst[e] = h[e];
@@ -254,37 +295,33 @@ __device__ __forceinline__ void store_c(const Params &p, uint8_t *Cb,
 // values and written column-major into the wave's own 32 KiB of LDS (column n
 // at n * 256 B, its 16-byte chunk c stored in slot c ^ (n & 15)), then read
 // back as 16 contiguous bytes (8 rows) per lane, so each global store
-// instruction writes four full 256-byte column segments of C.  Needs 16-byte
-// aligned columns (ldc % 8 == 0); rows or columns past M, N are masked.
+// instruction writes four full 256-byte column segments of C.  The stores are
+// non-temporal: C is not read again here, and keeping it out of L2 leaves the
+// room to the A and B strips.  Needs 16-byte aligned columns (ldc % 8 == 0);
+// rows or columns past M, N are masked.
 template <int KIND>
-__device__ __forceinline__ void store_c_lds(const Params &p, uint8_t *Cb,
-                                            const float16_t_v (&acc)[kSub][kSub],
-                                            __attribute__((address_space(3))) uint8_t *buf,
-                                            int64_t m_base, int64_t n_base, int lane) {
+__device__ __forceinline__ void store_c_lds(
+    const Params &p, uint8_t *Cb,
+    const typename AccShape<KIND>::acc_t (&acc)[AccShape<KIND>::NT][AccShape<KIND>::NT],
+    __attribute__((address_space(3))) uint8_t *buf, int64_t m_base, int64_t n_base, int lane) {
+  typedef AccShape<KIND> S;
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) u32x2 lds_u2;
   typedef __attribute__((address_space(3))) u32x4 lds_u4;
 #pragma unroll
-  for (int j = 0; j < kSub; ++j) {
-    const int n = kMma * j + (lane & 31);
+  for (int j = 0; j < S::NT; ++j) {
+    const int n = S::MT * j + (lane % S::MT);
 #pragma unroll
-    for (int i = 0; i < kSub; ++i) {
+    for (int i = 0; i < S::NT; ++i) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int m = kMma * i + 8 * b + 4 * (lane >> 5);
-        uint16_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (KIND == kF16) {
-            h[e] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][4 * b + e]);
-          } else {
-            h[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * b + e] * p.scale));
-          }
-        }
+      for (int b = 0; b < S::NB; ++b) {
+        const int m = S::MT * i + 8 * b + 4 * (lane / S::MT);
         u32x2 w;
-        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+        uint32_t w0, w1;
+        pack_run<KIND>(p, acc[i][j], 4 * b, w0, w1);
+        w.x = w0;
+        w.y = w1;
         const int chunk = (m >> 3) ^ (n & 15);
         *(lds_u2 *)(buf + n * 256 + chunk * 16 + (m & 7) * 2) = w;
       }
@@ -300,7 +337,7 @@ __device__ __forceinline__ void store_c_lds(const Params &p, uint8_t *Cb,
     const int64_t gm = m_base + 8 * mc, gn = n_base + n;
     uint16_t *dst = (uint16_t *)Cb + (gn * p.ldc + gm);
     if (full || (gn < p.N && gm + 7 < p.M)) {
-      *(u32x4 *)dst = v;
+      __builtin_nontemporal_store(v, (u32x4 *)dst);
     } else if (gn < p.N) {
       const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -345,28 +382,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   const uint32_t qs_a = (uint32_t)(32 * p.lda_b), qs_b = (uint32_t)(32 * p.ldb_b);
   const int kchunk = gchunk * (16 / T::es);           // K offset of the chunk in a step
 
-  // Fragment geometry: lane l reads row (l & 31) of each 32-row MFMA tile and
-  // the 16-byte chunk(s) of its K half (l >> 5).
+  // Fragment geometry: an MFMA operand covers MT rows (tile edge MT = 16 for
+  // fp16, 32 for fp8); lane l reads row l % MT of the tile and its K group
+  // l / MT: for fp16 (16x16x32) the 16-byte chunk 4s + g of the 128-byte row
+  // in sub-step s, for fp8 (32x32x64) the two chunks 4s + 2g + r, r = 0, 1.
+  typedef AccShape<KIND> S;
+  constexpr int MT = S::MT, NT = S::NT;
   const int wm = wave & 1, wn = wave >> 1;
+  const int rl = lane % MT, grp = lane / MT;
   uint32_t a_off[4], b_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // fp16: substep j reads chunk 2j + half; fp8: read j&1 of substep j>>1 for
-    // half h is chunk 4(j>>1) + 2h + (j&1).
-    const int chunk = (T::reads == 1) ? (2 * j + (lane >> 5))
-                                      : (4 * (j >> 1) + 2 * (lane >> 5) + (j & 1));
-    const uint32_t lo = (uint32_t)((lane & 31) * kRowBytes + ((chunk ^ ((lane >> 1) & 7)) * 16));
-    a_off[j] = lo + wm * kWaveTile * kRowBytes;
-    b_off[j] = lo + kStageBytes + wn * kWaveTile * kRowBytes;
+  for (int x = 0; x < T::subs * T::reads; ++x) {
+    const int chunk = (x / T::reads) * (8 / T::subs) + grp * T::reads + (x % T::reads);
+    const uint32_t lo = (uint32_t)(rl * kRowBytes + ((chunk ^ ((rl >> 1) & 7)) * 16));
+    a_off[x] = lo + wm * kWaveTile * kRowBytes;
+    b_off[x] = lo + kStageBytes + wn * kWaveTile * kRowBytes;
   }
 
-  float16_t_v acc[kSub][kSub];
+  typename S::acc_t acc[NT][NT];
 #pragma unroll
-  for (int i = 0; i < kSub; ++i)
+  for (int i = 0; i < NT; ++i)
 #pragma unroll
-    for (int j = 0; j < kSub; ++j)
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < MT * MT / 64; ++e) acc[i][j][e] = 0.f;
 
   // One loop iteration runs two K-steps, stage 0 then stage 1.  An odd K-step
   // count gets one leading step whose chunks all read as zero (adding exact
@@ -393,91 +432,168 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     return c;
   };
 
-  // Per K-step schedule (S substeps x 16 MFMA slots, one MFMA per slot):
-  //  * a substep reads the next substep's eight fragments in its first eight
-  //    slots (A0, B0..B3, A1..A3, in the order they are needed);
-  //  * the last substep instead reaches the barrier after its first eight slots
-  //    (step t+1 has landed everywhere; every wave is done with stage t) and
-  //    then reads step t+1's first fragments from the other stage;
-  //  * step t+2's sixteen copies into the freed stage start right after the
-  //    barrier and are spread over a window of kWin slots (the 8 slots after
-  //    the barrier, then the first kWin - 8 slots of step t+1), at most one per
-  //    slot, so the last one still has part of a step to land before step t+1's
-  //    barrier.  Copy c goes to window position (c * kWin) / 16.
-  constexpr int kSlots = T::subs * kSub * kSub;    // MFMAs per step
-  constexpr int kBar = kSlots - 8;                // barrier before this slot
-  // Copy window (slots), chosen by measurement (fp16 4096^3, fp8 8192^3).
-  constexpr int kWin = (T::reads == 1) ? 32 : 20;
-  static_assert(kWin >= 16 && kWin - 8 <= kBar, "copy window");
-  // Copies [first_copy(x), first_copy(x + 1)) are issued at window position x.
-  auto first_copy = [](int x) { return (x * 16 + kWin - 1) / kWin; };
-  const int kPost = first_copy(8);                // copies issued after the barrier
-
-  typedef typename T::frag_t frag_t;
-  frag_t fa[2][kSub], fb[2][kSub];
-
-  if (nk2 > 0) {
+  // Copies of all of step 0 and the first `post` of step 1, then the barrier
+  // that publishes step 0.
+  auto start = [&](int post) {
     const StepCopy c0 = step_copy(0);
 #pragma unroll
     for (int d = 0; d < 16; ++d) copy_one(c0, d, qs_a, qs_b);
     const StepCopy c1 = step_copy(1);
 #pragma unroll
     for (int d = 0; d < 16; ++d)
-      if (d < kPost) copy_one(c1, d, qs_a, qs_b);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));      // steps 0 (and part of 1) landed
+      if (d < post) copy_one(c1, d, qs_a, qs_b);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    lds_cptr st0 = (lds_cptr)smem;
-#pragma unroll
-    for (int j = 0; j < kSub; ++j) {
-      fa[0][j] = read_frag<KIND>(st0 + j * kMma * kRowBytes, a_off, 0);
-      fb[0][j] = read_frag<KIND>(st0 + j * kMma * kRowBytes, b_off, 0);
-    }
-  }
+  };
+  // The K-step barrier: step t+1's copies have landed for this wave and its
+  // last reads of stage t are complete; once every wave is here, stage t+1 is
+  // published and stage t may be refilled.
+  auto sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & 0xF0FF);  // vmcnt(0), lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  typedef typename T::frag_t frag_t;
+  constexpr int kTileBytes = MT * kRowBytes;      // LDS bytes between MFMA tiles
 
-  for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
+  if constexpr (MT == 16) {
+    // fp16: 8 x 8 MFMA tiles per wave, two 32-deep sub-steps per K-step, 64
+    // MFMA slots per sub-step with MFMA (g, j) in slot 8g + j:
+    //  * B fragments are double-buffered by sub-step; the next sub-step's eight
+    //    are read in slots 11, 13, .., 25;
+    //  * A fragment g (< 7) of the next sub-step goes into the register of the
+    //    current one right after its last use (slot 8g + 8); A_7 alternates
+    //    between two registers by sub-step parity and is read in slot 9;
+    //  * the second sub-step reads nothing before slot 8, so the K-step barrier
+    //    sits there: every read of stage t was issued during the first
+    //    sub-step, and the reads from slot 8 on come from stage t+1;
+    //  * step t+2's sixteen copies into the freed stage follow the barrier,
+    //    one every kWin/16 slots over a window of kWin slots that reaches into
+    //    step t+1, so the last one has most of a step to land.
+    constexpr int kQ = 64, kBarQ = 8, kBarSlot = kQ + kBarQ;
+    constexpr int kWin = 64;                       // about 1000 cycles of MFMA
+    constexpr int kAfter = 2 * kQ - kBarSlot;      // window slots in the barrier's step
+    static_assert(kWin >= 16 && kWin - kAfter <= kBarQ, "copy window");
+    auto first_copy = [](int x) { return (x * 16 + kWin - 1) / kWin; };
+    frag_t fa[8], fx, fb[2][8];
+    if (nk2 > 0) {
+      start(first_copy(kAfter));
+      lds_cptr st0 = (lds_cptr)smem;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {            // K-step t0 + h lives in stage h
-      const int64_t t = t0 + h;
-      const StepCopy cn = step_copy(t + 1);  // remaining copies of step t + 1
-      const StepCopy cnn = step_copy(t + 2); // first copies of step t + 2
-      lds_cptr cur = (lds_cptr)smem + h * 2 * kStageBytes;
-      lds_cptr nxt = (lds_cptr)smem + (1 - h) * 2 * kStageBytes;
+      for (int j = 0; j < 8; ++j) {
+        fb[0][j] = read_frag<KIND>(st0 + j * kTileBytes, b_off, 0);
+        fa[j] = read_frag<KIND>(st0 + j * kTileBytes, a_off, 0);
+      }
+    }
+    for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
 #pragma unroll
-      for (int s = 0; s < T::subs; ++s) {
-        const bool last = (s == T::subs - 1);
-        const int u = s & 1, v = u ^ 1;      // current / next fragment set
+      for (int h = 0; h < 2; ++h) {            // K-step t0 + h lives in stage h
+        const int64_t t = t0 + h;
+        const StepCopy cn = step_copy(t + 1);  // last copies of step t + 1
+        const StepCopy cnn = step_copy(t + 2); // first copies of step t + 2
+        lds_cptr cur = (lds_cptr)smem + h * 2 * kStageBytes;
+        lds_cptr nxt = (lds_cptr)smem + (1 - h) * 2 * kStageBytes;
 #pragma unroll
-        for (int g = 0; g < kSub; ++g) {
+        for (int s = 0; s < 2; ++s) {
+          const bool last = (s == 1);
+          lds_cptr src = last ? nxt : cur;     // where the next sub-step's data is
+          const int s_n = last ? 0 : 1;
 #pragma unroll
-          for (int j = 0; j < kSub; ++j) {
-            const int slot = (s * kSub + g) * kSub + j;
-            const int f = (slot & 15) - (last ? 8 : 0);  // fragment read in this slot
-            if (f >= 0 && f < 8) {
-              lds_cptr src = last ? nxt : cur;
-              const int s_n = last ? 0 : s + 1;
-              if (f == 0) fa[v][0] = read_frag<KIND>(src, a_off, s_n);
-              else if (f <= 4) fb[v][f - 1] = read_frag<KIND>(src + (f - 1) * kMma * kRowBytes, b_off, s_n);
-              else fa[v][f - 4] = read_frag<KIND>(src + (f - 4) * kMma * kRowBytes, a_off, s_n);
+          for (int g = 0; g < 8; ++g) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int q = 8 * g + j;
+              const int slot = kQ * s + q;
+              if (j == 0 && g >= 1) {
+                fa[g - 1] = read_frag<KIND>(src + (g - 1) * kTileBytes, a_off, s_n);
+              } else if (q == 9) {
+                if (s == 0) fx = read_frag<KIND>(src + 7 * kTileBytes, a_off, s_n);
+                else fa[7] = read_frag<KIND>(src + 7 * kTileBytes, a_off, s_n);
+              } else if (q >= 11 && q <= 25 && (q & 1) == 1) {
+                const int jj = (q - 11) / 2;
+                fb[s ^ 1][jj] = read_frag<KIND>(src + jj * kTileBytes, b_off, s_n);
+              }
+              if (slot < kWin - kAfter) {
+                const int x = slot + kAfter;   // at most one copy per slot
+                if (first_copy(x) < first_copy(x + 1)) copy_one(cn, first_copy(x), qs_a, qs_b);
+              } else if (slot >= kBarSlot) {
+                const int x = slot - kBarSlot;
+                if (first_copy(x) < first_copy(x + 1)) copy_one(cnn, first_copy(x), qs_a, qs_b);
+              }
+              if (g == 7 && s == 1) acc[g][j] = mma(fx, fb[s][j], acc[g][j]);
+              else acc[g][j] = mma(fa[g], fb[s][j], acc[g][j]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (last && q == kBarQ - 1) sync();
             }
-            if (slot < kWin - 8) {
-              for (int c = first_copy(slot + 8); c < first_copy(slot + 9); ++c)
-                copy_one(cn, c, qs_a, qs_b);
-            } else if (slot >= kBar) {
-              for (int c = first_copy(slot - kBar); c < first_copy(slot - kBar + 1); ++c)
-                copy_one(cnn, c, qs_a, qs_b);
-            }
-            acc[g][j] = mma(fa[u][g], fb[u][j], acc[g][j]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (slot == kBar - 1) {
-              // Step t+1's copies have landed for this wave and its last reads of
-              // stage h are complete; once every wave is here, stage 1-h is
-              // published and stage h may be refilled.
-              __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & 0xF0FF);  // vmcnt(0), lgkmcnt(0)
-              asm volatile("" ::: "memory");
-              __builtin_amdgcn_s_barrier();
-              asm volatile("" ::: "memory");
+          }
+        }
+      }
+    }
+    mfma_drain();
+  } else {
+    // fp8: 4 x 4 MFMA tiles per wave, two 64-deep sub-steps per K-step, 16
+    // slots per sub-step with MFMA (g, j) in slot 4g + j:
+    //  * a sub-step reads the next sub-step's eight fragments in its first
+    //    eight slots (A0, B0..B3, A1..A3, in the order they are needed), into
+    //    the other half of double-buffered A and B fragment sets;
+    //  * the last sub-step instead reaches the barrier after its first eight
+    //    slots and then reads step t+1's first fragments from the other stage;
+    //  * step t+2's copies start right after the barrier, spread over a window
+    //    of kWin slots (the 8 slots after the barrier, then the first kWin - 8
+    //    slots of step t+1).
+    constexpr int kPer = 16, kSlots = 32, kReads = 8, kBar = kSlots - kReads;
+    constexpr int kWin = 20;                       // chosen by measurement (8192^3)
+    static_assert(kWin >= 16 && kWin - kReads <= kBar, "copy window");
+    auto first_copy = [](int x) { return (x * 16 + kWin - 1) / kWin; };
+    frag_t fa[2][4], fb[2][4];
+    if (nk2 > 0) {
+      start(first_copy(kReads));
+      lds_cptr st0 = (lds_cptr)smem;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        fa[0][j] = read_frag<KIND>(st0 + j * kTileBytes, a_off, 0);
+        fb[0][j] = read_frag<KIND>(st0 + j * kTileBytes, b_off, 0);
+      }
+    }
+    for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t t = t0 + h;
+        const StepCopy cn = step_copy(t + 1);
+        const StepCopy cnn = step_copy(t + 2);
+        lds_cptr cur = (lds_cptr)smem + h * 2 * kStageBytes;
+        lds_cptr nxt = (lds_cptr)smem + (1 - h) * 2 * kStageBytes;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bool last = (s == 1);
+          const int u = s, v = s ^ 1;          // current / next fragment set
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int q = 4 * g + j;
+              const int slot = kPer * s + q;
+              const int f = q - (last ? kPer - kReads : 0);  // fragment read in this slot
+              if (f >= 0 && f < kReads) {
+                lds_cptr src = last ? nxt : cur;
+                const int s_n = last ? 0 : s + 1;
+                if (f == 0) fa[v][0] = read_frag<KIND>(src, a_off, s_n);
+                else if (f <= 4) fb[v][f - 1] = read_frag<KIND>(src + (f - 1) * kTileBytes, b_off, s_n);
+                else fa[v][f - 4] = read_frag<KIND>(src + (f - 4) * kTileBytes, a_off, s_n);
+              }
+              if (slot < kWin - kReads) {
+                const int x = slot + kReads;
+                if (first_copy(x) < first_copy(x + 1)) copy_one(cn, first_copy(x), qs_a, qs_b);
+              } else if (slot >= kBar) {
+                const int x = slot - kBar;
+                if (first_copy(x) < first_copy(x + 1)) copy_one(cnn, first_copy(x), qs_a, qs_b);
+              }
+              acc[g][j] = mma(fa[u][g], fb[u][j], acc[g][j]);
+              __builtin_amdgcn_sched_barrier(0);
+              if (slot == kBar - 1) sync();
             }
           }
         }
