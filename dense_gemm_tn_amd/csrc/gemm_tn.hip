@@ -84,11 +84,11 @@ template <> struct Traits<kF8> {
   static constexpr int es = 1;
   static constexpr int kstep = 128;
   static constexpr int reads = 2;    // 32 bytes of K per lane
-  // 256 x 256 kernel: v_mfma_f32_32x32x64_f8f6f4, two 64-deep sub-steps per K-step.
-  static constexpr int mt = 32;
-  static constexpr int subs = 2;
+  // 256 x 256 kernel: v_mfma_f32_16x16x128_f8f6f4, one 128-deep sub-step per K-step.
+  static constexpr int mt = 16;
+  static constexpr int subs = 1;
   typedef int8_t_v frag_t;
-  typedef float16_t_v acc_t;
+  typedef float4_t_v acc_t;
 };
 
 __device__ __forceinline__ float16_t_v mma(const half8_t &a, const half8_t &b, float16_t_v c) {
@@ -104,6 +104,12 @@ __device__ __forceinline__ float4_t_v mma(const half8_t &a, const half8_t &b, fl
   // the schedule gives them.  Callers leave wait states before reading an
   // accumulator with anything but another MFMA (see mfma_drain).
   asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
+  return c;
+}
+__device__ __forceinline__ float4_t_v mma(const int8_t_v &a, const int8_t_v &b, float4_t_v c) {
+  // v_mfma_f32_16x16x128_f8f6f4 with the default operand formats (FP8 E4M3
+  // for both) and no block scales; in place in AGPRs like the fp16 form.
+  asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
   return c;
 }
 // Wait states after the last MFMA before its accumulators are read by other
@@ -459,147 +465,84 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   typedef typename T::frag_t frag_t;
   constexpr int kTileBytes = MT * kRowBytes;      // LDS bytes between MFMA tiles
 
-  if constexpr (MT == 16) {
-    // fp16: 8 x 8 MFMA tiles per wave, two 32-deep sub-steps per K-step, 64
-    // MFMA slots per sub-step with MFMA (g, j) in slot 8g + j:
-    //  * B fragments are double-buffered by sub-step; the next sub-step's eight
-    //    are read in slots 11, 13, .., 25;
-    //  * A fragment g (< 7) of the next sub-step goes into the register of the
-    //    current one right after its last use (slot 8g + 8); A_7 alternates
-    //    between two registers by sub-step parity and is read in slot 9;
-    //  * the second sub-step reads nothing before slot 8, so the K-step barrier
-    //    sits there: every read of stage t was issued during the first
-    //    sub-step, and the reads from slot 8 on come from stage t+1;
-    //  * step t+2's sixteen copies into the freed stage follow the barrier,
-    //    one every kWin/16 slots over a window of kWin slots that reaches into
-    //    step t+1, so the last one has most of a step to land.
-    constexpr int kQ = 64, kBarQ = 8, kBarSlot = kQ + kBarQ;
-    constexpr int kWin = 64;                       // about 1000 cycles of MFMA
-    constexpr int kAfter = 2 * kQ - kBarSlot;      // window slots in the barrier's step
-    static_assert(kWin >= 16 && kWin - kAfter <= kBarQ, "copy window");
-    auto first_copy = [](int x) { return (x * 16 + kWin - 1) / kWin; };
-    frag_t fa[8], fx, fb[2][8];
-    if (nk2 > 0) {
-      start(first_copy(kAfter));
-      lds_cptr st0 = (lds_cptr)smem;
+  // 8 x 8 MFMA tiles per wave; a K-step is `subs` sub-steps (fp16: two 32-deep,
+  // fp8: one 128-deep) of 64 MFMA slots, MFMA (g, j) in slot 8g + j:
+  //  * B fragments are double-buffered by sub-step parity; the next sub-step's
+  //    eight are read in slots 11, 13, .., 25;
+  //  * A fragment g (< 7) of the next sub-step goes into the register of the
+  //    current one right after its last use (slot 8g + 8); A_7 alternates
+  //    between two registers by sub-step parity and is read in slot 9;
+  //  * the last sub-step of a K-step reads nothing before slot 8, so the
+  //    K-step barrier sits there: every read of stage t was issued earlier,
+  //    and the reads from slot 8 on come from stage t+1;
+  //  * step t+2's sixteen copies into the freed stage follow the barrier,
+  //    spread evenly over a window of kWin slots (which may reach into step
+  //    t+1), so the last one has most of a step to land.
+  static_assert(MT == 16 && NT == 8, "8 x 8 tiles of 16 x 16");
+  constexpr int kQ = 64, kBarQ = 8;
+  constexpr int kBarSlot = (T::subs - 1) * kQ + kBarQ;
+  constexpr int kAfter = T::subs * kQ - kBarSlot;  // window slots in the barrier's step
+  // Copy window in slots (about 1000 cycles of MFMA for either),
+  // chosen by measurement (fp16 4096^3, fp8 8192^3).
+  constexpr int kWin = (KIND == kF16) ? 64 : 32;
+  static_assert(kWin >= 16 && kWin - kAfter <= kBarQ, "copy window");
+  auto first_copy = [](int x) { return (x * 16 + kWin - 1) / kWin; };
+  frag_t fa[8], fx, fb[2][8];
+  if (nk2 > 0) {
+    start(first_copy(kAfter));
+    lds_cptr st0 = (lds_cptr)smem;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        fb[0][j] = read_frag<KIND>(st0 + j * kTileBytes, b_off, 0);
-        fa[j] = read_frag<KIND>(st0 + j * kTileBytes, a_off, 0);
-      }
+    for (int j = 0; j < 8; ++j) {
+      fb[0][j] = read_frag<KIND>(st0 + j * kTileBytes, b_off, 0);
+      fa[j] = read_frag<KIND>(st0 + j * kTileBytes, a_off, 0);
     }
-    for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
+  }
+  for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {            // K-step t0 + h lives in stage h
-        const int64_t t = t0 + h;
-        const StepCopy cn = step_copy(t + 1);  // last copies of step t + 1
-        const StepCopy cnn = step_copy(t + 2); // first copies of step t + 2
-        lds_cptr cur = (lds_cptr)smem + h * 2 * kStageBytes;
-        lds_cptr nxt = (lds_cptr)smem + (1 - h) * 2 * kStageBytes;
+    for (int h = 0; h < 2; ++h) {            // K-step t0 + h lives in stage h
+      const int64_t t = t0 + h;
+      const StepCopy cn = step_copy(t + 1);  // last copies of step t + 1
+      const StepCopy cnn = step_copy(t + 2); // first copies of step t + 2
+      lds_cptr cur = (lds_cptr)smem + h * 2 * kStageBytes;
+      lds_cptr nxt = (lds_cptr)smem + (1 - h) * 2 * kStageBytes;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bool last = (s == 1);
-          lds_cptr src = last ? nxt : cur;     // where the next sub-step's data is
-          const int s_n = last ? 0 : 1;
+      for (int s = 0; s < T::subs; ++s) {
+        const bool last = (s == T::subs - 1);
+        const int par = (h * T::subs + s) & 1;  // sub-step parity
+        lds_cptr src = last ? nxt : cur;       // where the next sub-step's data is
+        const int s_n = last ? 0 : s + 1;
 #pragma unroll
-          for (int g = 0; g < 8; ++g) {
+        for (int g = 0; g < 8; ++g) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int q = 8 * g + j;
-              const int slot = kQ * s + q;
-              if (j == 0 && g >= 1) {
-                fa[g - 1] = read_frag<KIND>(src + (g - 1) * kTileBytes, a_off, s_n);
-              } else if (q == 9) {
-                if (s == 0) fx = read_frag<KIND>(src + 7 * kTileBytes, a_off, s_n);
-                else fa[7] = read_frag<KIND>(src + 7 * kTileBytes, a_off, s_n);
-              } else if (q >= 11 && q <= 25 && (q & 1) == 1) {
-                const int jj = (q - 11) / 2;
-                fb[s ^ 1][jj] = read_frag<KIND>(src + jj * kTileBytes, b_off, s_n);
-              }
-              if (slot < kWin - kAfter) {
-                const int x = slot + kAfter;   // at most one copy per slot
-                if (first_copy(x) < first_copy(x + 1)) copy_one(cn, first_copy(x), qs_a, qs_b);
-              } else if (slot >= kBarSlot) {
-                const int x = slot - kBarSlot;
-                if (first_copy(x) < first_copy(x + 1)) copy_one(cnn, first_copy(x), qs_a, qs_b);
-              }
-              if (g == 7 && s == 1) acc[g][j] = mma(fx, fb[s][j], acc[g][j]);
-              else acc[g][j] = mma(fa[g], fb[s][j], acc[g][j]);
-              __builtin_amdgcn_sched_barrier(0);
-              if (last && q == kBarQ - 1) sync();
+          for (int j = 0; j < 8; ++j) {
+            const int q = 8 * g + j;
+            const int slot = kQ * s + q;
+            if (j == 0 && g >= 1) {
+              fa[g - 1] = read_frag<KIND>(src + (g - 1) * kTileBytes, a_off, s_n);
+            } else if (q == 9) {
+              if (par == 0) fx = read_frag<KIND>(src + 7 * kTileBytes, a_off, s_n);
+              else fa[7] = read_frag<KIND>(src + 7 * kTileBytes, a_off, s_n);
+            } else if (q >= 11 && q <= 25 && (q & 1) == 1) {
+              const int jj = (q - 11) / 2;
+              fb[par ^ 1][jj] = read_frag<KIND>(src + jj * kTileBytes, b_off, s_n);
             }
-          }
-        }
-      }
-    }
-    mfma_drain();
-  } else {
-    // fp8: 4 x 4 MFMA tiles per wave, two 64-deep sub-steps per K-step, 16
-    // slots per sub-step with MFMA (g, j) in slot 4g + j:
-    //  * a sub-step reads the next sub-step's eight fragments in its first
-    //    eight slots (A0, B0..B3, A1..A3, in the order they are needed), into
-    //    the other half of double-buffered A and B fragment sets;
-    //  * the last sub-step instead reaches the barrier after its first eight
-    //    slots and then reads step t+1's first fragments from the other stage;
-    //  * step t+2's copies start right after the barrier, spread over a window
-    //    of kWin slots (the 8 slots after the barrier, then the first kWin - 8
-    //    slots of step t+1).
-    constexpr int kPer = 16, kSlots = 32, kReads = 8, kBar = kSlots - kReads;
-    constexpr int kWin = 20;                       // chosen by measurement (8192^3)
-    static_assert(kWin >= 16 && kWin - kReads <= kBar, "copy window");
-    auto first_copy = [](int x) { return (x * 16 + kWin - 1) / kWin; };
-    frag_t fa[2][4], fb[2][4];
-    if (nk2 > 0) {
-      start(first_copy(kReads));
-      lds_cptr st0 = (lds_cptr)smem;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        fa[0][j] = read_frag<KIND>(st0 + j * kTileBytes, a_off, 0);
-        fb[0][j] = read_frag<KIND>(st0 + j * kTileBytes, b_off, 0);
-      }
-    }
-    for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int64_t t = t0 + h;
-        const StepCopy cn = step_copy(t + 1);
-        const StepCopy cnn = step_copy(t + 2);
-        lds_cptr cur = (lds_cptr)smem + h * 2 * kStageBytes;
-        lds_cptr nxt = (lds_cptr)smem + (1 - h) * 2 * kStageBytes;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bool last = (s == 1);
-          const int u = s, v = s ^ 1;          // current / next fragment set
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int q = 4 * g + j;
-              const int slot = kPer * s + q;
-              const int f = q - (last ? kPer - kReads : 0);  // fragment read in this slot
-              if (f >= 0 && f < kReads) {
-                lds_cptr src = last ? nxt : cur;
-                const int s_n = last ? 0 : s + 1;
-                if (f == 0) fa[v][0] = read_frag<KIND>(src, a_off, s_n);
-                else if (f <= 4) fb[v][f - 1] = read_frag<KIND>(src + (f - 1) * kTileBytes, b_off, s_n);
-                else fa[v][f - 4] = read_frag<KIND>(src + (f - 4) * kTileBytes, a_off, s_n);
-              }
-              if (slot < kWin - kReads) {
-                const int x = slot + kReads;
-                if (first_copy(x) < first_copy(x + 1)) copy_one(cn, first_copy(x), qs_a, qs_b);
-              } else if (slot >= kBar) {
-                const int x = slot - kBar;
-                if (first_copy(x) < first_copy(x + 1)) copy_one(cnn, first_copy(x), qs_a, qs_b);
-              }
-              acc[g][j] = mma(fa[u][g], fb[u][j], acc[g][j]);
-              __builtin_amdgcn_sched_barrier(0);
-              if (slot == kBar - 1) sync();
+            if (slot < kWin - kAfter) {
+              const int x = slot + kAfter;     // at most one copy per slot
+              if (first_copy(x) < first_copy(x + 1)) copy_one(cn, first_copy(x), qs_a, qs_b);
+            } else if (slot >= kBarSlot && slot - kBarSlot < kWin) {
+              const int x = slot - kBarSlot;
+              if (first_copy(x) < first_copy(x + 1)) copy_one(cnn, first_copy(x), qs_a, qs_b);
             }
+            if (g == 7 && par == 1) acc[g][j] = mma(fx, fb[par][j], acc[g][j]);
+            else acc[g][j] = mma(fa[g], fb[par][j], acc[g][j]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (last && q == kBarQ - 1) sync();
           }
         }
       }
     }
   }
+  mfma_drain();
 
   // Drain the trailing zero copies; every wave leaves the stages before the
   // epilogue reuses the LDS.
