@@ -420,21 +420,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   const int64_t pad = nk & 1;
   const int64_t nk2 = nk + pad;
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
-  auto step_copy = [&](int64_t t) {
-    // Steps outside the matrix (the leading pad step, and the steps past the end
-    // issued unconditionally by the last iterations) read zeros and touch no memory.
+  // Copy plan of step t, in three parts so the main loop can spread its
+  // instructions over three MFMA slots.  Steps outside the matrix (the leading
+  // pad step, and the steps past the end issued unconditionally by the last
+  // iterations) read zeros and touch no memory.
+  struct StepScalars {
+    uint32_t kb;   // byte offset of the step's K range
+    int left;      // K elements of the step inside the matrix (0 .. kstep)
+    int stage;
+  };
+  auto step_scalars = [&](int64_t t) {
     const int64_t k0 = (t - pad) * T::kstep;
     const bool inside = (k0 >= 0) && (t < nk2);
-    const uint32_t kb = inside ? (uint32_t)(k0 * T::es) : 0u;
-    const bool valid = inside && (kchunk < p.K - k0);
-    lds_u8 *st = (lds_u8 *)smem + (int)(t & 1) * 2 * kStageBytes + wave * 1024;
-    StepCopy c;
-    c.ra = make_rsrc(Ab + kb, rec_a - kb);
-    c.rb = make_rsrc(Bb + kb, rec_b - kb);
-    c.va = valid ? voff_a : kOob;
-    c.vb = valid ? voff_b : kOob;
+    const int64_t rem = p.K - k0;
+    StepScalars u;
+    u.kb = inside ? (uint32_t)(k0 * T::es) : 0u;
+    u.left = !inside ? 0 : (rem >= T::kstep ? T::kstep : (int)rem);
+    u.stage = (int)(t & 1);
+    return u;
+  };
+  auto step_rsrc = [&](const StepScalars &u, StepCopy &c) {
+    c.ra = make_rsrc(Ab + u.kb, rec_a - u.kb);
+    c.rb = make_rsrc(Bb + u.kb, rec_b - u.kb);
+    lds_u8 *st = (lds_u8 *)smem + u.stage * 2 * kStageBytes + wave * 1024;
     c.la = st;
     c.lb = st + kStageBytes;
+  };
+  auto step_lanes = [&](const StepScalars &u, StepCopy &c) {
+    const bool valid = kchunk < u.left;   // this lane's chunk is inside K
+    c.va = valid ? voff_a : kOob;
+    c.vb = valid ? voff_b : kOob;
+  };
+  auto step_copy = [&](int64_t t) {
+    const StepScalars u = step_scalars(t);
+    StepCopy c;
+    step_rsrc(u, c);
+    step_lanes(u, c);
     return c;
   };
 
@@ -497,12 +518,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
       fa[j] = read_frag<KIND>(st0 + j * kTileBytes, a_off, 0);
     }
   }
+  // cn: copies of step t + 1 (its last ones are issued early in step t);
+  // cnn: step t + 2's, planned in slots kPlan .. kPlan + 2 of step t.
+  StepCopy cn = step_copy(1), cnn;
+  StepScalars un;
+  constexpr int kPlan = kBarSlot - 6;
+  static_assert(kPlan >= kWin - kAfter, "plan after the last copy of step t + 1");
   for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {            // K-step t0 + h lives in stage h
       const int64_t t = t0 + h;
-      const StepCopy cn = step_copy(t + 1);  // last copies of step t + 1
-      const StepCopy cnn = step_copy(t + 2); // first copies of step t + 2
       lds_cptr cur = (lds_cptr)smem + h * 2 * kStageBytes;
       lds_cptr nxt = (lds_cptr)smem + (1 - h) * 2 * kStageBytes;
 #pragma unroll
@@ -526,6 +551,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
               const int jj = (q - 11) / 2;
               fb[par ^ 1][jj] = read_frag<KIND>(src + jj * kTileBytes, b_off, s_n);
             }
+            if (slot == kPlan) un = step_scalars(t + 2);
+            if (slot == kPlan + 1) step_rsrc(un, cnn);
+            if (slot == kPlan + 2) step_lanes(un, cnn);
             if (slot < kWin - kAfter) {
               const int x = slot + kAfter;     // at most one copy per slot
               if (first_copy(x) < first_copy(x + 1)) copy_one(cn, first_copy(x), qs_a, qs_b);
@@ -540,6 +568,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
           }
         }
       }
+      cn = cnn;
     }
   }
   mfma_drain();
