@@ -388,10 +388,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   const uint32_t qs_a = (uint32_t)(32 * p.lda_b), qs_b = (uint32_t)(32 * p.ldb_b);
   const int kchunk = gchunk * (16 / T::es);           // K offset of the chunk in a step
 
-  // Fragment geometry: an MFMA operand covers MT rows (tile edge MT = 16 for
-  // fp16, 32 for fp8); lane l reads row l % MT of the tile and its K group
-  // l / MT: for fp16 (16x16x32) the 16-byte chunk 4s + g of the 128-byte row
-  // in sub-step s, for fp8 (32x32x64) the two chunks 4s + 2g + r, r = 0, 1.
+  // Fragment geometry: an MFMA operand covers 16 rows; lane l reads row l % 16
+  // of the tile and serves K group g = l / 16 of the instruction.  fp16
+  // (16x16x32): the 16-byte chunk 4s + g of the 128-byte row in sub-step s.
+  // fp8 (16x16x128): the chunks g and g + 4, so that, as for fp16, the 16
+  // lanes of a ds_read_b128 phase read one chunk of 16 consecutive rows (with
+  // chunks 2g and 2g + 1 the reads bank-conflicted).  A and B use the same
+  // map, so each instruction still pairs equal K indices.
   typedef AccShape<KIND> S;
   constexpr int MT = S::MT, NT = S::NT;
   const int wm = wave & 1, wn = wave >> 1;
@@ -399,7 +402,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   uint32_t a_off[4], b_off[4];
 #pragma unroll
   for (int x = 0; x < T::subs * T::reads; ++x) {
-    const int chunk = (x / T::reads) * (8 / T::subs) + grp * T::reads + (x % T::reads);
+    const int chunk = (x / T::reads) * (8 / T::subs) + grp + 4 * (x % T::reads);
     const uint32_t lo = (uint32_t)(rl * kRowBytes + ((chunk ^ ((rl >> 1) & 7)) * 16));
     a_off[x] = lo + wm * kWaveTile * kRowBytes;
     b_off[x] = lo + kStageBytes + wn * kWaveTile * kRowBytes;
