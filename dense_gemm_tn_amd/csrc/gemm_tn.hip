@@ -41,6 +41,8 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "dense_gemm_tn.h"
 
 namespace dg {
@@ -136,6 +138,7 @@ struct Params {
   float scale;           // fp8 only: fp32(scale_a * scale_b)
   int32_t c_vec_ok;      // 8-byte C stores are aligned (ldc % 4 == 0)
   int32_t c_vec16_ok;    // 16-byte C stores are aligned (ldc % 8 == 0)
+  int32_t sk_walk;       // skinny-K kernel: consecutive M tiles per block
 };
 
 // Logical tile -> (head, tile_m, tile_n): the grouped order inside a head,
@@ -603,6 +606,7 @@ constexpr int kSkRow = 256;        // LDS bytes per row (all of K, zero-filled)
 constexpr int kSkStrip = kSkTile * kSkRow;  // 32 KiB per operand
 constexpr int kSkWave = 64;        // each wave owns 64 x 64 of C
 constexpr int kSkSub = 2;          // MFMA tiles per wave edge
+constexpr int kSkWalkMax = 32;     // most M tiles one block walks
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -614,30 +618,43 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // fills rows 16q + 4w .. +3 (1 KiB): lane l lands in row 16q + 4w + (l >> 4),
 // slot l & 15.  Chunks at or past K are pointed out of range and read zero.
 template <int KIND>
-__device__ __forceinline__ void sk_copy(const Params &p, lds_u8 *stage, int head, int tm, int tn,
-                                        int wave, int lane) {
+__device__ __forceinline__ void sk_copy_strip(const Params &p, lds_u8 *strip, const uint8_t *base,
+                                              int64_t ld_b, int64_t rows, int wave, int lane) {
   typedef Traits<KIND> T;
-  const int64_t m0 = (int64_t)tm * kSkTile, n0 = (int64_t)tn * kSkTile;
-  const uint8_t *Ab = p.A + head * p.stride_a_b + m0 * p.lda_b;
-  const uint8_t *Bb = p.B + head * p.stride_b_b + n0 * p.ldb_b;
-  const int64_t rows_a = (p.M - m0) < kSkTile ? (p.M - m0) : kSkTile;
-  const int64_t rows_b = (p.N - n0) < kSkTile ? (p.N - n0) : kSkTile;
   const uint32_t kbytes = (uint32_t)(p.K * T::es);
   const int crow = 4 * wave + (lane >> 4);
   const int gchunk = (lane & 15) ^ (crow & 15);
   const bool valid = gchunk * 16 < (int)kbytes;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab, (uint32_t)((rows_a - 1) * p.lda_b) + kbytes);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb, (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes);
-  const uint32_t va = valid ? (uint32_t)(crow * p.lda_b) + gchunk * 16 : kOob;
-  const uint32_t vb = valid ? (uint32_t)(crow * p.ldb_b) + gchunk * 16 : kOob;
-  lds_u8 *la = stage + wave * 1024;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint32_t)((rows - 1) * ld_b) + kbytes);
+  const uint32_t v = valid ? (uint32_t)(crow * ld_b) + gchunk * 16 : kOob;
+  lds_u8 *l = strip + wave * 1024;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(la + q * 4096), 16,
-                                             va + q * (uint32_t)(16 * p.lda_b), 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(la + kSkStrip + q * 4096), 16,
-                                             vb + q * (uint32_t)(16 * p.ldb_b), 0, 0, 0);
-  }
+  for (int q = 0; q < 8; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(l + q * 4096), 16,
+                                             v + q * (uint32_t)(16 * ld_b), 0, 0, 0);
+}
+
+// Copies of A's strip for tile row tm and of B's strip for tile column tn
+// (128 rows x 256 B each, rows of 256 B, chunk c of row r in slot c ^ (r & 15),
+// so a 16-row ds_read_b128 phase hits 16 distinct slots of the bank period).
+// Load q (0..7) of wave w fills rows 16q + 4w .. +3 (1 KiB): lane l lands in
+// row 16q + 4w + (l >> 4), slot l & 15.  Chunks at or past K are pointed out of
+// range and read zero.
+template <int KIND>
+__device__ __forceinline__ void sk_copy_a(const Params &p, lds_u8 *strip, int head, int tm,
+                                          int wave, int lane) {
+  const int64_t m0 = (int64_t)tm * kSkTile;
+  const int64_t rows = (p.M - m0) < kSkTile ? (p.M - m0) : kSkTile;
+  sk_copy_strip<KIND>(p, strip, p.A + head * p.stride_a_b + m0 * p.lda_b, p.lda_b, rows, wave,
+                      lane);
+}
+template <int KIND>
+__device__ __forceinline__ void sk_copy_b(const Params &p, lds_u8 *strip, int head, int tn,
+                                          int wave, int lane) {
+  const int64_t n0 = (int64_t)tn * kSkTile;
+  const int64_t rows = (p.N - n0) < kSkTile ? (p.N - n0) : kSkTile;
+  sk_copy_strip<KIND>(p, strip, p.B + head * p.stride_b_b + n0 * p.ldb_b, p.ldb_b, rows, wave,
+                      lane);
 }
 
 // The wave's 64 x 64 block of A x B from a stage (substeps of 32 B of K: one
@@ -724,45 +741,68 @@ __device__ __forceinline__ void sk_to_lds(const Params &p, const float16_t_v (&a
   }
 }
 
-// One tile per block (two blocks per CU).
+// A block walks p.sk_walk consecutive M tiles of one tile column (two blocks
+// per CU).  B's strip is copied once and stays in LDS; per tile: A's strip
+// lands, MFMAs, the 128 x 128 result is transposed through the A space and
+// read back into registers, then the next A strip is requested and the tile's
+// stores are issued, so the copy overlaps the stores.
 template <int KIND>
 __global__ __launch_bounds__(kThreads, 2) void gemm_tn_skinny_kernel(Params p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kSkStrip];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kSkStrip];  // [A strip | B strip]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int head, tm, tn;
-  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
+  const int chunks_m = (p.tiles_m + p.sk_walk - 1) / p.sk_walk;
+  int head, tmc, tn;
+  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, chunks_m, p.tiles_n, &head, &tmc, &tn);
+  const int tm0 = tmc * p.sk_walk;
+  const int tm_end = (tm0 + p.sk_walk) < p.tiles_m ? (tm0 + p.sk_walk) : p.tiles_m;
+  lds_u8 *const a_st = (lds_u8 *)smem;
+  lds_u8 *const b_st = (lds_u8 *)smem + kSkStrip;
   // (K = 0 still copies: every chunk is then out of range and reads zero.)
-  sk_copy<KIND>(p, (lds_u8 *)smem, head, tm, tn, wave, lane);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();
+  sk_copy_b<KIND>(p, b_st, head, tn, wave, lane);
+  sk_copy_a<KIND>(p, a_st, head, tm0, wave, lane);
   const int wm = wave & 1, wn = wave >> 1;
-  float16_t_v acc[kSkSub][kSkSub];
-  sk_compute<KIND>(acc, (lds_cptr)smem, wm, wn, lane);
-  __syncthreads();  // every wave is done reading the strips
-  lds_u8 *buf = (lds_u8 *)smem + wave * 8192;
-  sk_to_lds<KIND>(p, acc, buf, lane);
+  lds_u8 *buf = a_st + wave * 8192;   // this wave's transpose buffer (A space)
   uint8_t *Cb = p.C + head * p.stride_c_b;
-  const int64_t m_base = (int64_t)tm * kSkTile + wm * kSkWave;
   const int64_t n_base = (int64_t)tn * kSkTile + wn * kSkWave;
-  const bool full = (m_base + kSkWave <= p.M) && (n_base + kSkWave <= p.N) && p.c_vec16_ok;
+  for (int tm = tm0; tm < tm_end; ++tm) {
+    // This tile's A strip (and, first time round, B's) has landed; the wait
+    // also covers the previous tile's stores.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    float16_t_v acc[kSkSub][kSkSub];
+    sk_compute<KIND>(acc, (lds_cptr)smem, wm, wn, lane);
+    __syncthreads();  // every wave is done reading A's strip
+    sk_to_lds<KIND>(p, acc, buf, lane);
+    u32x4 v[8];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int n = 8 * r + (lane >> 3);
-    const int mc = lane & 7;
-    const u32x4 v = *(__attribute__((address_space(3))) u32x4 *)(buf + n * 128 + ((mc ^ (n & 7)) * 16));
-    const int64_t gm = m_base + 8 * mc, gn = n_base + n;
-    uint16_t *dst = (uint16_t *)Cb + (gn * p.ldc + gm);
-    if (full || (p.c_vec16_ok && gn < p.N && gm + 7 < p.M)) {
-      // Non-temporal: C is written once and never read here, and letting it
-      // allocate in L2 evicts the Q and K strips that later tiles re-read.
-      __builtin_nontemporal_store(v, (u32x4 *)dst);
-    } else if (gn < p.N) {
-      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    for (int r = 0; r < 8; ++r) {
+      const int n = 8 * r + (lane >> 3);
+      const int mc = lane & 7;
+      v[r] = *(__attribute__((address_space(3))) u32x4 *)(buf + n * 128 + ((mc ^ (n & 7)) * 16));
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the A space are done
+    __syncthreads();                     // everyone's are: the next A strip may land
+    if (tm + 1 < tm_end) sk_copy_a<KIND>(p, a_st, head, tm + 1, wave, lane);
+    const int64_t m_base = (int64_t)tm * kSkTile + wm * kSkWave;
+    const bool full = (m_base + kSkWave <= p.M) && (n_base + kSkWave <= p.N) && p.c_vec16_ok;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (gm + e < p.M) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+    for (int r = 0; r < 8; ++r) {
+      const int n = 8 * r + (lane >> 3);
+      const int mc = lane & 7;
+      const int64_t gm = m_base + 8 * mc, gn = n_base + n;
+      uint16_t *dst = (uint16_t *)Cb + (gn * p.ldc + gm);
+      if (full || (p.c_vec16_ok && gn < p.N && gm + 7 < p.M)) {
+        // Non-temporal: C is written once and never read here, and letting it
+        // allocate in L2 evicts the Q and K strips that later tiles re-read.
+        __builtin_nontemporal_store(v[r], (u32x4 *)dst);
+      } else if (gn < p.N) {
+        const uint32_t wv[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (gm + e < p.M) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+      }
     }
   }
 }
@@ -780,6 +820,21 @@ static bool overlaps(const void *a, uint64_t abytes, const void *b, uint64_t bby
 }
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Compute units of the current device, looked up once per device (256 on
+// MI355X; that value is assumed if the query fails).
+static int cu_count() {
+  static std::atomic<int> cached[64];  // zero-initialised; racing writers store the same value
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // Bytes spanned by `rows` rows of `row_elems` elements at stride `ld` (0 if empty).
 static uint64_t span_bytes(int64_t rows, int64_t row_elems, int64_t ld, int es) {
@@ -835,7 +890,16 @@ static int launch(const Problem &pr, hipStream_t stream) {
   const int64_t tile = skinny ? kSkTile : kTile;
   const int64_t tiles_m = (pr.M + tile - 1) / tile;
   const int64_t tiles_n = (pr.N + tile - 1) / tile;
-  const int64_t blocks = tiles_m * tiles_n * pr.batch;
+  // Skinny-K blocks walk up to kSkWalkMax M tiles of one column (each walk
+  // step saves a copy of B's strip), halved while that would leave fewer than
+  // eight blocks per CU.
+  int64_t walk = 1;
+  if (skinny) {
+    const int64_t want = 8 * (int64_t)cu_count();
+    walk = tiles_m < kSkWalkMax ? tiles_m : kSkWalkMax;
+    while (walk > 1 && ((tiles_m + walk - 1) / walk) * tiles_n * pr.batch < want) walk = (walk + 1) / 2;
+  }
+  const int64_t blocks = ((tiles_m + walk - 1) / walk) * tiles_n * pr.batch;
   if (blocks > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;
 
   Params p;
@@ -849,6 +913,7 @@ static int launch(const Problem &pr, hipStream_t stream) {
   p.scale = pr.scale;
   p.c_vec_ok = (pr.ldc % 4 == 0) ? 1 : 0;
   p.c_vec16_ok = (pr.ldc % 8 == 0) ? 1 : 0;
+  p.sk_walk = (int32_t)walk;
 
   if (skinny)
     hipLaunchKernelGGL(gemm_tn_skinny_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0,

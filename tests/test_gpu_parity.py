@@ -205,8 +205,8 @@ def test_batched_qkt_small():
 @pytest.mark.parametrize("H,M,N,D,pad", [(12, 640, 520, 128, 0), (12, 640, 520, 64, 8),
                                          (2, 1024, 2048, 128, 0), (3, 136, 264, 32, 16)])
 def test_batched_qkt_many_tiles(H, M, N, D, pad):
-    """More 128 x 128 tiles than CUs (the persistent skinny-K form walks several
-    tiles per block), N tails, a padded lds, and a K shorter than the LDS row."""
+    """More 128 x 128 tiles than CUs, N tails, a padded lds, and a K shorter
+    than the LDS row (grids this small give every block a single M tile)."""
     x = inputs.make_shape("qkt", M, N, D, dist="pm1", seed=H + M + D, batch=H)
     q, k = _dev(x["Q"]), _dev(x["K"])
     lds = M + pad
@@ -218,6 +218,32 @@ def test_batched_qkt_many_tiles(H, M, N, D, pad):
     for h in range(H):
         assert_exact("qkt", np.ascontiguousarray(got[h, :, :M]), ref[h])
         assert np.all(got[h, :, M:] == CANARY16)
+
+
+@pytest.mark.parametrize("H,M,N,D,pad", [(64, 4000, 3000, 128, 8), (8, 8152, 1000, 64, 0)])
+def test_batched_qkt_walks(H, M, N, D, pad):
+    """Grids of at least eight skinny-K blocks per CU, where each block walks
+    several M tiles of one column (16 and 2 here) and the walk ends on a ragged
+    M tile; +-1 data, so sampled entries are exact, and the lds padding keeps
+    its canaries."""
+    x = inputs.make_shape("qkt", M, N, D, dist="pm1", seed=H + M, batch=H)
+    q, k = _dev(x["Q"]), _dev(x["K"])
+    lds = M + pad
+    s = torch.full((H, N, lds), CANARY16, dtype=torch.int32, device=DEV).to(torch.int16)
+    dg.gemm_batched_qkt(q, k, s, H, M, N, D, D, D, lds, M * D, N * D, N * lds)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for h in sorted({0, H - 1} | set(rng.integers(0, H, 3).tolist())):
+        ms, ns = sample_entries(M, N, 400, seed=h)
+        ms = np.concatenate([ms, np.arange(M - 130, M)])  # the last, ragged M tile
+        ns = np.concatenate([ns, np.full(130, N - 1)])
+        ref = oracle.gemm_tn_entries(x["Q"][h], x["K"][h], oracle.FMT_F16, D, ms, ns)
+        got = s[h].cpu().numpy().view(np.uint16)
+        assert_exact("qkt", got[ns, ms], ref)
+        if pad:
+            assert np.all(got[:, M:] == CANARY16)
+    del s
+    torch.cuda.empty_cache()
 
 
 # ------------------------------------------------------------- full-size workloads
