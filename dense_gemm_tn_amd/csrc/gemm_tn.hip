@@ -5,14 +5,16 @@
 // RDNA 3 and RDNA 4", section "What we compute", and the dot-product equation of
 // "hello-gpu, chapter 11 (GEMM-like)", section 11.1.
 //
-// Kernel design (one family, fp16 and fp8 instantiations, optional head index):
+// Kernel design.  Two kernel families, each with fp16 and fp8 instantiations
+// and an optional head index:
+//
+// gemm_tn_kernel (K * es > 256 bytes):
 //   * 256 x 256 output tile per workgroup, 4 waves (one per SIMD), each wave owns
-//     a 128 x 128 quarter held as 4 x 4 MFMA 32x32 accumulator tiles (256
-//     accumulator registers per lane) -- the 4-wave layout of the MI355X FP8
-//     GEMM page, section "why 4 waves".  The matrix-core shapes are
-//     v_mfma_f32_32x32x16_f16 and v_mfma_f32_32x32x64_f8f6f4: on gfx950 the
-//     32x32x16 fp16 shape retires twice the flops per cycle of 16x16x32 (measured
-//     with a register-only probe), and the fp8 shapes run at the same rate.
+//     a 128 x 128 quarter as 8 x 8 MFMA tiles of 16 x 16 (256 accumulator
+//     registers per lane) -- the 4-wave layout of the MI355X FP8 GEMM page,
+//     section "why 4 waves", with its 16x16 matrix-core shapes
+//     (v_mfma_f32_16x16x32_f16, v_mfma_f32_16x16x128_f8f6f4), which sustain a
+//     higher clock under load than the 32x32 shapes.
 //   * A K-step moves 128 bytes of K per row (64 fp16 or 128 fp8 elements):
 //     256 rows x 128 B of A and of B per stage, two stages in LDS (128 KiB).
 //   * Global -> LDS copies are buffer loads that write LDS directly (no VGPR
@@ -24,19 +26,24 @@
 //     c ^ ((r >> 1) & 7), the XOR swizzle of the MI355X FP8 GEMM page (section
 //     "XOR swizzle"), so the 16 rows read by one ds_read_b128 phase hit 16
 //     distinct 16-byte bank groups of the 256-byte bank period.
-//   * Fragments are software-pipelined in registers (the prefetch interleaving
-//     of "FP16 GEMM optimisation ...", Step 7, and the MFMA / ds_read
-//     interleave of the MI355X FP8 GEMM page): A fragments in a ring read two
-//     MFMA groups ahead, B fragments double-buffered per substep, one barrier
-//     per K-step placed mid-substep; sched_barrier pins the order.
+//   * One MFMA per schedule slot, with fragment reads and copies in fixed slots
+//     (the prefetch interleaving of "FP16 GEMM optimisation ...", Step 7, and
+//     the MFMA / ds_read interleave of the MI355X FP8 GEMM page): fragments of
+//     the next sub-step are read while the current one computes, one barrier
+//     per K-step; sched_barrier pins the order.
 //   * Block ids are remapped so each XCD (workgroups are dealt round-robin over
 //     the 8 XCDs) receives a contiguous range of tiles, and that range is walked
 //     in the grouped order of "FP16 GEMM optimisation ...", Step 6 (groups of 8
 //     tile rows), so the blocks co-resident on one XCD share A and B strips in
 //     its L2 (the chiplet-aware remap of the MI355X FP8 GEMM page).
 //   * Epilogue: fp32 -> fp16 (round to nearest even) or fp32 * (sa*sb) -> bf16
-//     (round to nearest even), masked column-major stores that never touch C
-//     outside its M x N logical extent (section 11.4 of the hello-gpu chapter).
+//     (round to nearest even), transposed through LDS into whole column runs,
+//     masked column-major stores that never touch C outside its M x N logical
+//     extent (section 11.4 of the hello-gpu chapter).
+//
+// gemm_tn_skinny_kernel (K * es <= 256 bytes, e.g. QK^T with head dim 128):
+//   all of K fits one LDS row, so there is no K pipeline; blocks walk a column
+//   of 128 x 128 tiles with B's strip resident, bound by writing C.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -465,21 +472,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     return c;
   };
 
-  // Copies of all of step 0 and the first `post` of step 1, then the barrier
-  // that publishes step 0.
-  auto start = [&](int post) {
-    const StepCopy c0 = step_copy(0);
-#pragma unroll
-    for (int d = 0; d < 16; ++d) copy_one(c0, d, qs_a, qs_b);
-    const StepCopy c1 = step_copy(1);
-#pragma unroll
-    for (int d = 0; d < 16; ++d)
-      if (d < post) copy_one(c1, d, qs_a, qs_b);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
   // The K-step barrier: step t+1's copies have landed for this wave and its
   // last reads of stage t are complete; once every wave is here, stage t+1 is
   // published and stage t may be refilled.
@@ -514,9 +506,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   constexpr int kWin = (KIND == kF16) ? 64 : 32;
   static_assert(kWin >= 16 && kWin - kAfter <= kBarQ, "copy window");
   auto first_copy = [](int x) { return (x * 16 + kWin - 1) / kWin; };
+  constexpr int kPost = (kAfter * 16 + kWin - 1) / kWin;  // first_copy(kAfter)
   frag_t fa[8], fx, fb[2][8];
   if (nk2 > 0) {
-    start(first_copy(kAfter));
+    // Copies of all of step 0 and the first kPost of step 1; wait for step 0
+    // only (loads complete in order) and publish it.
+    const StepCopy c0 = step_copy(0);
+#pragma unroll
+    for (int d = 0; d < 16; ++d) copy_one(c0, d, qs_a, qs_b);
+    const StepCopy c1 = step_copy(1);
+#pragma unroll
+    for (int d = 0; d < kPost; ++d) copy_one(c1, d, qs_a, qs_b);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPost));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     lds_cptr st0 = (lds_cptr)smem;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
