@@ -245,9 +245,10 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // element 4*b + e of tile (i, j) in lane l is C row MT*i + 8*b + 4*(l / MT) + e,
 // column MT*j + (l % MT), for b < MT*MT/256 -- runs of four consecutive rows of
 // one column of the column-major C.
-template <int KIND> struct AccShape {
+template <int KIND, int NTN> struct AccShape {
   static constexpr int MT = Traits<KIND>::mt;
-  static constexpr int NT = kWaveTile / MT;        // tiles per wave edge
+  static constexpr int NTM = kWaveTile / MT;       // tiles per wave along M
+  static constexpr int WN = MT * NTN;              // wave tile width (columns)
   static constexpr int NB = MT * MT / 256;         // runs of four per lane per tile
   typedef typename Traits<KIND>::acc_t acc_t;
 };
@@ -269,20 +270,20 @@ __device__ __forceinline__ void pack_run(const Params &p, const typename Traits<
   w1 = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
 }
 
-template <int KIND>
+template <int KIND, int NTN>
 __device__ __forceinline__ void store_c(
     const Params &p, uint8_t *Cb,
-    const typename AccShape<KIND>::acc_t (&acc)[AccShape<KIND>::NT][AccShape<KIND>::NT],
+    const typename AccShape<KIND, NTN>::acc_t (&acc)[AccShape<KIND, NTN>::NTM][NTN],
     int64_t m_base, int64_t n_base, int lane) {
-  typedef AccShape<KIND> S;
+  typedef AccShape<KIND, NTN> S;
   const int64_t m_lane = m_base + 4 * (lane / S::MT);
   const int64_t n_lane = n_base + (lane % S::MT);
-  const bool full = (m_base + kWaveTile <= p.M) && (n_base + kWaveTile <= p.N) && p.c_vec_ok;
+  const bool full = (m_base + kWaveTile <= p.M) && (n_base + S::WN <= p.N) && p.c_vec_ok;
 #pragma unroll
-  for (int j = 0; j < S::NT; ++j) {
+  for (int j = 0; j < NTN; ++j) {
     const int64_t n = n_lane + S::MT * j;
 #pragma unroll
-    for (int i = 0; i < S::NT; ++i) {
+    for (int i = 0; i < S::NTM; ++i) {
 #pragma unroll
       for (int b = 0; b < S::NB; ++b) {
         const int64_t m = m_lane + S::MT * i + 8 * b;
@@ -315,21 +316,21 @@ __device__ __forceinline__ void store_c(
 // non-temporal: C is not read again here, and keeping it out of L2 leaves the
 // room to the A and B strips.  Needs 16-byte aligned columns (ldc % 8 == 0);
 // rows or columns past M, N are masked.
-template <int KIND>
+template <int KIND, int NTN>
 __device__ __forceinline__ void store_c_lds(
     const Params &p, uint8_t *Cb,
-    const typename AccShape<KIND>::acc_t (&acc)[AccShape<KIND>::NT][AccShape<KIND>::NT],
+    const typename AccShape<KIND, NTN>::acc_t (&acc)[AccShape<KIND, NTN>::NTM][NTN],
     __attribute__((address_space(3))) uint8_t *buf, int64_t m_base, int64_t n_base, int lane) {
-  typedef AccShape<KIND> S;
+  typedef AccShape<KIND, NTN> S;
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) u32x2 lds_u2;
   typedef __attribute__((address_space(3))) u32x4 lds_u4;
 #pragma unroll
-  for (int j = 0; j < S::NT; ++j) {
+  for (int j = 0; j < NTN; ++j) {
     const int n = S::MT * j + (lane % S::MT);
 #pragma unroll
-    for (int i = 0; i < S::NT; ++i) {
+    for (int i = 0; i < S::NTM; ++i) {
 #pragma unroll
       for (int b = 0; b < S::NB; ++b) {
         const int m = S::MT * i + 8 * b + 4 * (lane / S::MT);
@@ -344,9 +345,9 @@ __device__ __forceinline__ void store_c_lds(
     }
   }
   // Same wave wrote what it reads next: the LDS counter wait orders them.
-  const bool full = (m_base + kWaveTile <= p.M) && (n_base + kWaveTile <= p.N);
+  const bool full = (m_base + kWaveTile <= p.M) && (n_base + S::WN <= p.N);
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
+  for (int r = 0; r < S::WN / 4; ++r) {
     const int n = 4 * r + (lane >> 4);
     const int mc = lane & 15;
     const u32x4 v = *(lds_u4 *)(buf + n * 256 + ((mc ^ (n & 15)) * 16));
@@ -363,9 +364,24 @@ __device__ __forceinline__ void store_c_lds(
   }
 }
 
-template <int KIND>
+// Read schedule of the 256 x 256 kernel's sub-steps (8 x NTN slots): besides
+// the A fragments (slot NTN*g), item k (0 = A_7, 1 + j = B_j) is read in slot
+// extra_slot(k): every other slot from NTN + 1 on, stepping over the A slots.
+template <int NTN>
+constexpr int extra_slot(int k) {
+  return NTN == 8 ? 9 + 2 * k : 8 + 2 * k + (k >= 3) + (k >= 6);
+}
+static_assert(extra_slot<8>(8) == 25 && extra_slot<7>(0) == 8 && extra_slot<7>(3) == 15 &&
+                  extra_slot<7>(5) == 19 && extra_slot<7>(6) == 22 && extra_slot<7>(7) == 24,
+              "read slots avoid the A slots");
+
+// NTN = 16-column MFMA tiles per wave along N: 8 (256 x 256 block tiles) or 7
+// (256 x 224, which the host picks when it packs the grid into fewer rounds
+// of one block per CU).
+template <int KIND, int NTN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   typedef Traits<KIND> T;
+  constexpr int kTileN = 2 * 16 * NTN;   // block tile width (columns of B / C)
   // Two stages of [A strip | B strip], 64 KiB each.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * 2 * kStageBytes];
 
@@ -375,13 +391,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
 
   int head, tm, tn;
   tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
-  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTileN;
 
   const uint8_t *Ab = p.A + head * p.stride_a_b + m0 * p.lda_b;
   const uint8_t *Bb = p.B + head * p.stride_b_b + n0 * p.ldb_b;
   uint8_t *Cb = p.C + head * p.stride_c_b;
   const int64_t rows_a = (p.M - m0) < kTile ? (p.M - m0) : kTile;
-  const int64_t rows_b = (p.N - n0) < kTile ? (p.N - n0) : kTile;
+  const int64_t rows_b = (p.N - n0) < kTileN ? (p.N - n0) : kTileN;
   const uint32_t kbytes = (uint32_t)(p.K * T::es);
   const uint32_t rec_a = (uint32_t)((rows_a - 1) * p.lda_b) + kbytes;
   const uint32_t rec_b = (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes;
@@ -405,8 +421,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   // lanes of a ds_read_b128 phase read one chunk of 16 consecutive rows (with
   // chunks 2g and 2g + 1 the reads bank-conflicted).  A and B use the same
   // map, so each instruction still pairs equal K indices.
-  typedef AccShape<KIND> S;
-  constexpr int MT = S::MT, NT = S::NT;
+  typedef AccShape<KIND, NTN> S;
+  constexpr int MT = S::MT, NTM = S::NTM;
   const int wm = wave & 1, wn = wave >> 1;
   const int rl = lane % MT, grp = lane / MT;
   uint32_t a_off[4], b_off[4];
@@ -415,14 +431,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     const int chunk = (x / T::reads) * (8 / T::subs) + grp + 4 * (x % T::reads);
     const uint32_t lo = (uint32_t)(rl * kRowBytes + ((chunk ^ ((rl >> 1) & 7)) * 16));
     a_off[x] = lo + wm * kWaveTile * kRowBytes;
-    b_off[x] = lo + kStageBytes + wn * kWaveTile * kRowBytes;
+    b_off[x] = lo + kStageBytes + wn * S::WN * kRowBytes;
   }
 
-  typename S::acc_t acc[NT][NT];
+  typename S::acc_t acc[NTM][NTN];
 #pragma unroll
-  for (int i = 0; i < NT; ++i)
+  for (int i = 0; i < NTM; ++i)
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
+    for (int j = 0; j < NTN; ++j)
 #pragma unroll
       for (int e = 0; e < MT * MT / 64; ++e) acc[i][j][e] = 0.f;
 
@@ -484,36 +500,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   typedef typename T::frag_t frag_t;
   constexpr int kTileBytes = MT * kRowBytes;      // LDS bytes between MFMA tiles
 
-  // 8 x 8 MFMA tiles per wave; a K-step is `subs` sub-steps (fp16: two 32-deep,
-  // fp8: one 128-deep) of 64 MFMA slots, MFMA (g, j) in slot 8g + j:
-  //  * B fragments are double-buffered by sub-step parity; the next sub-step's
-  //    eight are read in slots 11, 13, .., 25;
+  // 8 x NTN MFMA tiles per wave; a K-step is `subs` sub-steps (fp16: two
+  // 32-deep, fp8: one 128-deep) of 8 * NTN MFMA slots, MFMA (g, j) in slot
+  // NTN*g + j:
   //  * A fragment g (< 7) of the next sub-step goes into the register of the
-  //    current one right after its last use (slot 8g + 8); A_7 alternates
-  //    between two registers by sub-step parity and is read in slot 9;
-  //  * the last sub-step of a K-step reads nothing before slot 8, so the
+  //    current one right after its last use (slot NTN*(g+1)); A_7 alternates
+  //    between two registers by sub-step parity;
+  //  * B fragments are double-buffered by sub-step parity;
+  //  * A_7 and the B fragments of the next sub-step are read every other slot
+  //    from slot NTN + 1 on (skipping the A slots);
+  //  * the last sub-step of a K-step reads nothing before slot NTN, so the
   //    K-step barrier sits there: every read of stage t was issued earlier,
-  //    and the reads from slot 8 on come from stage t+1;
-  //  * step t+2's sixteen copies into the freed stage follow the barrier,
+  //    and the reads from slot NTN on come from stage t+1;
+  //  * step t+2's 8 + NTN copies into the freed stage follow the barrier,
   //    spread evenly over a window of kWin slots (which may reach into step
   //    t+1), so the last one has most of a step to land.
-  static_assert(MT == 16 && NT == 8, "8 x 8 tiles of 16 x 16");
-  constexpr int kQ = 64, kBarQ = 8;
+  static_assert(MT == 16 && NTM == 8 && (NTN == 8 || NTN == 7), "8 x NTN tiles of 16 x 16");
+  constexpr int kQ = 8 * NTN, kBarQ = NTN;
   constexpr int kBarSlot = (T::subs - 1) * kQ + kBarQ;
   constexpr int kAfter = T::subs * kQ - kBarSlot;  // window slots in the barrier's step
-  // Copy window in slots (about 1000 cycles of MFMA for either),
-  // chosen by measurement (fp16 4096^3, fp8 8192^3).
-  constexpr int kWin = (KIND == kF16) ? 64 : 32;
-  static_assert(kWin >= 16 && kWin - kAfter <= kBarQ, "copy window");
-  auto first_copy = [](int x) { return (x * 16 + kWin - 1) / kWin; };
-  constexpr int kPost = (kAfter * 16 + kWin - 1) / kWin;  // first_copy(kAfter)
-  frag_t fa[8], fx, fb[2][8];
+  constexpr int kCopies = 8 + NTN;                 // copy instructions per wave per step
+  // Copy window in slots (about 1000 cycles of MFMA for either), chosen by
+  // measurement (fp16 4096^3, fp8 8192^3), capped by the slots before the
+  // next step's barrier.
+  constexpr int kWin0 = (KIND == kF16) ? 64 : 32;
+  constexpr int kWin = kWin0 < kAfter + kBarQ ? kWin0 : kAfter + kBarQ;
+  static_assert(kWin >= kCopies && kWin - kAfter <= kBarQ, "copy window");
+  auto first_copy = [](int x) { return (x * kCopies + kWin - 1) / kWin; };
+  constexpr int kPost = (kAfter * kCopies + kWin - 1) / kWin;  // first_copy(kAfter)
+  frag_t fa[8], fx, fb[2][NTN];
   if (nk2 > 0) {
     // Copies of all of step 0 and the first kPost of step 1; wait for step 0
     // only (loads complete in order) and publish it.
     const StepCopy c0 = step_copy(0);
 #pragma unroll
-    for (int d = 0; d < 16; ++d) copy_one(c0, d, qs_a, qs_b);
+    for (int d = 0; d < kCopies; ++d) copy_one(c0, d, qs_a, qs_b);
     const StepCopy c1 = step_copy(1);
 #pragma unroll
     for (int d = 0; d < kPost; ++d) copy_one(c1, d, qs_a, qs_b);
@@ -523,17 +544,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     asm volatile("" ::: "memory");
     lds_cptr st0 = (lds_cptr)smem;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      fb[0][j] = read_frag<KIND>(st0 + j * kTileBytes, b_off, 0);
-      fa[j] = read_frag<KIND>(st0 + j * kTileBytes, a_off, 0);
-    }
+    for (int j = 0; j < NTN; ++j) fb[0][j] = read_frag<KIND>(st0 + j * kTileBytes, b_off, 0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) fa[g] = read_frag<KIND>(st0 + g * kTileBytes, a_off, 0);
   }
   // cn: copies of step t + 1 (its last ones are issued early in step t);
   // cnn: step t + 2's, planned in slots kPlan .. kPlan + 2 of step t.
   StepCopy cn = step_copy(1), cnn;
   StepScalars un;
   constexpr int kPlan = kBarSlot - 6;
-  static_assert(kPlan >= kWin - kAfter, "plan after the last copy of step t + 1");
+  static_assert(kPlan >= 0 && kPlan >= kWin - kAfter, "plan after the last copy of step t + 1");
   for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {            // K-step t0 + h lives in stage h
@@ -549,18 +569,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int q = 8 * g + j;
+          for (int j = 0; j < NTN; ++j) {
+            const int q = NTN * g + j;
             const int slot = kQ * s + q;
-            if (j == 0 && g >= 1) {
+            if (j == 0 && g >= 1)
               fa[g - 1] = read_frag<KIND>(src + (g - 1) * kTileBytes, a_off, s_n);
-            } else if (q == 9) {
+            if (q == extra_slot<NTN>(0)) {
               if (par == 0) fx = read_frag<KIND>(src + 7 * kTileBytes, a_off, s_n);
               else fa[7] = read_frag<KIND>(src + 7 * kTileBytes, a_off, s_n);
-            } else if (q >= 11 && q <= 25 && (q & 1) == 1) {
-              const int jj = (q - 11) / 2;
-              fb[par ^ 1][jj] = read_frag<KIND>(src + jj * kTileBytes, b_off, s_n);
             }
+#pragma unroll
+            for (int jj = 0; jj < NTN; ++jj)
+              if (q == extra_slot<NTN>(jj + 1))
+                fb[par ^ 1][jj] = read_frag<KIND>(src + jj * kTileBytes, b_off, s_n);
             if (slot == kPlan) un = step_scalars(t + 2);
             if (slot == kPlan + 1) step_rsrc(un, cnn);
             if (slot == kPlan + 2) step_lanes(un, cnn);
@@ -588,15 +609,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   __builtin_amdgcn_s_waitcnt(0);
   if (p.c_vec16_ok) {
     __syncthreads();
-    store_c_lds<KIND>(p, Cb, acc, (__attribute__((address_space(3))) uint8_t *)smem + wave * 32768,
-                      m0 + wm * kWaveTile, n0 + wn * kWaveTile, lane);
+    store_c_lds<KIND, NTN>(p, Cb, acc,
+                           (__attribute__((address_space(3))) uint8_t *)smem + wave * 32768,
+                           m0 + wm * kWaveTile, n0 + wn * S::WN, lane);
   } else {
-    store_c<KIND>(p, Cb, acc, m0 + wm * kWaveTile, n0 + wn * kWaveTile, lane);
+    store_c<KIND, NTN>(p, Cb, acc, m0 + wm * kWaveTile, n0 + wn * S::WN, lane);
   }
 }
 
-template __global__ void gemm_tn_kernel<kF16>(Params);
-template __global__ void gemm_tn_kernel<kF8>(Params);
+template __global__ void gemm_tn_kernel<kF16, 8>(Params);
+template __global__ void gemm_tn_kernel<kF16, 7>(Params);
+template __global__ void gemm_tn_kernel<kF8, 8>(Params);
+template __global__ void gemm_tn_kernel<kF8, 7>(Params);
 
 // ----------------------------------------------------------------- skinny K
 // Kernels for K * es <= 256 bytes (the QK^T shape: K = head dim 128): the whole
@@ -894,9 +918,24 @@ static int launch(const Problem &pr, hipStream_t stream) {
   // Skinny contractions (all of K fits one 256-byte LDS row) take the 128 x 128
   // tile kernel with two blocks per CU; everything else the 256 x 256 pipeline.
   const bool skinny = pr.K * es <= kSkRow;
-  const int64_t tile = skinny ? kSkTile : kTile;
-  const int64_t tiles_m = (pr.M + tile - 1) / tile;
-  const int64_t tiles_n = (pr.N + tile - 1) / tile;
+  // The 256-row pipeline takes 256- or 224-column tiles (NTN = 8 or 7 MFMA
+  // tiles per wave): with one block per CU the time is about (rounds of CU
+  // count blocks) x (tile width), so take the narrower tile when it packs
+  // the grid into enough fewer rounds (1920 x 13900: 440 wide tiles are two
+  // rounds of 256 CUs, 504 narrow ones also two, each 7/8 as long).
+  int ntn = 8;
+  if (!skinny) {
+    const int64_t cus = cu_count();
+    const int64_t tm = (pr.M + kTile - 1) / kTile;
+    auto cost = [&](int64_t w) {
+      const int64_t blocks = tm * ((pr.N + 32 * w - 1) / (32 * w)) * pr.batch;
+      return ((blocks + cus - 1) / cus) * w;
+    };
+    if (cost(7) < cost(8)) ntn = 7;
+  }
+  const int64_t tile_m = skinny ? kSkTile : kTile, tile_n = skinny ? kSkTile : 32 * ntn;
+  const int64_t tiles_m = (pr.M + tile_m - 1) / tile_m;
+  const int64_t tiles_n = (pr.N + tile_n - 1) / tile_n;
   // Skinny-K blocks walk up to kSkWalkMax M tiles of one column (each walk
   // step saves a copy of B's strip), halved while that would leave fewer than
   // eight blocks per CU.
@@ -925,8 +964,10 @@ static int launch(const Problem &pr, hipStream_t stream) {
   if (skinny)
     hipLaunchKernelGGL(gemm_tn_skinny_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, p);
+  else if (ntn == 8)
+    hipLaunchKernelGGL((gemm_tn_kernel<KIND, 8>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(gemm_tn_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_tn_kernel<KIND, 7>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 

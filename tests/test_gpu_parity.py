@@ -246,6 +246,33 @@ def test_batched_qkt_walks(H, M, N, D, pad):
     torch.cuda.empty_cache()
 
 
+def tile_width(M, N, batch=1, cus=256):
+    """The 256-row kernel's tile width the host picks: 256 columns, or 224
+    when that packs the grid into enough fewer rounds of one block per CU."""
+    def cost(w):
+        blocks = -(-M // 256) * -(-N // (32 * w)) * batch
+        return -(-blocks // cus) * w
+    return 224 if cost(7) < cost(8) else 256
+
+
+@pytest.mark.parametrize("kind,M,N,K", [("f16", 4024, 3996, 3976), ("f8", 4024, 3996, 3856),
+                                        ("f16", 1000, 700, 3976)])
+def test_ragged_large_tiles(kind, M, N, K):
+    """Grids large enough for 256-column tiles (the small ragged cases get 224),
+    with M, N and K tails and an odd K-step count; +-1 data, sampled entries
+    exact, the whole tail row and column exact, canaries intact."""
+    assert tile_width(M, N) == (256 if M > 1000 else 224)
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=M + N + K)
+    got, canary = run_gemm(kind, x, M, N, K)
+    assert canary
+    ms, ns = sample_entries(M, N, 1500, seed=K)
+    ms = np.concatenate([ms, np.arange(M), np.full(N, M - 1)])
+    ns = np.concatenate([ns, np.full(M, N - 1), np.arange(N)])
+    scale = float(x["scale_a"]) * float(x["scale_b"]) if kind == "f8" else 1.0
+    ref = oracle.gemm_tn_entries(x["A"], x["B"], in_fmt(kind), K, ms, ns, scale=scale)
+    assert_exact(kind, got[ns, ms], ref)
+
+
 # ------------------------------------------------------------- full-size workloads
 
 def sample_entries(M, N, count, seed):
