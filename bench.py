@@ -36,7 +36,21 @@ METRIC = "TFLOP/s and % of dense MFMA peak: FP16 TN 4096^3, FP8 e4m3 8192^3"
 # Published MI355X dense peaks: 256 CUs x 2.4 GHz x 4096 (fp16) / 8192 (fp8) flop/clk/CU.
 PEAK_TFLOPS = {"f16": 2516.6, "qkt": 2516.6, "f8": 5033.2}
 HBM_PEAK_GBS = 8000.0
-KERNEL_NAME = {"f16": "gemm_tn_kernel<0>", "qkt": "gemm_tn_skinny_kernel<0>", "f8": "gemm_tn_kernel<1>"}
+
+
+def kernel_name(w, cus):
+    """The kernel the library launches for workload w (its tile-width choice:
+    256 columns, or 224 when that packs the grid into fewer rounds of one
+    block per CU)."""
+    es = 1 if w.kind == "f8" else 2
+    if w.K * es <= 256:
+        return "gemm_tn_skinny_kernel<%d>" % (1 if w.kind == "f8" else 0)
+
+    def cost(ntn):
+        blocks = -(-w.M // 256) * -(-w.N // (32 * ntn)) * w.batch
+        return -(-blocks // cus) * ntn
+
+    return "gemm_tn_kernel<%d, %d>" % (1 if w.kind == "f8" else 0, 7 if cost(7) < cost(8) else 8)
 SRC = os.path.join(ROOT, "dense_gemm_tn_amd", "csrc", "gemm_tn.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -239,7 +253,7 @@ def main():
             "peak": HBM_PEAK_GBS if w.kind == "qkt" else PEAK_TFLOPS[w.kind],
             "unit": "GB/s" if w.kind == "qkt" else "TFLOP/s",
             "traffic": tb,
-            "kernel": KERNEL_NAME[w.kind],
+            "kernel": kernel_name(w, torch.cuda.get_device_properties(dev).multi_processor_count),
         }
         r = res["roofline"]
         r["frac"] = r["achieved"] / r["peak"]
