@@ -14,6 +14,11 @@ Definitions followed (page, section):
     A row-major M x K, B column-major (K contiguous per column), C column-major.
   * FP8 inputs carry per-tensor scales; the oracle applies scale_a * scale_b to
     the exact binary64 sum.
+  * Attention (``attention_rows``): the hello-gpu chapter summary names joining the
+    product with softmax as the next step, and the mlqm.cn TileLang attention page
+    motivates fusing softmax with QK^T.  No page gives the formula, so the oracle is
+    the textbook softmax attention O = softmax(scale * Q K^T) V, row by row, in
+    binary64 (see oracle.c).
 
 Every function here has at least one pin in ``tests/test_oracle_pins.py`` that
 does not come from this code (the worked example of section 11.1, the rank-1
@@ -66,8 +71,10 @@ def _load():
                                        ctypes.c_double, ctypes.c_int]
         lib.oracle_gemm_tn_entries.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, vp, vp, i64,
                                                ctypes.c_double, vp]
+        lib.oracle_attention_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp, i64,
+                                              ctypes.c_double, vp, ctypes.c_int]
         for f in (lib.oracle_decode, lib.oracle_encode, lib.oracle_gemm_tn,
-                  lib.oracle_gemm_tn_entries):
+                  lib.oracle_gemm_tn_entries, lib.oracle_attention_rows):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -170,4 +177,34 @@ def batched_qkt(Q: np.ndarray, Kmat: np.ndarray, batch: int, M: int, N: int, D: 
     out = np.empty((batch, N, M), dtype=np.float64)
     for h in range(batch):
         out[h] = gemm_tn(q[h], k[h], FMT_F16, M, N, D, nthreads=nthreads)
+    return out
+
+
+def attention_rows(Q: np.ndarray, Kmat: np.ndarray, Vt: np.ndarray, N: int, D: int, rows,
+                   scale: float, ldq: int | None = None, ldk: int | None = None,
+                   ldv: int | None = None, nthreads: int | None = None) -> np.ndarray:
+    """binary64 softmax attention of query rows `rows` of one head, shape [len(rows), D].
+
+    Q holds query rows of ldq fp16 codes, Kmat key rows of ldk codes, Vt holds V
+    column-major (D rows of ldv codes, row d = V[:, d]).  Definition in oracle.c.
+    """
+    ldq = D if ldq is None else ldq
+    ldk = D if ldk is None else ldk
+    ldv = N if ldv is None else ldv
+    rq = _raw(Q, FMT_F16).reshape(-1)
+    rk = _raw(Kmat, FMT_F16).reshape(-1)
+    rv = _raw(Vt, FMT_F16).reshape(-1)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1)
+    if rows.size and (rows.min() < 0 or rows.max() * ldq + D > rq.size):
+        raise ValueError("query row out of range")
+    if (N - 1) * ldk + D > rk.size or (D - 1) * ldv + N > rv.size:
+        raise ValueError("K or Vt too small")
+    out = np.empty((rows.size, D), dtype=np.float64)
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    rc = _load().oracle_attention_rows(_ptr(rq), _ptr(rk), _ptr(rv), N, D, ldq, ldk, ldv,
+                                       _ptr(rows), rows.size, float(scale), _ptr(out),
+                                       int(nthreads))
+    if rc:
+        raise RuntimeError("oracle_attention_rows failed with %d" % rc)
     return out

@@ -32,6 +32,19 @@
  * Encoders round to nearest, ties to even.  binary16 and bfloat16 overflow
  * to +-Inf as IEEE rounding does; E4M3FN saturates to +-448.
  *
+ * Attention (oracle_attention_rows): the chapter summary of the hello-gpu
+ * GEMM chapter names the next step as joining the matrix product with softmax
+ * so the intermediate result need not be written back; the TileLang attention
+ * page motivates the same fusion for QK^T.  The pages define no formula for
+ * it, so the oracle is the textbook definition of softmax attention for one
+ * query row i of one head:
+ *     s_n = scale * sum_d Q[i,d] * K[n,d]            (d ascending, binary64)
+ *     w_n = exp(s_n - max_n s_n)                     (libm exp, binary64)
+ *     O[i,d] = (sum_n w_n * V[n,d]) / (sum_n w_n)    (n ascending)
+ * with V given column-major (Vt[d*ldv + n], the K-contiguous operand of the
+ * TN product O = P V).  Subtracting the row maximum changes nothing
+ * mathematically and keeps exp in range.
+ *
  * Build: gcc -O2 -std=c11 -fPIC -shared -pthread (no -ffast-math: the sum
  * order must stay exactly k ascending).
  */
@@ -272,4 +285,88 @@ int oracle_gemm_tn_entries(int fmt, const void *A, const void *B, int64_t K,
     out[i] = acc * scale;
   }
   return 0;
+}
+
+/* ---------------------------------------------------------------- attention */
+
+typedef struct {
+  const double *q, *k, *vt; /* decoded: rows x D, N x D, D x N */
+  double *o;                /* rows x D */
+  int64_t N, D, r_begin, r_end;
+  double scale;
+} attn_job;
+
+static void *attn_worker(void *arg) {
+  const attn_job *j = (const attn_job *)arg;
+  double *s = (double *)malloc(sizeof(double) * (size_t)(j->N > 0 ? j->N : 1));
+  if (!s) return (void *)1;
+  for (int64_t r = j->r_begin; r < j->r_end; ++r) {
+    const double *qr = j->q + r * j->D;
+    double mx = -INFINITY;
+    for (int64_t n = 0; n < j->N; ++n) {
+      const double *kr = j->k + n * j->D;
+      double acc = 0.0;
+      for (int64_t d = 0; d < j->D; ++d) acc += qr[d] * kr[d];
+      s[n] = acc * j->scale;
+      if (s[n] > mx) mx = s[n];
+    }
+    double z = 0.0;
+    for (int64_t n = 0; n < j->N; ++n) {
+      s[n] = exp(s[n] - mx);
+      z += s[n];
+    }
+    for (int64_t d = 0; d < j->D; ++d) {
+      const double *vr = j->vt + d * j->N;
+      double acc = 0.0;
+      for (int64_t n = 0; n < j->N; ++n) acc += s[n] * vr[n];
+      j->o[r * j->D + d] = acc / z;
+    }
+  }
+  free(s);
+  return NULL;
+}
+
+/*
+ * Softmax attention of the query rows rows[0..count-1] of one head (binary16
+ * inputs): O[r*D + d] for r < count, as defined in the header.  Q[i*ldq + d],
+ * K[n*ldk + d], Vt[d*ldv + n].  N >= 1.  Returns 0 on success.
+ */
+int oracle_attention_rows(const void *Q, const void *K, const void *Vt, int64_t N, int64_t D,
+                          int64_t ldq, int64_t ldk, int64_t ldv, const int64_t *rows,
+                          int64_t count, double scale, double *O, int nthreads) {
+  if (N < 1 || D < 1 || count < 0 || ldq < D || ldk < D || ldv < N) return 1;
+  double *q = (double *)malloc(sizeof(double) * (size_t)((count > 0 ? count : 1) * D));
+  double *k = (double *)malloc(sizeof(double) * (size_t)(N * D));
+  double *vt = (double *)malloc(sizeof(double) * (size_t)(N * D));
+  if (!q || !k || !vt) { free(q); free(k); free(vt); return 2; }
+  for (int64_t r = 0; r < count; ++r)
+    for (int64_t d = 0; d < D; ++d) q[r * D + d] = decode_one(ORACLE_FMT_F16, Q, rows[r] * ldq + d);
+  for (int64_t n = 0; n < N; ++n)
+    for (int64_t d = 0; d < D; ++d) k[n * D + d] = decode_one(ORACLE_FMT_F16, K, n * ldk + d);
+  for (int64_t d = 0; d < D; ++d)
+    for (int64_t n = 0; n < N; ++n) vt[d * N + n] = decode_one(ORACLE_FMT_F16, Vt, d * ldv + n);
+
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > count) nthreads = (int)(count > 0 ? count : 1);
+  pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  attn_job *jobs = (attn_job *)malloc(sizeof(attn_job) * (size_t)nthreads);
+  int rc = 0;
+  if (!tid || !jobs) rc = 2;
+  int started = 0;
+  for (int t = 0; rc == 0 && t < nthreads; ++t) {
+    jobs[t].q = q; jobs[t].k = k; jobs[t].vt = vt; jobs[t].o = O;
+    jobs[t].N = N; jobs[t].D = D; jobs[t].scale = scale;
+    jobs[t].r_begin = count * t / nthreads;
+    jobs[t].r_end = count * (t + 1) / nthreads;
+    if (nthreads == 1) { if (attn_worker(&jobs[t])) rc = 2; continue; }
+    if (pthread_create(&tid[t], NULL, attn_worker, &jobs[t]) != 0) { rc = 3; break; }
+    ++started;
+  }
+  for (int t = 0; t < started; ++t) {
+    void *ret = NULL;
+    pthread_join(tid[t], &ret);
+    if (ret) rc = 2;
+  }
+  free(jobs); free(tid); free(q); free(k); free(vt);
+  return rc;
 }
