@@ -1,9 +1,9 @@
-"""Python binding of libdense_gemm_tn.so (gfx950 TN GEMM).
+"""Python binding of libdense_gemm_tn.so (gfx950 TN GEMM and fused attention).
 
-Argument marshalling only: every step of the GEMM runs in the HIP kernels of
-``csrc/gemm_tn.hip`` behind the C ABI declared in ``include/dense_gemm_tn.h``.
-PyTorch supplies device memory and the current HIP stream.  If the library has
-not been built, every call raises -- there is no other code path.
+Argument marshalling only: every step runs in the HIP kernels of
+``csrc/gemm_tn.hip`` and ``csrc/attention.hip`` behind the C ABI declared in
+``include/dense_gemm_tn.h``.  PyTorch supplies device memory and the current HIP
+stream.  If the library has not been built, every call raises -- there is no other code path.
 
 Layouts (TN, "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", section "What we
 compute"): A is row-major M x K (a [M, lda] tensor), B is column-major K x N,
@@ -27,6 +27,7 @@ EXPORTS = (
     "gemm_f16_tn",
     "gemm_f8_tn",
     "gemm_batched_qkt",
+    "attention_fwd_f16",
     "gemm_status_string",
     "gemm_tile_order",
     "gemm_block_tile",
@@ -54,12 +55,13 @@ def lib() -> ctypes.CDLL:
         L.gemm_f8_tn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, vp]
         L.gemm_batched_qkt.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                        i64, vp]
+        L.attention_fwd_f16.argtypes = [vp, vp, vp, vp] + [i64] * 12 + [f32, vp]
         L.gemm_status_string.argtypes = [ctypes.c_int]
         L.gemm_status_string.restype = ctypes.c_char_p
         L.gemm_tile_order.argtypes = [i64, i64, i64, vp]
         L.gemm_block_tile.argtypes = []
-        for f in (L.gemm_f16_tn, L.gemm_f8_tn, L.gemm_batched_qkt, L.gemm_tile_order,
-                  L.gemm_block_tile):
+        for f in (L.gemm_f16_tn, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
+                  L.gemm_tile_order, L.gemm_block_tile):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -114,6 +116,16 @@ def gemm_batched_qkt(Q, Kmat, S, batch: int, M: int, N: int, D: int, ldq: int, l
     _check("gemm_batched_qkt",
            lib().gemm_batched_qkt(_ptr(Q), _ptr(Kmat), _ptr(S), batch, M, N, D, ldq, ldk, lds,
                                   stride_q, stride_k, stride_s, _stream(stream)))
+
+
+def attention_fwd_f16(Q, Kmat, Vt, O, batch: int, M: int, N: int, D: int, ldq: int, ldk: int,
+                      ldv: int, ldo: int, stride_q: int, stride_k: int, stride_v: int,
+                      stride_o: int, scale: float, stream=None) -> None:
+    """O_h = softmax(scale * Q_h K_h^T) V_h with V_h passed as Vt_h (D x N, keys contiguous)."""
+    _check("attention_fwd_f16",
+           lib().attention_fwd_f16(_ptr(Q), _ptr(Kmat), _ptr(Vt), _ptr(O), batch, M, N, D, ldq,
+                                   ldk, ldv, ldo, stride_q, stride_k, stride_v, stride_o,
+                                   float(scale), _stream(stream)))
 
 
 def tile_order(tiles_m: int, tiles_n: int, batch: int = 1):
@@ -172,4 +184,32 @@ def qkt(q, k, out=None, stream=None):
         out = torch.empty((H, N, M), dtype=torch.float16, device=q.device)
     gemm_batched_qkt(q, k, out, H, M, N, D, q.stride(1), k.stride(1), out.stride(1),
                      q.stride(0), k.stride(0), out.stride(0), stream)
+    return out
+
+
+def attention(q, k, vt, scale: float | None = None, out=None, stream=None):
+    """q: [H, M, D], k: [H, N, D], vt: [H, D, N] fp16 -> O as [H, M, D] fp16.
+
+    scale defaults to 1/sqrt(D).  Row strides are taken from the tensors (the last
+    dimension must be contiguous, and every row stride a multiple of 8 elements:
+    for N % 8 != 0 pass a slice of a [H, D, N rounded up to 8] buffer as vt).
+    """
+    import math
+
+    import torch
+
+    H, M, D = q.shape
+    Hk, N, Dk = k.shape
+    Hv, Dv, Nv = vt.shape
+    if (H, D) != (Hk, Dk) or (H, D, N) != (Hv, Dv, Nv):
+        raise ValueError("attention expects [H, M, D], [H, N, D] and [H, D, N]")
+    if any(t.dtype != torch.float16 or t.stride(2) != 1 for t in (q, k, vt)):
+        raise ValueError("attention expects fp16 tensors with a contiguous last dimension")
+    if out is None:
+        out = torch.empty((H, M, D), dtype=torch.float16, device=q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    attention_fwd_f16(q, k, vt, out, H, M, N, D, q.stride(1), k.stride(1), vt.stride(1),
+                      out.stride(1), q.stride(0), k.stride(0), vt.stride(0), out.stride(0),
+                      scale, stream)
     return out

@@ -2,7 +2,8 @@
 
     python -m dense_gemm_tn_amd.build
 
-compiles ``csrc/gemm_tn.hip`` into ``libdense_gemm_tn.so`` next to this file.
+compiles ``csrc/gemm_tn.hip`` (GEMM kernels) and ``csrc/attention.hip`` (fused
+attention forward) into ``libdense_gemm_tn.so`` next to this file.
 """
 from __future__ import annotations
 
@@ -12,7 +13,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "gemm_tn.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("gemm_tn.hip", "attention.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdense_gemm_tn.so")
 
@@ -35,7 +36,7 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

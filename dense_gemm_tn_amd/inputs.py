@@ -1,12 +1,12 @@
-"""Seeded synthetic inputs for the TN GEMM workloads.
+"""Seeded synthetic inputs for the TN GEMM and attention workloads.
 
 This module only draws and encodes input elements (numpy PCG64 streams, the
 fp16 cast, the per-tensor FP8 quantiser); it contains none of the GEMM's
 arithmetic.  Both the GPU path and the CPU oracle receive exactly the bytes
 made here.
 
-Recipe (one numpy ``default_rng(seed)`` per workload, drawing A then B, or Q
-then K):
+Recipe (one numpy ``default_rng(seed)`` per workload, drawing A then B, Q then
+K, or Q, K then Vt for attention):
   * "pm1"    elements uniform on {-1, +1} (the exact-comparison inputs of
              "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", section "What we
              compute": every product is +-1 and every partial sum an integer);
@@ -28,7 +28,7 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str            # "f16", "f8" or "qkt"
+    kind: str            # "f16", "f8", "qkt" or "attn"
     M: int
     N: int
     K: int               # contraction length (head dim D for "qkt")
@@ -40,8 +40,10 @@ class Workload:
 
     @property
     def flops(self) -> int:
-        """Algorithmic work: 2*M*N*K per head (section 11.1 of the hello-gpu chapter)."""
-        return 2 * self.M * self.N * self.K * self.batch
+        """Algorithmic work: 2*M*N*K per head (section 11.1 of the hello-gpu chapter);
+        attention does two such products per head (Q K^T and P V, K = head dim)."""
+        products = 2 if self.kind == "attn" else 1
+        return products * 2 * self.M * self.N * self.K * self.batch
 
 
 # The five workloads (sizes and distributions as stated for this GEMM).
@@ -55,6 +57,7 @@ WORKLOADS = {
         Workload("f8_8192", "f8", 8192, 8192, 8192, "normal", seed=0),
         Workload("qkt_64x4096x4096x128", "qkt", 4096, 4096, 128, "normal", seed=0, batch=64,
                  std=1.0 / math.sqrt(128.0)),
+        Workload("attn_64x4096x4096x128", "attn", 4096, 4096, 128, "normal", seed=0, batch=64),
     )
 }
 
@@ -103,6 +106,8 @@ def make(w: Workload | str, dist: str | None = None, seed: int | None = None):
       f16:  A [M, K] fp16, B [N, K] fp16 (row n = column n of B)
       f8:   A [M, K] uint8, B [N, K] uint8, scale_a, scale_b (fp32 values)
       qkt:  Q [batch, M, D] fp16, K [batch, N, D] fp16
+      attn: Q [batch, M, D], K [batch, N, D], Vt [batch, D, N] fp16 (Vt row d =
+            column d of V), all N(0, std^2)
     """
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -129,4 +134,9 @@ def make_shape(kind: str, M: int, N: int, K: int, dist: str = "normal", seed: in
         if dist == "pm1":
             return {"Q": pm1_f16(rng, (batch, M, K)), "K": pm1_f16(rng, (batch, N, K))}
         return {"Q": normal_f16(rng, (batch, M, K), std), "K": normal_f16(rng, (batch, N, K), std)}
+    if kind == "attn":
+        if dist != "normal":
+            raise ValueError("attention inputs are normal only")
+        return {"Q": normal_f16(rng, (batch, M, K), std), "K": normal_f16(rng, (batch, N, K), std),
+                "Vt": normal_f16(rng, (batch, K, N), std)}
     raise ValueError("unknown kind %r" % kind)

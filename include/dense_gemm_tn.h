@@ -100,6 +100,45 @@ int gemm_batched_qkt(const void *Q, const void *Kmat, void *S,
                      int64_t stride_q, int64_t stride_k, int64_t stride_s,
                      void *stream);
 
+/*
+ * Fused softmax attention forward (fp16 in, fp16 out; fp32 scores, fp32
+ * accumulation, probabilities rounded to fp16 for the second product): for
+ * each head h < batch and query row i < M,
+ *   s_n     = scale * sum_d Q[h*stride_q + i*ldq + d] * K[h*stride_k + n*ldk + d]
+ *   O[h*stride_o + i*ldo + d] = sum_n exp(s_n - max s) * Vt[h*stride_v + d*ldv + n]
+ *                               / sum_n exp(s_n - max s)
+ * over keys n < N, for d < D.  The score matrix is never written to memory.
+ * Source: the chapter summary of "hello-gpu, chapter 11 (GEMM-like)" (the
+ * next step after the GEMM joins it with softmax so the intermediate result
+ * need not go back to memory) and the fused attention of the mlqm.cn TileLang
+ * attention page; the pages give no formula, so the operation is the textbook
+ * softmax attention.  Both products are TN products (each operand contiguous
+ * along the summed dimension), which is why V is passed transposed: Vt is
+ * D rows of N keys (row d = column d of V), e.g. the column-major output of
+ * the V projection computed with gemm_f16_tn.
+ *
+ * Sizes and storage (strides in elements): Q row-major M x D (ldq >= D), K
+ * row-major N x D (ldk >= D), Vt row-major D x N (ldv >= N), O row-major
+ * M x D (ldo >= D).  D must be 128 (else DG_ERR_UNSUPPORTED).  Pointers must
+ * be 16-byte aligned and all ld and stride values multiples of 8 (else
+ * DG_ERR_UNSUPPORTED).  Input head strides may be 0 (one K/V shared by all
+ * heads); the heads of O must not overlap (stride_o >= (M-1)*ldo + D when
+ * batch > 1) and O must not overlap Q, K or Vt (else DG_ERR_INVALID_ARGUMENT).
+ * scale must be finite and >= 0; N must be >= 1 when M > 0 (softmax over no
+ * keys is undefined); negative sizes or strides and null pointers are
+ * DG_ERR_INVALID_ARGUMENT.  batch == 0 or M == 0 is a successful no-op.
+ * Per-head extents of Q, K (plus 64 rows) and Vt (plus 64 keys) must stay
+ * below 2^31 bytes (else DG_ERR_UNSUPPORTED).  Elements of Q, K and Vt
+ * outside their logical extents (ld padding, head gaps) are never read, and
+ * O is written only at its batch x M x D logical positions.  Device pointers, stream and ordering as
+ * for the GEMM entry points above; one kernel launch, no allocation.
+ */
+int attention_fwd_f16(const void *Q, const void *K, const void *Vt, void *O,
+                      int64_t batch, int64_t M, int64_t N, int64_t D,
+                      int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo,
+                      int64_t stride_q, int64_t stride_k, int64_t stride_v, int64_t stride_o,
+                      float scale, void *stream);
+
 /* Static, NUL-terminated name of a dg_status value ("unknown status" otherwise). */
 const char *gemm_status_string(int status);
 
