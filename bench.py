@@ -1,5 +1,5 @@
 #!/usr/bin/env python3
-"""Throughput of the gfx950 TN GEMM on synthetic inputs resident in HBM.
+"""Throughput of the gfx950 TN GEMM (and fused attention) on synthetic inputs in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME ...] [--no-cpu]
 
@@ -14,8 +14,9 @@ step / time (section 11.1 of the hello-gpu chapter counts a multiply-add as
 two flops).
 
 Prints ONE JSON line.  The headline `value` is the FP16 TN 4096^3 workload; the
-FP8 8192^3 workload (and any other requested one) is reported under
-"workloads" in the same line.  `roofline` is for the FP16 kernel; `traffic`
+FP8 8192^3 workload, the fused attention forward over 64 heads x 4096 queries x
+4096 keys x head dim 128 (4*M*N*D flops per head: two products), and any other
+requested workload are reported under "workloads" in the same line.  `roofline` is for the FP16 kernel; `traffic`
 comes from a stored rocprofv3 counter summary and is null when the kernel
 source changed after the counters were taken.  `cpu_baseline` times the CPU
 oracle on a bounded column sample of the same workload.
@@ -34,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "TFLOP/s and % of dense MFMA peak: FP16 TN 4096^3, FP8 e4m3 8192^3"
 # Published MI355X dense peaks: 256 CUs x 2.4 GHz x 4096 (fp16) / 8192 (fp8) flop/clk/CU.
-PEAK_TFLOPS = {"f16": 2516.6, "qkt": 2516.6, "f8": 5033.2}
+PEAK_TFLOPS = {"f16": 2516.6, "qkt": 2516.6, "attn": 2516.6, "f8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 
 
@@ -42,6 +43,8 @@ def kernel_name(w, cus):
     """The kernel the library launches for workload w (its tile-width choice:
     256 columns, or 224 when that packs the grid into fewer rounds of one
     block per CU)."""
+    if w.kind == "attn":
+        return "attention_fwd_kernel"
     es = 1 if w.kind == "f8" else 2
     if w.K * es <= 256:
         return "gemm_tn_skinny_kernel<%d>" % (1 if w.kind == "f8" else 0)
@@ -51,17 +54,25 @@ def kernel_name(w, cus):
         return -(-blocks // cus) * ntn
 
     return "gemm_tn_kernel<%d, %d>" % (1 if w.kind == "f8" else 0, 7 if cost(7) < cost(8) else 8)
-SRC = os.path.join(ROOT, "dense_gemm_tn_amd", "csrc", "gemm_tn.hip")
+CSRC = os.path.join(ROOT, "dense_gemm_tn_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
 
-def source_hash() -> str:
-    return hashlib.sha256(open(SRC, "rb").read()).hexdigest()[:16]
+def source_file(kind: str) -> str:
+    """The source that holds the kernel of a workload kind."""
+    return os.path.join(CSRC, "attention.hip" if kind == "attn" else "gemm_tn.hip")
+
+
+def source_hash(kind: str = "f16") -> str:
+    return hashlib.sha256(open(source_file(kind), "rb").read()).hexdigest()[:16]
 
 
 def algorithmic_bytes(w) -> int:
     """Read A and B once, write C once (the ideal-traffic model of section 11.6 of
-    the hello-gpu chapter, with 2-byte fp16 / 1-byte fp8 inputs and 2-byte outputs)."""
+    the hello-gpu chapter, with 2-byte fp16 / 1-byte fp8 inputs and 2-byte outputs).
+    Attention: read Q, K and V once and write O once (M*D + 2*N*D + M*D fp16 per head)."""
+    if w.kind == "attn":
+        return w.batch * (2 * w.M * w.K + 2 * w.N * w.K) * 2
     es = 1 if w.kind == "f8" else 2
     return w.batch * ((w.M * w.K + w.N * w.K) * es + w.M * w.N * 2)
 
@@ -83,7 +94,13 @@ def make_launcher(w, dev):
     R = rotation_sets(w)
     sets = []
     for r in range(R):
-        if w.kind == "qkt":
+        if w.kind == "attn":
+            q = torch.from_numpy(x["Q"]).to(dev)
+            k = torch.from_numpy(x["K"]).to(dev)
+            vt = torch.from_numpy(x["Vt"]).to(dev)
+            o = torch.empty((w.batch, w.M, w.K), dtype=torch.float16, device=dev)
+            sets.append((q, k, vt, o))
+        elif w.kind == "qkt":
             q = torch.from_numpy(x["Q"]).to(dev)
             k = torch.from_numpy(x["K"]).to(dev)
             s = torch.empty((w.batch, w.N, w.M), dtype=torch.float16, device=dev)
@@ -95,7 +112,14 @@ def make_launcher(w, dev):
             c = torch.empty((w.N, w.M), dtype=cdt, device=dev)
             sets.append((a, b, c))
 
+    scale = 1.0 / w.K ** 0.5
+
     def launch(i):
+        if w.kind == "attn":
+            q, k, vt, o = sets[i % R]
+            dg.attention_fwd_f16(q, k, vt, o, w.batch, w.M, w.N, w.K, w.K, w.K, w.N, w.K,
+                                 w.M * w.K, w.N * w.K, w.K * w.N, w.M * w.K, scale)
+            return
         a, b, c = sets[i % R]
         if w.kind == "f16":
             dg.gemm_f16_tn(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M)
@@ -148,7 +172,7 @@ def traffic_for(name, w, kernel_s):
     except ValueError:
         return None
     ent = t.get("workloads", {}).get(name)
-    if not ent or t.get("source_sha256_16") != source_hash():
+    if not ent or ent.get("source_sha256_16", t.get("source_sha256_16")) != source_hash(w.kind):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -209,7 +233,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", action="append", default=None,
-                    help="workload names (default: f16_4096 and f8_8192)")
+                    help="workload names (default: f16_4096, f8_8192 and "
+                         "attn_64x4096x4096x128)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (a known-size kernel for "
@@ -238,7 +263,7 @@ def main():
     from dense_gemm_tn_amd import inputs
 
     dev = torch.device("cuda:0")
-    names = args.workload or ["f16_4096", "f8_8192"]
+    names = args.workload or ["f16_4096", "f8_8192", "attn_64x4096x4096x128"]
     head = "f16_4096" if "f16_4096" in names else names[0]
     results = {}
     keep = {}
@@ -290,7 +315,7 @@ def main():
                      ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "cpu_baseline": cpu,
         "workloads": results,
-        "kernel_source_sha256_16": source_hash(),
+        "kernel_source_sha256_16": {k: source_hash(k) for k in ("f16", "attn")},
     }
     print(json.dumps(line), flush=True)
 

@@ -43,6 +43,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dense_gemm_tn.h"
 
 namespace dga {
@@ -201,10 +203,17 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(const AttnPa
   float4_t o[8][2];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt][0] = o[dt][1] = float4_t{0.f, 0.f, 0.f, 0.f};
+  // Running reference maximum (log2 units) and this lane's part of the sum of
+  // the fp16-rounded probabilities, per query column u.
   float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
   const float c = p.c;
+  typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+  const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  for (int kb = 0; kb < p.n_blocks; ++kb) {
+  // One key block.  kMasked: the block is the last one and N cuts it, so keys
+  // past N get score -inf and probability 0 (only that block pays for it).
+  auto block = [&](int kb, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     const int st = kb & 1;
     if (kb + 1 < p.n_blocks) issue_copies(kb + 1, st ^ 1);
     const lds_u8 *Ks = lds + st * kStage;
@@ -224,37 +233,58 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(const AttnPa
       }
     }
 
-    const int64_t valid = p.N - (int64_t)kb * kBN;  // >= 1
+    const int valid = kMasked ? (int)(p.N - (int64_t)kb * kBN) : kBN;
+    float mx[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (kMasked && 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e >= valid)
+            sacc[t][u][e] = -INFINITY;
+          m = fmaxf(m, sacc[t][u][e]);
+        }
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      mx[u] = m * c;
+    }
+    // The reference maximum moves only when a block's maximum exceeds it by
+    // more than 2^kTau in probability (or on the first block): probabilities
+    // then stay <= 2^kTau, far inside fp16 range, and the rescaling of O and l
+    // (exact in real arithmetic: it cancels in O / l) is skipped for most
+    // blocks.  The branch is taken per wave.
+    constexpr float kTau = 8.0f;
+    if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + kTau || mx[1] > m_run[1] + kTau)) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float mnew = fmaxf(m_run[u], mx[u]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[u] - mnew);
+        m_run[u] = mnew;
+        l_run[u] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[dt][u] *= alpha;
+      }
+    }
+
     half8_t pf[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      float mx = -INFINITY;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int key = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e;
-          if (valid < kBN && key >= valid) sacc[t][u][e] = -INFINITY;
-          mx = fmaxf(mx, sacc[t][u][e]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m_run[u], mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[u] - mnew);
-      m_run[u] = mnew;
-      l_run[u] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt][u] *= alpha;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e;
-          float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][u][e], c, -mnew));
-          if (valid < kBN && key >= valid) pv = 0.f;
-          l_run[u] += pv;
+          float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][u][e], c, -m_run[u]));
+          if (kMasked && 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e >= valid) pv = 0.f;
           pf[t >> 1][u][4 * (t & 1) + e] = (_Float16)pv;
         }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          l_run[u] = __builtin_amdgcn_fdot2(
+              half2_t{pf[j][u][2 * h], pf[j][u][2 * h + 1]}, ones, l_run[u], false);
     }
 
 #pragma unroll
@@ -270,7 +300,11 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(const AttnPa
 
     if (kb + 1 < p.n_blocks) finish_copies(kb + 1, st ^ 1);
     __syncthreads();
-  }
+  };
+
+  const int full_blocks = (int)(p.N / kBN);
+  for (int kb = 0; kb < full_blocks; ++kb) block(kb, std::false_type{});
+  if (full_blocks < p.n_blocks) block(full_blocks, std::true_type{});
 
   // Normalise and store: lane (i, g) holds O[q][16 dt + 4 g + e] of query
   // q = q0 + 16u + i.
