@@ -25,8 +25,10 @@
 //     operand straight from the lane's registers (no shuffle), and the Vt
 //     operand is one 16-byte LDS read.
 //   * Online softmax in base 2 (exp2 of scale*log2(e)*s minus the running
-//     maximum), the maximum reduced across the four lanes of a query by two
-//     cross-lane exchanges; the running sum stays per lane until the end.
+//     reference maximum), the maximum reduced across the four lanes of a query
+//     by two lane-swap instructions; the running sum stays per lane until the
+//     end.  The reference maximum moves only when a block's maximum exceeds it
+//     by more than 2^8 in probability, so O is rarely rescaled.
 //   * LDS swizzles: K rows (256 B) store chunk c of row r in slot
 //     c ^ ((r & 3) | ((r >> 1) & 12)), which is the lane's row index in its
 //     MFMA tile, so a 16-lane read phase touches 16 distinct 16-byte slots;
@@ -92,6 +94,36 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 // s_waitcnt immediate for "no vector-memory operation outstanding" (vmcnt 0,
 // expcnt and lgkmcnt left at their maxima).
 constexpr int kVmcnt0 = (7 << 4) | (15 << 8);
+
+// Exchanges between the four lanes l, l ^ 16, l ^ 32, l ^ 48 that hold one
+// query column, with the gfx950 lane-swap instructions (no trip through LDS).
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with
+// the lower 32 lanes of its second, v_permlane16_swap the odd 16-lane rows of
+// the first with the even rows of the second; starting from two copies of x,
+// each pair of results then holds x and its partner lane's x in every lane.
+// Written as inline assembly because the compiler folds the builtins' two
+// results into one when both inputs are the same value.  The s_nop gives the
+// wait states a lane-swap needs after a VALU write of its operands.
+__device__ __forceinline__ void swap32(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32_e32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap16(float &a, float &b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32_e32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_over_column(float x) {
+  float a = x, b = x;
+  swap32(a, b);
+  float c = fmaxf(a, b), d = c;
+  swap16(c, d);
+  return fmaxf(c, d);
+}
+__device__ __forceinline__ float sum_over_column(float x) {
+  float a = x, b = x;
+  swap32(a, b);
+  float c = a + b, d = c;
+  swap16(c, d);
+  return c + d;
+}
 
 __device__ __forceinline__ float4_t mma(const half8_t &a, const half8_t &b, const float4_t &c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -246,9 +278,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(const AttnPa
             sacc[t][u][e] = -INFINITY;
           m = fmaxf(m, sacc[t][u][e]);
         }
-      m = fmaxf(m, __shfl_xor(m, 16));
-      m = fmaxf(m, __shfl_xor(m, 32));
-      mx[u] = m * c;
+      mx[u] = max_over_column(m) * c;
     }
     // The reference maximum moves only when a block's maximum exceeds it by
     // more than 2^kTau in probability (or on the first block): probabilities
@@ -310,10 +340,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(const AttnPa
   // q = q0 + 16u + i.
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    float l = l_run[u];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const float inv = 1.0f / l;
+    const float inv = 1.0f / sum_over_column(l_run[u]);
     const int64_t q = q0 + 16 * u + i;
     if (q < p.M) {
       _Float16 *orow = (_Float16 *)p.O + head * p.so + q * p.ldo + 4 * g;
