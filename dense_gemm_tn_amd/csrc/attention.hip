@@ -58,14 +58,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kD = 128;                 // head dim
-constexpr int kBM = 128;                // queries per workgroup
+constexpr int kWaveQ = 64;              // queries per wave
+constexpr int kBM = 4 * kWaveQ;         // queries per workgroup
 constexpr int kBN = 64;                 // keys per block
 constexpr int kThreads = 256;           // 4 waves
 constexpr int kKRow = kD * 2;           // bytes per K row in LDS
 constexpr int kVRow = kBN * 2;          // bytes per Vt row in LDS
 constexpr int kKBytes = kBN * kKRow;    // 16 KiB
 constexpr int kVBytes = kD * kVRow;     // 16 KiB
-constexpr int kStage = kKBytes + kVBytes;
+constexpr int kLdsBytes = 3 * kKBytes + 2 * kVBytes;  // three K slots, two Vt slots
 constexpr int kXcds = 8;
 constexpr uint32_t kOob = 0x80000000u;  // an offset past every descriptor
 // Word 3 of a raw buffer resource (32-bit data format: byte range checking).
@@ -117,6 +118,13 @@ __device__ __forceinline__ float max_over_column(float x) {
   swap16(c, d);
   return fmaxf(c, d);
 }
+// max(a, b, c) without the quieting the compiler adds to fmaxf in IEEE mode
+// (the operands here are finite scores or -inf).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float sum_over_column(float x) {
   float a = x, b = x;
   swap32(a, b);
@@ -125,12 +133,92 @@ __device__ __forceinline__ float sum_over_column(float x) {
   return c + d;
 }
 
-__device__ __forceinline__ float4_t mma(const half8_t &a, const half8_t &b, const float4_t &c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+// Matrix-core products, all v_mfma_f32_16x16x32_f16 written as inline
+// assembly so each operand stays in the register file chosen for it:
+//   * score products S^T = K Q^T accumulate in VGPRs (the softmax reads
+//     them) and take the wave's resident Q fragments from AGPRs;
+//   * output products O^T += Vt P^T accumulate in place in AGPRs.  While an
+//     MFMA with AGPR accumulators runs, the SIMD still issues about two
+//     independent VALU instructions of the same wave (measured on MI355X; with
+//     VGPR accumulators about one), which is what hides the softmax.
+// The compiler knows no latency for these, so every VALU read of an MFMA
+// result is placed behind a scheduling barrier far enough after the product
+// (or behind mfma_drain), and a product whose B operand was just written by
+// the VALU starts with the two wait states that hazard needs.
+__device__ __forceinline__ void mma_s0(const half8_t &a, const half8_t &b, float4_t &c) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mma_s(const half8_t &a, const half8_t &b, float4_t &c) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "a"(b));
+}
+__device__ __forceinline__ void mma_o(const half8_t &a, const half8_t &b, float4_t &c) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_o_fresh_b(const half8_t &a, const half8_t &b, float4_t &c) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// fp32 16x16x4 products that rewrite an output tile (see the rescale below).
+// The first one overwrites the tile in place ("+a" keeps the tile in its
+// registers, so no copies appear where the rare path rejoins).
+__device__ __forceinline__ void mma_f32_0(float a, float b, float4_t &c) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x4_f32 %0, %1, %2, 0" : "+a"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mma_f32(float a, float b, float4_t &c) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_16x16x4_f32 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+// Wait states after the last MFMA before other instructions read its result.
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(const AttnParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStage];
+// Empty statements that "modify" a value in place: placed after mfma_drain,
+// they keep reads of an MFMA result from being hoisted above the wait.
+__device__ __forceinline__ void tie_agpr(float4_t &v) { asm volatile("" : "+a"(v)); }
+__device__ __forceinline__ void tie_vgpr(float4_t &v) { asm volatile("" : "+v"(v)); }
+
+// mfma_drain for accumulators that other instructions read next: the empty
+// statements tie each tile to the wait, so no read is hoisted above it.
+template <int R, int C>
+__device__ __forceinline__ void drain_agprs(float4_t (&acc)[R][C]) {
+  mfma_drain();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int c = 0; c < C; ++c) tie_agpr(acc[r][c]);
+}
+
+// f(std::integral_constant<int, k>) for k = B .. E-1, in order: compile-time
+// slot indices, so every register-array index below is a constant.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Schedule of one key block kb ("body"), per wave.  The wave's 64 queries are
+// two halves of 32 (query tiles u = 2H, 2H + 1), each with its own scores,
+// softmax state and output tiles, run half a block apart so one half's
+// matrix-core products always overlap the other half's softmax arithmetic:
+//
+//   slots   MFMA (one per slot)                VALU (about two per slot)
+//   0..31   scores of half 1, block kb         probabilities of half 0, block kb
+//   32..63  output of half 0, block kb         ... and maxima of half 1, block kb
+//   64..95  scores of half 0, block kb + 1     probabilities of half 1, block kb
+//   96..127 output of half 1, block kb         ... and maxima of half 0, block kb + 1
+//
+// Each group of two slots shares one operand fragment read from LDS
+// (K rows for scores, Vt rows for outputs), three groups ahead.  A half's
+// reference maximum is checked (and, rarely, moved) right after its maxima.
+constexpr int kSlots = 128;
+constexpr int kGroups = kSlots / 2;   // one fragment per group of two MFMAs
+constexpr int kAhead = 3;             // fragment lookahead in groups
+constexpr int kRing = 8;              // fragment registers (divides kGroups)
+static_assert(kGroups % kRing == 0 && kAhead < kRing, "fragment ring");
+
+__global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
 
@@ -140,17 +228,17 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(const AttnPa
   const int x = b % kXcds, q8 = p.blocks / kXcds, r8 = p.blocks % kXcds;
   const int logical = x * q8 + (x < r8 ? x : r8) + b / kXcds;
   const int head = logical / p.tiles_m;
-  const int64_t q0 = (int64_t)(logical - head * p.tiles_m) * kBM + 32 * w;
+  const int64_t q0 = (int64_t)(logical - head * p.tiles_m) * kBM + kWaveQ * w;
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + head * p.sq_b, p.q_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.K + head * p.sk_b, p.k_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.V + head * p.sv_b, p.v_bytes);
 
-  // Q fragments: column tile u, K-step s (32 dims): lane (i, g) holds query
-  // q0 + 16u + i, dims 32s + 8g .. +7.
-  half8_t qf[2][4];
+  // Q fragments (AGPRs): query tile u, K-step s (32 dims): lane (i, g) holds
+  // query q0 + 16u + i, dims 32s + 8g .. +7.
+  half8_t qf[4][4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < 4; ++u) {
     const int64_t row = q0 + 16 * u + i;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -160,51 +248,59 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(const AttnPa
     }
   }
 
-  // Copy plan.  K: wave load q fills LDS rows 16q + 4w .. +3 (1 KiB); lane l
-  // lands in row 16q + 4w + (l >> 4), slot l & 15, and fetches the chunk the
-  // swizzle keeps there.  Vt: wave load q fills rows 32q + 8w .. +7; lane l
-  // lands in row 32q + 8w + (l >> 3), slot l & 7.
+  // LDS: three K slots (block b in slot b % 3) and two Vt slots (b & 1).
+  // K: wave load q fills LDS rows 16q + 4w .. +3 (1 KiB); lane l lands in row
+  // 16q + 4w + (l >> 4), slot l & 15, and fetches the chunk the swizzle keeps
+  // there.  Vt: wave load q fills rows 32q + 8w .. +7; lane l lands in row
+  // 32q + 8w + (l >> 3), slot l & 7.
   uint32_t koff[4], voff[4];
   int vkey[4];  // first key (block-relative) of the lane's Vt chunk
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int r = 16 * q + 4 * w + (lane >> 4);
-    const int c = (lane & 15) ^ ((r & 3) | ((r >> 1) & 12));
-    koff[q] = (uint32_t)(r * p.ldk_b) + (uint32_t)(c * 16);
+    const int cc = (lane & 15) ^ ((r & 3) | ((r >> 1) & 12));
+    koff[q] = (uint32_t)(r * p.ldk_b) + (uint32_t)(cc * 16);
     const int rv_ = 32 * q + 8 * w + (lane >> 3);
     const int cv = (lane & 7) ^ ((rv_ >> 1) & 7);
     voff[q] = (uint32_t)(rv_ * p.ldv_b) + (uint32_t)(cv * 16);
     vkey[q] = 8 * cv;
   }
   lds_u8 *const lds = (lds_u8 *)smem;
+  auto kslot = [&](int kb) { return lds + (kb % 3) * kKBytes; };
+  auto vslot = [&](int kb) { return lds + 3 * kKBytes + (kb & 1) * kVBytes; };
 
-  auto issue_copies = [&](int kb, int st) {
-    lds_u8 *kd = lds + st * kStage + (4 * w) * kKRow;
-    lds_u8 *vd = lds + st * kStage + kKBytes + (8 * w) * kVRow;
+  // Load q (0..3) of this wave's share of K block kb / Vt block kb.
+  auto copy_k1 = [&](int kb, int q) {
+    lds_u8 *kd = kslot(kb) + (4 * w) * kKRow;
     const uint32_t kbase = (uint32_t)((int64_t)kb * kBN * p.ldk_b);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(kd + q * 16 * kKRow), 16,
-                                               kbase + koff[q], 0, 0, 0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      // Only whole 8-key chunks are copied; a chunk that straddles N is filled
-      // by finish_copies, so nothing past a row's N keys is ever read.
-      const uint32_t off =
-          (int64_t)kb * kBN + vkey[q] + 8 <= p.N ? voff[q] + (uint32_t)(kb * kVRow) : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vd + q * 32 * kVRow), 16, off,
-                                               0, 0, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(kd + q * 16 * kKRow), 16,
+                                             kbase + koff[q], 0, 0, 0);
   };
-  // Wait for this wave's copies of key block kb (in stage st).  If N cuts an
-  // 8-key chunk of that block, the lane that owns the chunk's LDS slot (its
-  // copy read zeros) fills the valid keys with 2-byte loads and leaves the
-  // rest zero; the slot is the lane's own, so no other wave is involved.
-  auto finish_copies = [&](int kb, int st) {
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  auto copy_v1 = [&](int kb, int q) {
+    lds_u8 *vd = vslot(kb) + (8 * w) * kVRow;
+    // Only whole 8-key chunks are copied; a chunk that straddles N is filled
+    // by finish_v, so nothing past a row's N keys is ever read.
+    const uint32_t off =
+        (int64_t)kb * kBN + vkey[q] + 8 <= p.N ? voff[q] + (uint32_t)(kb * kVRow) : kOob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vd + q * 32 * kVRow), 16, off, 0,
+                                             0, 0);
+  };
+  auto copy_k = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) copy_k1(kb, q);
+  };
+  auto copy_v = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) copy_v1(kb, q);
+  };
+  // After this wave's copies have landed: if N cuts an 8-key chunk of Vt
+  // block kb, the lane that owns the chunk's LDS slot (its copy read zeros)
+  // fills the valid keys with 2-byte loads and leaves the rest zero; the slot
+  // is the lane's own, so no other wave is involved.
+  auto finish_v = [&](int kb) {
     const int64_t tail = p.N - (int64_t)kb * kBN;  // valid keys in this block
     if (tail < kBN && (tail & 7)) {
-      lds_u8 *vd = lds + st * kStage + kKBytes + (8 * w) * kVRow;
+      lds_u8 *vd = vslot(kb) + (8 * w) * kVRow;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (vkey[q] == (int)(tail & ~7)) {
@@ -218,128 +314,302 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(const AttnPa
     }
   };
 
-  issue_copies(0, 0);
-  finish_copies(0, 0);
-  __syncthreads();
-
-  // K row read by lane i of S^T tile t (block-relative key):
-  // 32 (t >> 1) + 8 (i >> 2) + 4 (t & 1) + (i & 3).  The lane then holds keys
-  // 32 (t >> 1) + 8 g + 4 (t & 1) + e of its query column, e < 4.
-  uint32_t kread[4];
+  // Fragment addresses.  K row read by lane i of score tile t (block-relative
+  // key): 32 (t >> 1) + 8 (i >> 2) + 4 (t & 1) + (i & 3); the lane then holds
+  // keys 32 (t >> 1) + 8 g + 4 (t & 1) + e of its query column, e < 4, and
+  // the keys of tiles 2j, 2j + 1 are the eight consecutive keys 32j + 8g ..
+  // of the Vt fragment of K-step j.
+  const uint32_t kread0 = (uint32_t)((8 * (i >> 2) + (i & 3)) * kKRow);
+  uint32_t ksw[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-    kread[t] = (uint32_t)((32 * (t >> 1) + 8 * (i >> 2) + 4 * (t & 1) + (i & 3)) * kKRow);
-  const uint32_t vread = (uint32_t)(i * kVRow);
-  const int vsw = (i >> 1) & 7;
-
-  float4_t o[8][2];
+  for (int s = 0; s < 4; ++s) ksw[s] = kread0 + (uint32_t)((((4 * s + g) ^ i) << 4));
+  uint32_t vsw[2];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) o[dt][0] = o[dt][1] = float4_t{0.f, 0.f, 0.f, 0.f};
-  // Running reference maximum (log2 units) and this lane's part of the sum of
-  // the fp16-rounded probabilities, per query column u.
-  float m_run[2] = {-1e30f, -1e30f}, l_run[2] = {0.f, 0.f};
+  for (int j = 0; j < 2; ++j) vsw[j] = (uint32_t)(i * kVRow + (((4 * j + g) ^ ((i >> 1) & 7)) << 4));
+  // Fragment of group f (0..63) of the body over key block kb: groups 0..15
+  // and 32..47 are K fragments (t, s) of blocks kb and kb + 1, the others Vt
+  // fragments (j, dt) of block kb.
+  auto frag = [&](int kb, auto fc) -> half8_t {
+    constexpr int f = decltype(fc)::value, ph = f >> 4, y = f & 15;
+    if constexpr (ph == 0 || ph == 2) {
+      constexpr int t = y >> 2, s = y & 3;
+      const lds_u8 *Ks = kslot(ph == 0 ? kb : kb + 1);
+      return *(const __attribute__((address_space(3))) half8_t *)(
+          Ks + ksw[s] + (32 * (t >> 1) + 4 * (t & 1)) * kKRow);
+    } else {
+      constexpr int j = y >> 3, dt = y & 7;
+      return *(const __attribute__((address_space(3))) half8_t *)(vslot(kb) + vsw[j] +
+                                                                 dt * 16 * kVRow);
+    }
+  };
+
+  const int n = p.n_blocks;
   const float c = p.c;
   typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
   const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+  float4_t o[8][4];  // O^T tiles [dt][u], AGPRs
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[dt][u] = float4_t{0.f, 0.f, 0.f, 0.f};
+  // Per query tile u: reference maximum (log2 units) and this lane's part of
+  // the sum of the fp16-rounded probabilities.
+  float m_run[4], l_run[4] = {0.f, 0.f, 0.f, 0.f};
+  float4_t sc[2][4][2];  // scores [half][t][uu] of the half's current block
+  half8_t pf[2][2][2];   // probabilities [half][j][uu] as output-product operands
+  float mloc[2][2], mx[2][2];
+  float pv8[8];
+  half8_t fr[kRing];
 
-  // One key block.  kMasked: the block is the last one and N cuts it, so keys
-  // past N get score -inf and probability 0 (only that block pays for it).
-  auto block = [&](int kb, auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    const int st = kb & 1;
-    if (kb + 1 < p.n_blocks) issue_copies(kb + 1, st ^ 1);
-    const lds_u8 *Ks = lds + st * kStage;
-    const lds_u8 *Vs = Ks + kKBytes;
-
-    float4_t sacc[4][2];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const half8_t a =
-            *(const __attribute__((address_space(3))) half8_t *)(Ks + kread[t] +
-                                                                 (((4 * s + g) ^ i) << 4));
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          sacc[t][u] = mma(a, qf[u][s], s == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : sacc[t][u]);
-      }
-    }
-
-    const int valid = kMasked ? (int)(p.N - (int64_t)kb * kBN) : kBN;
-    float mx[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (kMasked && 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e >= valid)
-            sacc[t][u][e] = -INFINITY;
-          m = fmaxf(m, sacc[t][u][e]);
-        }
-      mx[u] = max_over_column(m) * c;
-    }
-    // The reference maximum moves only when a block's maximum exceeds it by
-    // more than 2^kTau in probability (or on the first block): probabilities
-    // then stay <= 2^kTau, far inside fp16 range, and the rescaling of O and l
-    // (exact in real arithmetic: it cancels in O / l) is skipped for most
-    // blocks.  The branch is taken per wave.
-    constexpr float kTau = 8.0f;
-    if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + kTau || mx[1] > m_run[1] + kTau)) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const float mnew = fmaxf(m_run[u], mx[u]);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[u] - mnew);
-        m_run[u] = mnew;
-        l_run[u] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) o[dt][u] *= alpha;
-      }
-    }
-
-    half8_t pf[2][2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pv = __builtin_amdgcn_exp2f(fmaf(sacc[t][u][e], c, -m_run[u]));
-          if (kMasked && 32 * (t >> 1) + 8 * g + 4 * (t & 1) + e >= valid) pv = 0.f;
-          pf[t >> 1][u][4 * (t & 1) + e] = (_Float16)pv;
-        }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-          l_run[u] = __builtin_amdgcn_fdot2(
-              half2_t{pf[j][u][2 * h], pf[j][u][2 * h + 1]}, ones, l_run[u], false);
-    }
-
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const half8_t a = *(const __attribute__((address_space(3))) half8_t *)(
-            Vs + dt * 16 * kVRow + vread + (((4 * j + g) ^ vsw) << 4));
-#pragma unroll
-        for (int u = 0; u < 2; ++u) o[dt][u] = mma(a, pf[j][u], o[dt][u]);
-      }
-    }
-
-    if (kb + 1 < p.n_blocks) finish_copies(kb + 1, st ^ 1);
-    __syncthreads();
+  auto fence_accumulators = [&]() {
+    mfma_drain();
+    static_for<0, 32>([&](auto tc) {
+      tie_agpr(o[decltype(tc)::value >> 2][decltype(tc)::value & 3]);
+    });
+    static_for<0, 16>([&](auto tc) {
+      constexpr int v = decltype(tc)::value;
+      tie_vgpr(sc[v >> 3][(v >> 1) & 3][v & 1]);
+    });
   };
 
-  const int full_blocks = (int)(p.N / kBN);
-  for (int kb = 0; kb < full_blocks; ++kb) block(kb, std::false_type{});
-  if (full_blocks < p.n_blocks) block(full_blocks, std::true_type{});
+  // The reference maximum moves only when a block's maximum exceeds it by
+  // more than 2^kTau in probability: probabilities stay <= 2^kTau, far inside
+  // fp16 range, and O and l are rescaled (exact in real arithmetic: the factor
+  // cancels in O / l) only on those rare blocks.  The decision is per wave.
+  constexpr float kTau = 8.0f;
+  // Moves half H's reference maxima to cover mx[H] (rare).  O's tiles are
+  // rewritten by v_mfma_f32_16x16x4_f32 with A (lane l: row l & 15, k = l >> 4)
+  // = [row == 4k + kk] and B (lane l: k-row l >> 4, column l & 15) = element kk
+  // of the lane's scaled tile, which gives back the scaled tile: the rewrite
+  // stays in the AGPRs and O is never written by anything but MFMAs.
+  auto check_half = [&](auto hc) {
+    constexpr int H = decltype(hc)::value;
+    if (__builtin_amdgcn_ballot_w64(mx[H][0] > m_run[2 * H] + kTau ||
+                                    mx[H][1] > m_run[2 * H + 1] + kTau)) {
+      // Column maxima across the four lanes of each query.
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) mx[H][uu] = max_over_column(mloc[H][uu]) * c;
+      mfma_drain();
+      static_for<0, 8>([&](auto dc) {
+        constexpr int dt = decltype(dc)::value;
+        tie_agpr(o[dt][2 * H]);
+        tie_agpr(o[dt][2 * H + 1]);
+      });
+      float alpha[2];
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int u = 2 * H + uu;
+        const float mnew = fmaxf(m_run[u], mx[H][uu]);
+        alpha[uu] = __builtin_amdgcn_exp2f(m_run[u] - mnew);
+        m_run[u] = mnew;
+        l_run[u] *= alpha[uu];
+      }
+      float sel[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) sel[kk] = (i == 4 * g + kk) ? 1.0f : 0.0f;
+      static_for<0, 16>([&](auto tc) {
+        constexpr int dt = decltype(tc)::value >> 1, uu = decltype(tc)::value & 1;
+        const float4_t v = o[dt][2 * H + uu] * alpha[uu];
+        mma_f32_0(sel[0], v[0], o[dt][2 * H + uu]);
+#pragma unroll
+        for (int kk = 1; kk < 4; ++kk) mma_f32(sel[kk], v[kk], o[dt][2 * H + uu]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      mfma_drain();
+    }
+  };
 
+  // VALU share of the probabilities of half H (item 0..47): items 12 (2j + uu)
+  // .. +11 make pf[H][j][uu]: eight exp2 items, then four pack-and-sum items.
+  auto prob_item = [&](auto hc, auto ic, int valid, auto mask) {
+    constexpr int H = decltype(hc)::value, it = decltype(ic)::value;
+    constexpr int j = it / 24, uu = (it % 24) / 12, r = it % 12, u = 2 * H + uu;
+    if constexpr (r < 8) {
+      constexpr int t = 2 * j + (r >> 2), e = r & 3;
+      float pv = __builtin_amdgcn_exp2f(fmaf(sc[H][t][uu][e], c, -m_run[u]));
+      if (decltype(mask)::value && 32 * j + 8 * g + 4 * (t & 1) + e >= valid) pv = 0.f;
+      pv8[r] = pv;
+    } else {
+      constexpr int h = r - 8;
+      pf[H][j][uu][2 * h] = (_Float16)pv8[2 * h];
+      pf[H][j][uu][2 * h + 1] = (_Float16)pv8[2 * h + 1];
+      l_run[u] = __builtin_amdgcn_fdot2(half2_t{pf[H][j][uu][2 * h], pf[H][j][uu][2 * h + 1]},
+                                        ones, l_run[u], false);
+    }
+  };
+  // VALU share of the maxima of half H (item 0..11): per uu, four items fold
+  // one score tile each into the lane's running maximum, then it is scaled to
+  // log2 units.  Only the lane's own keys are covered: the reference is
+  // checked lane by lane (any lane over it moves the whole column, and the
+  // column maximum is reduced across lanes only then).
+  auto max_item = [&](auto hc, auto ic, int valid, auto mask) {
+    constexpr int H = decltype(hc)::value, it = decltype(ic)::value;
+    constexpr int uu = it / 6, r = it % 6;
+    if constexpr (r < 4) {
+      constexpr int t = r;
+      if constexpr (decltype(mask)::value) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (32 * (t >> 1) + 8 * g + 4 * (t & 1) + e >= valid) sc[H][t][uu][e] = -INFINITY;
+      }
+      const float4_t &v = sc[H][t][uu];
+      if constexpr (r == 0) {
+        mloc[H][uu] = max3(max3(v[0], v[1], v[2]), v[3], v[3]);
+      } else {
+        mloc[H][uu] = max3(max3(mloc[H][uu], v[0], v[1]), v[2], v[3]);
+      }
+    } else if constexpr (r == 4) {
+      mx[H][uu] = mloc[H][uu] * c;
+    }
+  };
+  // The MFMA of group slot (phase ph, group y, member uu).
+  auto slot_mfma = [&](auto fc, auto uc, const half8_t &a) {
+    constexpr int f = decltype(fc)::value, uu = decltype(uc)::value;
+    constexpr int ph = f >> 4, y = f & 15;
+    if constexpr (ph == 0 || ph == 2) {
+      constexpr int H = ph == 0 ? 1 : 0, t = y >> 2, s = y & 3;
+      if constexpr (s == 0)
+        mma_s0(a, qf[2 * H + uu][s], sc[H][t][uu]);
+      else
+        mma_s(a, qf[2 * H + uu][s], sc[H][t][uu]);
+    } else {
+      constexpr int H = ph == 1 ? 0 : 1, j = y >> 3, dt = y & 7;
+      if constexpr (dt == 0)
+        mma_o_fresh_b(a, pf[H][j][uu], o[dt][2 * H + uu]);
+      else
+        mma_o(a, pf[H][j][uu], o[dt][2 * H + uu]);
+    }
+  };
+
+  // One body.  kNext: block kb + 1 exists (its half-0 scores and maxima are
+  // part of this body).  mask_cur: block kb may be cut by N; mask_next: block
+  // kb + 1 may be.  Fragments of this body's first kAhead groups were read by
+  // the previous body (or the prologue); this body reads the next body's.
+  auto body = [&](int kb, auto has_next, auto mask_cur, auto mask_next) {
+    constexpr bool kNext = decltype(has_next)::value;
+    const int64_t rest = p.N - (int64_t)kb * kBN;
+    const int valid = decltype(mask_cur)::value && rest < kBN ? (int)rest : kBN;
+    const int64_t rest1 = rest - kBN;
+    const int valid1 = decltype(mask_next)::value && rest1 < kBN ? (int)rest1 : kBN;
+    const bool more_k = kb + 2 < n;
+    auto run_slots = [&](auto lo, auto hi) {
+      static_for<decltype(lo)::value, decltype(hi)::value>([&](auto kc) {
+        constexpr int k = decltype(kc)::value, f = k >> 1, uu = k & 1, ph = f >> 4;
+        // Fragment read kAhead groups ahead (the next body's first groups are
+        // K fragments of block kb + 1, which is resident now).
+        if constexpr (uu == 0) {
+          constexpr int fn = f + kAhead;
+          if constexpr (fn < kGroups) {
+            if constexpr (kNext || !(fn >= 32 && fn < 48))
+              fr[fn % kRing] = frag(kb, std::integral_constant<int, fn>{});
+          } else if constexpr (kNext) {
+            fr[fn % kRing] = frag(kb + 1, std::integral_constant<int, fn - kGroups>{});
+          }
+        }
+        // Copies of K block kb + 2 and Vt block kb + 1, spread over slots.
+        if constexpr (kNext && (k & 7) == 3 && k < 64) {
+          if constexpr ((k >> 3) < 4) {
+            if (more_k) copy_k1(kb + 2, k >> 3);
+          } else {
+            copy_v1(kb + 1, (k >> 3) - 4);
+          }
+        }
+        // VALU share.
+        if constexpr (k < 48) {
+          prob_item(std::integral_constant<int, 0>{}, std::integral_constant<int, k>{}, valid,
+                    mask_cur);
+        } else if constexpr (k >= 50 && k < 62) {
+          max_item(std::integral_constant<int, 1>{}, std::integral_constant<int, k - 50>{},
+                   valid, mask_cur);
+        } else if constexpr (k >= 64 && k < 112) {
+          prob_item(std::integral_constant<int, 1>{}, std::integral_constant<int, k - 64>{},
+                    valid, mask_cur);
+        } else if constexpr (kNext && k >= 114 && k < 126) {
+          max_item(std::integral_constant<int, 0>{}, std::integral_constant<int, k - 114>{},
+                   valid1, mask_next);
+        }
+        // The MFMA.
+        if constexpr (kNext || ph != 2)
+          slot_mfma(std::integral_constant<int, f>{}, std::integral_constant<int, uu>{},
+                    fr[f % kRing]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // Each run of slots ends a basic block; the compiler may place register
+    // copies at block boundaries, so the products still in flight are drained
+    // and every accumulator is tied to that point first.
+    run_slots(std::integral_constant<int, 0>{}, std::integral_constant<int, 64>{});
+    fence_accumulators();
+    check_half(std::integral_constant<int, 1>{});
+    run_slots(std::integral_constant<int, 64>{}, std::integral_constant<int, 128>{});
+    fence_accumulators();
+    if constexpr (kNext) {
+      check_half(std::integral_constant<int, 0>{});
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      finish_v(kb + 1);
+      __syncthreads();
+    }
+  };
+
+  // Prologue: K blocks 0 and 1, Vt block 0; half-0 scores and maxima of block
+  // 0 set half 0's first reference maximum (half 1's is set by the first
+  // check, which always moves it from -inf).
+  copy_k(0);
+  if (n > 1) copy_k(1);
+  copy_v(0);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  finish_v(0);
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) m_run[u] = -1e30f;
+  {
+    // Scores of half 0, block 0 (K slot 0).
+    static_for<0, 16>([&](auto yc) {
+      constexpr int y = decltype(yc)::value, t = y >> 2, s = y & 3;
+      const half8_t a = *(const __attribute__((address_space(3))) half8_t *)(
+          kslot(0) + ksw[s] + (32 * (t >> 1) + 4 * (t & 1)) * kKRow);
+      if constexpr (s == 0) {
+        mma_s0(a, qf[0][s], sc[0][t][0]);
+        mma_s0(a, qf[1][s], sc[0][t][1]);
+      } else {
+        mma_s(a, qf[0][s], sc[0][t][0]);
+        mma_s(a, qf[1][s], sc[0][t][1]);
+      }
+    });
+    mfma_drain();
+    static_for<0, 4>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      tie_vgpr(sc[0][t][0]);
+      tie_vgpr(sc[0][t][1]);
+    });
+    const int64_t rest = p.N;
+    const int valid0 = rest < kBN ? (int)rest : kBN;
+    static_for<0, 12>([&](auto ic) {
+      max_item(std::integral_constant<int, 0>{}, ic, valid0, std::true_type{});
+    });
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) m_run[uu] = max_over_column(mloc[0][uu]) * c;
+  }
+  static_for<0, kAhead>([&](auto fc) {
+    constexpr int f = decltype(fc)::value;
+    fr[f % kRing] = frag(0, fc);
+  });
+
+  const std::true_type T;
+  const std::false_type F;
+  int kb = 0;
+  for (; kb + 2 < n; ++kb) body(kb, T, F, F);
+  if (kb + 1 < n) {
+    body(kb, T, F, T);
+    ++kb;
+  }
+  body(kb, F, T, F);
+
+  drain_agprs(o);
   // Normalise and store: lane (i, g) holds O[q][16 dt + 4 g + e] of query
   // q = q0 + 16u + i.
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < 4; ++u) {
     const float inv = 1.0f / sum_over_column(l_run[u]);
     const int64_t q = q0 + 16 * u + i;
     if (q < p.M) {
