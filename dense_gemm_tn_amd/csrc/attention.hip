@@ -506,12 +506,13 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
             fr[fn % kRing] = frag(kb + 1, std::integral_constant<int, fn - kGroups>{});
           }
         }
-        // Copies of K block kb + 2 and Vt block kb + 1, spread over slots.
-        if constexpr (kNext && (k & 7) == 3 && k < 64) {
-          if constexpr ((k >> 3) < 4) {
-            if (more_k) copy_k1(kb + 2, k >> 3);
+        // Copies of K block kb + 2 and Vt block kb + 1, one every other slot
+        // from the start of the body (the most time to land before its end).
+        if constexpr (kNext && (k & 1) == 1 && k < 16) {
+          if constexpr ((k >> 1) < 4) {
+            if (more_k) copy_k1(kb + 2, k >> 1);
           } else {
-            copy_v1(kb + 1, (k >> 3) - 4);
+            copy_v1(kb + 1, (k >> 1) - 4);
           }
         }
         // VALU share.

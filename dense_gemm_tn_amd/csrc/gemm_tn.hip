@@ -603,6 +603,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     }
   }
   mfma_drain();
+  // Tie every accumulator to the wait above, so the compiler cannot hoist an
+  // accumulator read (it does not know the products' latency) above it.
+#pragma unroll
+  for (int i = 0; i < NTM; ++i)
+#pragma unroll
+    for (int j = 0; j < NTN; ++j) asm volatile("" : "+a"(acc[i][j]));
 
   // Drain the trailing zero copies; every wave leaves the stages before the
   // epilogue reuses the LDS.
