@@ -15,8 +15,9 @@ two flops).
 
 Prints ONE JSON line.  The headline `value` is the FP16 TN 4096^3 workload; the
 FP8 8192^3 workload, the fused attention forward over 64 heads x 4096 queries x
-4096 keys x head dim 128 (4*M*N*D flops per head: two products), and any other
-requested workload are reported under "workloads" in the same line.  `roofline` is for the FP16 kernel; `traffic`
+4096 keys x head dim 128 (4*M*N*D flops per head: two products), FP16 2048^3
+(a grid the 256-wide tiles cannot fill, served by the 128 x 128 kernel), and any
+other requested workload are reported under "workloads" in the same line.  `roofline` is for the FP16 kernel; `traffic`
 comes from a stored rocprofv3 counter summary and is null when the kernel
 source changed after the counters were taken.  `cpu_baseline` times the CPU
 oracle on a bounded column sample of the same workload.
@@ -39,21 +40,19 @@ PEAK_TFLOPS = {"f16": 2516.6, "qkt": 2516.6, "attn": 2516.6, "f8": 5033.2}
 HBM_PEAK_GBS = 8000.0
 
 
-def kernel_name(w, cus):
-    """The kernel the library launches for workload w (its tile-width choice:
-    256 columns, or 224 when that packs the grid into fewer rounds of one
-    block per CU)."""
+def kernel_name(w):
+    """The kernel the library launches for workload w (its configuration
+    selector, queried through the C ABI)."""
+    import dense_gemm_tn_amd as dg
+
     if w.kind == "attn":
         return "attention_fwd_kernel"
-    es = 1 if w.kind == "f8" else 2
-    if w.K * es <= 256:
-        return "gemm_tn_skinny_kernel<%d>" % (1 if w.kind == "f8" else 0)
+    kind = 1 if w.kind == "f8" else 0
+    cfg = dg.tn_config(w.M, w.N, w.K, w.batch, fp8=(w.kind == "f8"))
+    return {0: "gemm_tn_kernel<%d, 8>" % kind, 1: "gemm_tn_kernel<%d, 7>" % kind,
+            2: "gemm_tn_mid_kernel<%d>" % kind, 3: "gemm_tn_skinny_kernel<%d>" % kind}[cfg]
 
-    def cost(ntn):
-        blocks = -(-w.M // 256) * -(-w.N // (32 * ntn)) * w.batch
-        return -(-blocks // cus) * ntn
 
-    return "gemm_tn_kernel<%d, %d>" % (1 if w.kind == "f8" else 0, 7 if cost(7) < cost(8) else 8)
 CSRC = os.path.join(ROOT, "dense_gemm_tn_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 
@@ -233,8 +232,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", action="append", default=None,
-                    help="workload names (default: f16_4096, f8_8192 and "
-                         "attn_64x4096x4096x128)")
+                    help="workload names (default: f16_4096, f8_8192, "
+                         "attn_64x4096x4096x128 and f16_2048)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (a known-size kernel for "
@@ -263,7 +262,7 @@ def main():
     from dense_gemm_tn_amd import inputs
 
     dev = torch.device("cuda:0")
-    names = args.workload or ["f16_4096", "f8_8192", "attn_64x4096x4096x128"]
+    names = args.workload or ["f16_4096", "f8_8192", "attn_64x4096x4096x128", "f16_2048"]
     head = "f16_4096" if "f16_4096" in names else names[0]
     results = {}
     keep = {}
@@ -278,7 +277,7 @@ def main():
             "peak": HBM_PEAK_GBS if w.kind == "qkt" else PEAK_TFLOPS[w.kind],
             "unit": "GB/s" if w.kind == "qkt" else "TFLOP/s",
             "traffic": tb,
-            "kernel": kernel_name(w, torch.cuda.get_device_properties(dev).multi_processor_count),
+            "kernel": kernel_name(w),
         }
         r = res["roofline"]
         r["frac"] = r["achieved"] / r["peak"]

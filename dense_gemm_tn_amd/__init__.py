@@ -31,6 +31,7 @@ EXPORTS = (
     "gemm_status_string",
     "gemm_tile_order",
     "gemm_block_tile",
+    "gemm_tn_config",
 )
 
 _lib = None
@@ -60,8 +61,9 @@ def lib() -> ctypes.CDLL:
         L.gemm_status_string.restype = ctypes.c_char_p
         L.gemm_tile_order.argtypes = [i64, i64, i64, vp]
         L.gemm_block_tile.argtypes = []
+        L.gemm_tn_config.argtypes = [ctypes.c_int, i64, i64, i64, i64]
         for f in (L.gemm_f16_tn, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
-                  L.gemm_tile_order, L.gemm_block_tile):
+                  L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -139,6 +141,14 @@ def tile_order(tiles_m: int, tiles_n: int, batch: int = 1):
 
 def block_tile() -> int:
     return lib().gemm_block_tile()
+
+
+CONFIG_NAMES = {0: "256x256", 1: "256x224", 2: "128x128", 3: "skinny-K"}
+
+
+def tn_config(M: int, N: int, K: int, batch: int = 1, fp8: bool = False) -> int:
+    """Kernel configuration code the GEMM entry points choose (see gemm_tn_config)."""
+    return lib().gemm_tn_config(1 if fp8 else 0, M, N, K, batch)
 
 
 # ----------------------------------------------------------- tensor helpers

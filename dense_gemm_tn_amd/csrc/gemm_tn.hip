@@ -47,6 +47,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <atomic>
 
@@ -886,6 +887,194 @@ struct Problem {
   float scale;
 };
 
+// ---------------------------------------------------------------------------
+// gemm_tn_mid_kernel<KIND>: 128 x 128 output tiles with two blocks per CU, for
+// grids the 256-wide tiles cannot fill (one tile configuration is wrong for
+// small or skinny products, so a set of configurations with a selector is
+// needed: "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", sections "Final
+// results" and "Further tuning").
+//   * 4 waves of 64 x 64 (4 x 4 MFMA tiles of 16 x 16, accumulators in VGPRs
+//     and the products left to the compiler: the two co-resident blocks
+//     interleave their waves on each SIMD, which hides what one wave waits on).
+//   * K-steps of 128 bytes per row in two LDS stages of [A strip | B strip]
+//     (128 rows x 128 B each, same XOR swizzle and fragment map as the
+//     256 x 256 kernel), one barrier per K-step; the next step's copies are
+//     issued right after it, so they have a whole step to land.
+//   * Direct column-major stores of runs of four rows (8 bytes), masked past
+//     M and N.
+constexpr int kMidTile = 128;
+constexpr int kMidStrip = kMidTile * kRowBytes;  // 16 KiB per operand per stage
+// Relative cost per output element of the 128 x 128 kernel, in 64ths of the
+// 256-row kernel's (measured; see the host selector in launch<>).
+constexpr int kMidCost = 83;
+
+__device__ __forceinline__ float4_t_v mma_c(const half8_t &a, const half8_t &b,
+                                            const float4_t_v &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t_v mma_c(const int8_t_v &a, const int8_t_v &b,
+                                            const float4_t_v &c) {
+  // v_mfma_f32_16x16x128_f8f6f4, FP8 E4M3 operands, no block scales.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
+  typedef Traits<KIND> T;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * kMidStrip];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int head, tm, tn;
+  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * kMidTile, n0 = (int64_t)tn * kMidTile;
+  const uint8_t *Ab = p.A + head * p.stride_a_b + m0 * p.lda_b;
+  const uint8_t *Bb = p.B + head * p.stride_b_b + n0 * p.ldb_b;
+  uint8_t *Cb = p.C + head * p.stride_c_b;
+  const int64_t rows_a = (p.M - m0) < kMidTile ? (p.M - m0) : kMidTile;
+  const int64_t rows_b = (p.N - n0) < kMidTile ? (p.N - n0) : kMidTile;
+  const uint32_t kbytes = (uint32_t)(p.K * T::es);
+  const uint32_t rec_a = (uint32_t)((rows_a - 1) * p.lda_b) + kbytes;
+  const uint32_t rec_b = (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes;
+
+  // Copies: load q (0..3) of wave w fills strip rows 32q + 8w .. +7 (1 KiB);
+  // lane l lands in row 32q + 8w + (l >> 3), slot l & 7, and fetches the
+  // global chunk the swizzle keeps there.  Rows past the matrix and chunks at
+  // or past K read zero.
+  const int crow = 8 * wave + (lane >> 3);
+  const int gchunk = (lane & 7) ^ ((crow >> 1) & 7);
+  const uint32_t voff_a = (uint32_t)(crow * p.lda_b) + gchunk * 16;
+  const uint32_t voff_b = (uint32_t)(crow * p.ldb_b) + gchunk * 16;
+  const uint32_t qs_a = (uint32_t)(32 * p.lda_b), qs_b = (uint32_t)(32 * p.ldb_b);
+  const int kchunk = gchunk * (16 / T::es);
+  const int64_t nk = (p.K + T::kstep - 1) / T::kstep;
+  auto copy_step = [&](int64_t t) {
+    const int64_t k0 = t * T::kstep;
+    const int64_t rem = p.K - k0;
+    const int left = rem >= T::kstep ? T::kstep : (int)rem;
+    const uint32_t kb = (uint32_t)(k0 * T::es);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + kb, rec_a - kb);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, rec_b - kb);
+    const bool valid = kchunk < left;
+    const uint32_t va = valid ? voff_a : kOob, vb = valid ? voff_b : kOob;
+    __attribute__((address_space(3))) uint8_t *st =
+        (__attribute__((address_space(3))) uint8_t *)smem + (t & 1) * 2 * kMidStrip + wave * 1024;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(st + q * 4096), 16,
+                                               va + q * qs_a, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + kMidStrip + q * 4096), 16,
+                                               vb + q * qs_b, 0, 0, 0);
+  };
+
+  // Fragments: lane l reads row l % 16 of a 16-row tile; fp16 takes chunk
+  // 4s + g of sub-step s, fp8 chunks g and g + 4 (g = l / 16), as in the
+  // 256 x 256 kernel.
+  const int wm = wave & 1, wn = wave >> 1;
+  const int rl = lane & 15, grp = lane >> 4;
+  uint32_t a_off[4] = {0, 0, 0, 0}, b_off[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int x = 0; x < T::subs * T::reads; ++x) {
+    const int chunk = (x / T::reads) * (8 / T::subs) + grp + 4 * (x % T::reads);
+    const uint32_t lo = (uint32_t)(rl * kRowBytes + ((chunk ^ ((rl >> 1) & 7)) * 16));
+    a_off[x] = lo + wm * 64 * kRowBytes;
+    b_off[x] = lo + kMidStrip + wn * 64 * kRowBytes;
+  }
+
+  float4_t_v acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = float4_t_v{0.f, 0.f, 0.f, 0.f};
+
+  copy_step(0);
+  for (int64_t t = 0; t < nk; ++t) {
+    // This wave's copies of step t have landed; after the barrier every
+    // wave's have, and every wave is done reading the other stage.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    if (t + 1 < nk) copy_step(t + 1);
+    lds_cptr st = (lds_cptr)smem + (t & 1) * 2 * kMidStrip;
+#pragma unroll
+    for (int s = 0; s < T::subs; ++s) {
+      typename T::frag_t fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = read_frag<KIND>(st + i * 16 * kRowBytes, a_off, s);
+        fb[i] = read_frag<KIND>(st + i * 16 * kRowBytes, b_off, s);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mma_c(fa[i], fb[j], acc[i][j]);
+    }
+  }
+
+  // Lane (rl, grp) of tile (i, j) holds C rows 16i + 4 grp .. +3 of column
+  // 16j + rl of the wave's 64 x 64 block.
+  const int64_t mb = m0 + wm * 64 + 4 * grp, nb = n0 + wn * 64 + rl;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t n = nb + 16 * j;
+    if (n >= p.N) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = mb + 16 * i;
+      uint32_t w0, w1;
+      pack_run<KIND>(p, acc[i][j], 0, w0, w1);
+      uint16_t *dst = (uint16_t *)Cb + (n * p.ldc + m);
+      if (p.c_vec_ok && m + 3 < p.M) {
+        *(uint2 *)dst = uint2{w0, w1};
+      } else {
+        const uint16_t h[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1,
+                               (uint16_t)(w1 >> 16)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (m + e < p.M) dst[e] = h[e];
+      }
+    }
+  }
+}
+
+// Kernel configuration of a problem (the codes are the C ABI's
+// gemm_tn_config values).
+enum { kCfg256 = 0, kCfg224 = 1, kCfgMid = 2, kCfgSkinny = 3 };
+struct Config {
+  int kind;
+};
+// Skinny contractions (all of K fits one 256-byte LDS row) take the skinny-K
+// kernel.  Otherwise the 256-row pipeline takes 256- or 224-column tiles
+// (NTN = 8 or 7 MFMA tiles per wave): with one block per CU its time is about
+// (rounds of CU-count blocks) x (tile width), so the narrower tile wins when
+// it packs the grid into enough fewer rounds (1920 x 13900: 440 wide tiles are
+// two rounds of 256 CUs, 504 narrow ones also two, each 7/8 as long).  Grids
+// that leave CUs idle that way take the 128 x 128 kernel instead: modelled
+// time = (blocks per CU, rounded up) x tile area, the small tile's area
+// weighted by kMidCost / 64.  DG_GEMM_TILE = 256, 224 or 128 in the
+// environment forces the tile of a non-skinny problem (measurement and tests).
+static Config choose_config(int es, int64_t M, int64_t N, int64_t K, int64_t batch) {
+  if (K * es <= kSkRow) return Config{kCfgSkinny};
+  if (const char *force = getenv("DG_GEMM_TILE")) {
+    if (!strcmp(force, "256")) return Config{kCfg256};
+    if (!strcmp(force, "224")) return Config{kCfg224};
+    if (!strcmp(force, "128")) return Config{kCfgMid};
+  }
+  const int64_t cus = cu_count();
+  const int64_t tm = (M + kTile - 1) / kTile;
+  auto cost = [&](int64_t w) {
+    const int64_t blocks = tm * ((N + 32 * w - 1) / (32 * w)) * batch;
+    return ((blocks + cus - 1) / cus) * w;
+  };
+  const int64_t ntn = cost(7) < cost(8) ? 7 : 8;
+  const int64_t mid_blocks = ((M + kMidTile - 1) / kMidTile) * ((N + kMidTile - 1) / kMidTile) * batch;
+  const int64_t t_big = cost(ntn) * kTile * 32 * 64;  // x 64: the scale of kMidCost
+  const int64_t t_mid = ((mid_blocks + cus - 1) / cus) * kMidTile * kMidTile * kMidCost;
+  if (t_mid < t_big) return Config{kCfgMid};
+  return Config{ntn == 7 ? kCfg224 : kCfg256};
+}
+
 template <int KIND>
 static int launch(const Problem &pr, hipStream_t stream) {
   typedef Traits<KIND> T;
@@ -921,25 +1110,11 @@ static int launch(const Problem &pr, hipStream_t stream) {
       reach_b >= (int64_t)kOob)
     return DG_ERR_UNSUPPORTED;
 
-  // Skinny contractions (all of K fits one 256-byte LDS row) take the 128 x 128
-  // tile kernel with two blocks per CU; everything else the 256 x 256 pipeline.
-  const bool skinny = pr.K * es <= kSkRow;
-  // The 256-row pipeline takes 256- or 224-column tiles (NTN = 8 or 7 MFMA
-  // tiles per wave): with one block per CU the time is about (rounds of CU
-  // count blocks) x (tile width), so take the narrower tile when it packs
-  // the grid into enough fewer rounds (1920 x 13900: 440 wide tiles are two
-  // rounds of 256 CUs, 504 narrow ones also two, each 7/8 as long).
-  int ntn = 8;
-  if (!skinny) {
-    const int64_t cus = cu_count();
-    const int64_t tm = (pr.M + kTile - 1) / kTile;
-    auto cost = [&](int64_t w) {
-      const int64_t blocks = tm * ((pr.N + 32 * w - 1) / (32 * w)) * pr.batch;
-      return ((blocks + cus - 1) / cus) * w;
-    };
-    if (cost(7) < cost(8)) ntn = 7;
-  }
-  const int64_t tile_m = skinny ? kSkTile : kTile, tile_n = skinny ? kSkTile : 32 * ntn;
+  const Config cfg = choose_config(es, pr.M, pr.N, pr.K, pr.batch);
+  const bool skinny = cfg.kind == kCfgSkinny, mid = cfg.kind == kCfgMid;
+  const int ntn = cfg.kind == kCfg224 ? 7 : 8;
+  const int64_t tile_m = skinny ? kSkTile : mid ? kMidTile : kTile;
+  const int64_t tile_n = skinny ? kSkTile : mid ? kMidTile : 32 * ntn;
   const int64_t tiles_m = (pr.M + tile_m - 1) / tile_m;
   const int64_t tiles_n = (pr.N + tile_n - 1) / tile_n;
   // Skinny-K blocks walk up to kSkWalkMax M tiles of one column (each walk
@@ -969,6 +1144,9 @@ static int launch(const Problem &pr, hipStream_t stream) {
 
   if (skinny)
     hipLaunchKernelGGL(gemm_tn_skinny_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, p);
+  else if (mid)
+    hipLaunchKernelGGL(gemm_tn_mid_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, p);
   else if (ntn == 8)
     hipLaunchKernelGGL((gemm_tn_kernel<KIND, 8>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
@@ -1027,5 +1205,10 @@ int gemm_tile_order(int64_t tiles_m, int64_t tiles_n, int64_t batch, int64_t *ou
 }
 
 int gemm_block_tile(void) { return dg::kTile; }
+
+int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch) {
+  if (M < 0 || N < 0 || K < 0 || batch < 0) return -1;
+  return dg::choose_config(fp8 ? 1 : 2, M, N, K, batch).kind;
+}
 
 }  // extern "C"

@@ -52,6 +52,7 @@ WORKLOADS = {
     for w in (
         Workload("f16_256_pm1", "f16", 256, 256, 256, "pm1", seed=0),
         Workload("f16_4096", "f16", 4096, 4096, 4096, "normal", seed=0),
+        Workload("f16_2048", "f16", 2048, 2048, 2048, "normal", seed=0),
         Workload("f16_1920x13900x4096", "f16", 1920, 13900, 4096, "normal", seed=0),
         Workload("f16_1920x13900x4096_pm1", "f16", 1920, 13900, 4096, "pm1", seed=1),
         Workload("f8_8192", "f8", 8192, 8192, 8192, "normal", seed=0),

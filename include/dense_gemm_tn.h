@@ -153,8 +153,25 @@ const char *gemm_status_string(int status);
  */
 int gemm_tile_order(int64_t tiles_m, int64_t tiles_n, int64_t batch, int64_t *out);
 
-/* Output tile edge (rows and columns of C per block) used by the kernels. */
+/* Output tile edge (rows of C per block) of the main, 256-row kernel. */
 int gemm_block_tile(void);
+
+/*
+ * The kernel configuration the GEMM entry points choose for a problem of the
+ * given sizes on the current HIP device (fp8 != 0: one-byte elements, else
+ * fp16).  One tile shape does not suit every size, so the library has a small
+ * set and a selector ("FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4",
+ * sections "Final results" and "Further tuning"):
+ *   0  256 x 256 output tiles, one block per CU, pipelined K loop;
+ *   1  256 x 224 tiles (fewer rounds of one block per CU for some widths);
+ *   2  128 x 128 tiles, two blocks per CU (grids the wide tiles leave idle);
+ *   3  the skinny-K kernel (K * element bytes <= 256);
+ *  -1  negative sizes.
+ * The choice is a pure function of the sizes and the device's CU count.  For
+ * measurement and tests, the environment variable DG_GEMM_TILE = 256, 224 or
+ * 128 forces configuration 0, 1 or 2 for every non-skinny problem.
+ */
+int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch);
 
 #ifdef __cplusplus
 }

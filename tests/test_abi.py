@@ -4,7 +4,9 @@
   * argument validation returns the documented status before any HIP call;
   * the block -> tile order is a bijection onto all (head, tile_m, tile_n) for
     every workload's grid and for ragged grids, and each XCD receives a
-    contiguous run of logical tiles.
+    contiguous run of logical tiles;
+  * the tile-configuration selector picks the documented kernel for each
+    workload shape (with the 256-CU count the library assumes without a device).
 """
 import ctypes
 import os
@@ -179,3 +181,39 @@ def test_tile_order_groups_per_xcd():
         rows = set(mine[:, 1])
         cols = set(mine[:, 2])
         assert len(mine) == 32 and len(rows) == 8 and len(cols) == 4
+
+
+@pytest.mark.parametrize("M,N,K,batch,fp8,want", [
+    (4096, 4096, 4096, 1, False, 0),      # one full round of 256 x 256 tiles
+    (8192, 8192, 8192, 1, True, 0),
+    (1920, 13900, 4096, 1, False, 1),     # 224-column tiles pack the grid
+    (2048, 2048, 2048, 1, False, 2),      # 64 wide tiles would leave 3/4 of the CUs idle
+    (256, 256, 256, 1, False, 2),
+    (1000, 700, 3976, 1, False, 2),
+    (4096, 4096, 128, 64, False, 3),      # QK^T: K row of 256 bytes
+    (1024, 1024, 256, 1, True, 3),        # fp8 K of 256 bytes
+    (-1, 4, 4, 1, False, -1),
+])
+def test_tile_config_selector(M, N, K, batch, fp8, want, monkeypatch):
+    monkeypatch.delenv("DG_GEMM_TILE", raising=False)
+    if torch_device_count() > 0:
+        pytest.skip("selector expectations assume the 256-CU default of a device-less host")
+    assert dg.tn_config(M, N, K, batch, fp8) == want
+
+
+def test_tile_config_override(monkeypatch):
+    for force, code in (("256", 0), ("224", 1), ("128", 2)):
+        monkeypatch.setenv("DG_GEMM_TILE", force)
+        assert dg.tn_config(2048, 2048, 2048) == code
+        assert dg.tn_config(4096, 4096, 128, 64) == 3   # skinny-K is never forced
+    monkeypatch.setenv("DG_GEMM_TILE", "64")            # unknown values are ignored
+    assert dg.tn_config(4096, 4096, 4096) in (0, 1, 2)
+
+
+def torch_device_count():
+    try:
+        import torch
+
+        return torch.cuda.device_count()
+    except Exception:
+        return 0

@@ -1,0 +1,91 @@
+"""GPU parity of every GEMM tile configuration, including the 128 x 128 kernel.
+
+The library picks a tile configuration per problem ("FP16 GEMM optimisation on
+AMD RDNA 3 and RDNA 4", sections "Final results" and "Further tuning": one tile
+shape is wrong for small or skinny products, so a set plus a selector is
+needed).  Here each of the three K-pipelined configurations (256 x 256,
+256 x 224, 128 x 128) is forced through DG_GEMM_TILE on the same ragged shapes
+(M, N and K tails, a single row or column, one K-step and many), with +-1
+inputs compared bit-exactly and canaries around C, plus padded leading
+dimensions and an odd ldc.  The selector's own choice for the small-grid shapes
+it sends to the 128 x 128 kernel is checked on the full 2048^3 problem.
+"""
+import numpy as np
+import pytest
+
+import dense_gemm_tn_amd as dg
+import oracle
+from dense_gemm_tn_amd import inputs
+from test_gpu_parity import assert_exact, normwise_error, reference, run_gemm, F16_TOL
+
+pytestmark = pytest.mark.gpu
+
+# K rows longer than 256 bytes (shorter ones always take the skinny-K kernel).
+SHAPES16 = [(1, 1, 136), (3, 5, 136), (31, 33, 264), (129, 131, 136), (257, 255, 520),
+            (300, 290, 200), (513, 260, 1000), (64, 700, 3976), (700, 64, 392)]
+SHAPES8 = [(1, 1, 272), (3, 5, 272), (31, 33, 528), (129, 131, 272), (257, 255, 1040),
+           (513, 260, 400), (300, 290, 3856)]
+FORCED = [("256", 0), ("224", 1), ("128", 2)]
+
+
+@pytest.fixture
+def force(monkeypatch):
+    def _set(value):
+        monkeypatch.setenv("DG_GEMM_TILE", value)
+    yield _set
+
+
+@pytest.mark.parametrize("tile,code", FORCED)
+@pytest.mark.parametrize("kind,M,N,K", [("f16",) + s for s in SHAPES16] +
+                         [("f8",) + s for s in SHAPES8])
+def test_forced_tile_exact(force, tile, code, kind, M, N, K):
+    force(tile)
+    assert dg.tn_config(M, N, K, fp8=(kind == "f8")) == code
+    print("forced tile %s %s %dx%dx%d" % (tile, kind, M, N, K), flush=True)
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=M * 7 + N + K)
+    got, canary = run_gemm(kind, x, M, N, K)
+    assert canary
+    assert_exact(kind, got, reference(kind, x, M, N, K))
+
+
+@pytest.mark.parametrize("tile,code", FORCED)
+@pytest.mark.parametrize("kind", ["f16", "f8"])
+def test_forced_tile_padding_and_odd_ldc(force, tile, code, kind):
+    force(tile)
+    M, N, K = 270, 300, 528
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=11)
+    vec = 8 if kind == "f16" else 16
+    got, canary = run_gemm(kind, x, M, N, K, lda=K + vec, ldb=K + 3 * vec, ldc=M + 1)
+    assert canary
+    assert_exact(kind, got, reference(kind, x, M, N, K))
+
+
+@pytest.mark.parametrize("tile", ["256", "128"])
+def test_forced_tile_normal_data(force, tile):
+    force(tile)
+    M, N, K = 520, 390, 1544
+    x = inputs.make_shape("f16", M, N, K, dist="normal", seed=5)
+    got, canary = run_gemm("f16", x, M, N, K)
+    assert canary
+    assert normwise_error("f16", got, reference("f16", x, M, N, K)) <= F16_TOL
+
+
+def test_selector_sends_2048_cube_to_128_tiles(monkeypatch):
+    """The selector's choice on this device for the small-grid workload, run in
+    full: +-1 data compared exactly everywhere, N(0,1) data on sampled entries."""
+    monkeypatch.delenv("DG_GEMM_TILE", raising=False)
+    w = inputs.WORKLOADS["f16_2048"]
+    assert dg.tn_config(w.M, w.N, w.K) == 2
+    print("selector 2048^3", flush=True)
+    x = inputs.make(w, dist="pm1")
+    got, canary = run_gemm("f16", x, w.M, w.N, w.K)
+    assert canary
+    assert_exact("f16", got, reference("f16", x, w.M, w.N, w.K))
+    x = inputs.make(w)
+    got, canary = run_gemm("f16", x, w.M, w.N, w.K)
+    rng = np.random.default_rng(3)
+    ms = rng.integers(0, w.M, 2000)
+    ns = rng.integers(0, w.N, 2000)
+    ref = oracle.gemm_tn_entries(x["A"], x["B"], oracle.FMT_F16, w.K, ms, ns)
+    g = oracle.decode(got[ns, ms], oracle.FMT_F16)
+    assert np.max(np.abs(g - ref)) / np.max(np.abs(ref)) <= F16_TOL
