@@ -100,7 +100,9 @@ def normwise_error(kind, got_codes, ref):
 # Edge shapes of section 11.4 (1x1x1, 3x5x7, 15x17x19, 17x19x23, 31x33x29) with K
 # rounded up to the 16-byte vector, plus multi-tile ragged shapes and K tails.
 # K rows of at most 256 bytes take the skinny-K kernel (fp16 K <= 128, fp8
-# K <= 256), longer ones the pipelined 256 x 256 kernel; both are covered.
+# K <= 256); longer ones, on grids this small, the 128 x 128 kernel (the
+# library's selector).  The 256-row kernels get ragged shapes of their own in
+# test_gpu_tiles.py (forced configuration) and below (large grids).
 EDGE = [(1, 1, 8), (3, 5, 8), (15, 17, 24), (17, 19, 24), (31, 33, 32)]
 EDGE8 = [(1, 1, 16), (3, 5, 16), (15, 17, 32), (17, 19, 32), (31, 33, 32)]
 RAGGED = [(256, 256, 256), (300, 290, 200), (257, 255, 72), (513, 260, 136), (64, 700, 64),
@@ -246,22 +248,14 @@ def test_batched_qkt_walks(H, M, N, D, pad):
     torch.cuda.empty_cache()
 
 
-def tile_width(M, N, batch=1, cus=256):
-    """The 256-row kernel's tile width the host picks: 256 columns, or 224
-    when that packs the grid into enough fewer rounds of one block per CU."""
-    def cost(w):
-        blocks = -(-M // 256) * -(-N // (32 * w)) * batch
-        return -(-blocks // cus) * w
-    return 224 if cost(7) < cost(8) else 256
-
-
 @pytest.mark.parametrize("kind,M,N,K", [("f16", 4024, 3996, 3976), ("f8", 4024, 3996, 3856),
                                         ("f16", 1000, 700, 3976)])
 def test_ragged_large_tiles(kind, M, N, K):
-    """Grids large enough for 256-column tiles (the small ragged cases get 224),
+    """Grids large enough for 256-row tiles (the small ragged case takes the
+    128 x 128 kernel),
     with M, N and K tails and an odd K-step count; +-1 data, sampled entries
     exact, the whole tail row and column exact, canaries intact."""
-    assert tile_width(M, N) == (256 if M > 1000 else 224)
+    assert dg.tn_config(M, N, K, fp8=(kind == "f8")) == (0 if M > 1000 else 2)
     x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=M + N + K)
     got, canary = run_gemm(kind, x, M, N, K)
     assert canary
