@@ -14,6 +14,10 @@ Definitions followed (page, section):
     A row-major M x K, B column-major (K contiguous per column), C column-major.
   * FP8 inputs carry per-tensor scales; the oracle applies scale_a * scale_b to
     the exact binary64 sum.
+  * Other layouts (``gemm``, ``gemm_strided``): the same sum with A(m, k), B(k, n)
+    and C(m, n) at arbitrary element strides -- the row-major storage and index
+    table of section 11.1 of the hello-gpu chapter, and the BLAS-style 'T' / 'N'
+    operand codes against a column-major C.
   * Attention (``attention_rows``): the hello-gpu chapter summary names joining the
     product with softmax as the next step, and the mlqm.cn TileLang attention page
     motivates fusing softmax with QK^T.  No page gives the formula, so the oracle is
@@ -73,8 +77,13 @@ def _load():
                                                ctypes.c_double, vp]
         lib.oracle_attention_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp, i64,
                                               ctypes.c_double, vp, ctypes.c_int]
+        lib.oracle_gemm_strided.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64, vp, i64,
+                                            i64, i64, i64, i64, ctypes.c_double, ctypes.c_int]
+        lib.oracle_gemm_strided_entries.argtypes = [ctypes.c_int, vp, i64, i64, vp, i64, i64,
+                                                    i64, vp, vp, i64, ctypes.c_double, vp]
         for f in (lib.oracle_decode, lib.oracle_encode, lib.oracle_gemm_tn,
-                  lib.oracle_gemm_tn_entries, lib.oracle_attention_rows):
+                  lib.oracle_gemm_tn_entries, lib.oracle_attention_rows,
+                  lib.oracle_gemm_strided, lib.oracle_gemm_strided_entries):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -161,6 +170,80 @@ def gemm_tn_entries(A: np.ndarray, B: np.ndarray, fmt: int, K: int, ms, ns,
                                         _ptr(ns), ms.size, float(scale), _ptr(out))
     if rc:
         raise RuntimeError("oracle_gemm_tn_entries failed with %d" % rc)
+    return out
+
+
+def gemm_strided(A: np.ndarray, sam: int, sak: int, B: np.ndarray, sbk: int, sbn: int,
+                 fmt: int, M: int, N: int, K: int, scm: int, scn: int, c_size: int,
+                 scale: float = 1.0, nthreads: int | None = None) -> np.ndarray:
+    """binary64 C(m, n) = scale * sum_k A[m*sam + k*sak] * B[k*sbk + n*sbn], stored at
+    C[m*scm + n*scn] of a flat array of c_size elements (other elements stay 0)."""
+    ra = _raw(A, fmt).reshape(-1)
+    rb = _raw(B, fmt).reshape(-1)
+    if M and K and ra.size <= (M - 1) * sam + (K - 1) * sak:
+        raise ValueError("A is too small for its strides")
+    if N and K and rb.size <= (K - 1) * sbk + (N - 1) * sbn:
+        raise ValueError("B is too small for its strides")
+    if M and N and c_size <= (M - 1) * scm + (N - 1) * scn:
+        raise ValueError("C is too small for its strides")
+    C = np.zeros(c_size, dtype=np.float64)
+    if nthreads is None:
+        nthreads = len(os.sched_getaffinity(0))
+    rc = _load().oracle_gemm_strided(fmt, _ptr(ra), sam, sak, _ptr(rb), sbk, sbn, _ptr(C), scm,
+                                     scn, M, N, K, float(scale), int(nthreads))
+    if rc:
+        raise RuntimeError("oracle_gemm_strided failed with %d" % rc)
+    return C
+
+
+def _op_strides(trans_a: str, trans_b: str, lda: int, ldb: int):
+    """Element strides of A(m, k) and B(k, n) for the BLAS-style op codes of a
+    column-major C: trans_a 'T' = A[m*lda + k] (K contiguous), 'N' = A[m + k*lda];
+    trans_b 'N' = B[k + n*ldb] (K contiguous), 'T' = B[k*ldb + n]."""
+    if trans_a not in ("T", "N") or trans_b not in ("T", "N"):
+        raise ValueError("trans codes are 'T' or 'N'")
+    sam, sak = (lda, 1) if trans_a == "T" else (1, lda)
+    sbk, sbn = (1, ldb) if trans_b == "N" else (ldb, 1)
+    return sam, sak, sbk, sbn
+
+
+def gemm(A: np.ndarray, B: np.ndarray, fmt: int, M: int, N: int, K: int,
+         trans_a: str = "T", trans_b: str = "N", lda: int | None = None,
+         ldb: int | None = None, scale: float = 1.0, nthreads: int | None = None) -> np.ndarray:
+    """binary64 C = op(A) op(B) for any of the four layouts, returned as [N, M] (row n is
+    column n of the column-major C).  Default leading dimensions are the packed ones."""
+    if lda is None:
+        lda = K if trans_a == "T" else M
+    if ldb is None:
+        ldb = K if trans_b == "N" else N
+    sam, sak, sbk, sbn = _op_strides(trans_a, trans_b, lda, ldb)
+    return gemm_strided(A, sam, sak, B, sbk, sbn, fmt, M, N, K, 1, M, M * N, scale,
+                        nthreads).reshape(N, M)
+
+
+def gemm_entries(A: np.ndarray, B: np.ndarray, fmt: int, K: int, ms, ns, M: int, N: int,
+                 trans_a: str = "T", trans_b: str = "N", lda: int | None = None,
+                 ldb: int | None = None, scale: float = 1.0) -> np.ndarray:
+    """binary64 entries C[ms[i], ns[i]] of gemm(...), one by one."""
+    if lda is None:
+        lda = K if trans_a == "T" else M
+    if ldb is None:
+        ldb = K if trans_b == "N" else N
+    sam, sak, sbk, sbn = _op_strides(trans_a, trans_b, lda, ldb)
+    ra = _raw(A, fmt).reshape(-1)
+    rb = _raw(B, fmt).reshape(-1)
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    if ms.shape != ns.shape:
+        raise ValueError("ms and ns differ in shape")
+    if ms.size and (ms.min() < 0 or ns.min() < 0 or ms.max() >= M or ns.max() >= N):
+        raise ValueError("entry index out of range")
+    out = np.empty(ms.shape, dtype=np.float64)
+    rc = _load().oracle_gemm_strided_entries(fmt, _ptr(ra), sam, sak, _ptr(rb), sbk, sbn, K,
+                                             _ptr(ms), _ptr(ns), ms.size, float(scale),
+                                             _ptr(out))
+    if rc:
+        raise RuntimeError("oracle_gemm_strided_entries failed with %d" % rc)
     return out
 
 

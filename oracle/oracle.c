@@ -227,24 +227,32 @@ static void *gemm_worker(void *arg) {
 }
 
 /*
- * C[m + n*ldc] = scale * sum_k A[m*lda + k] * B[n*ldb + k]  (binary64)
- * fmt selects the element format of A and B.  Returns 0 on success.
+ * General strides (element units, all >= 0):
+ *   C(m, n) = scale * sum_k A(m, k) * B(k, n)                      (binary64)
+ *   A(m, k) = A[m*sam + k*sak],  B(k, n) = B[k*sbk + n*sbn],
+ *   C(m, n) is stored at C[m*scm + n*scn].
+ * The row-major storage of section 11.1 of the hello-gpu chapter (A[m*K + k],
+ * B[k*N + n], C[m*N + n]) and the TN layout below are special cases.  fmt
+ * selects the element format of A and B.  Returns 0 on success.
  */
-int oracle_gemm_tn(int fmt, const void *A, const void *B, double *C,
-                   int64_t M, int64_t N, int64_t K,
-                   int64_t lda, int64_t ldb, int64_t ldc,
-                   double scale, int nthreads) {
-  if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldc < M) return 1;
+int oracle_gemm_strided(int fmt, const void *A, int64_t sam, int64_t sak,
+                        const void *B, int64_t sbk, int64_t sbn,
+                        double *C, int64_t scm, int64_t scn,
+                        int64_t M, int64_t N, int64_t K, double scale, int nthreads) {
+  if (M < 0 || N < 0 || K < 0 || sam < 0 || sak < 0 || sbk < 0 || sbn < 0 || scm < 0 ||
+      scn < 0)
+    return 1;
   if (fmt != ORACLE_FMT_F16 && fmt != ORACLE_FMT_BF16 && fmt != ORACLE_FMT_E4M3FN)
     return 1;
   if (M == 0 || N == 0) return 0;
   double *a = (double *)malloc(sizeof(double) * (size_t)(M * K > 0 ? M * K : 1));
   double *b = (double *)malloc(sizeof(double) * (size_t)(N * K > 0 ? N * K : 1));
-  if (!a || !b) { free(a); free(b); return 2; }
+  double *c = (double *)malloc(sizeof(double) * (size_t)(M * N));
+  if (!a || !b || !c) { free(a); free(b); free(c); return 2; }
   for (int64_t m = 0; m < M; ++m)
-    for (int64_t k = 0; k < K; ++k) a[m * K + k] = decode_one(fmt, A, m * lda + k);
+    for (int64_t k = 0; k < K; ++k) a[m * K + k] = decode_one(fmt, A, m * sam + k * sak);
   for (int64_t n = 0; n < N; ++n)
-    for (int64_t k = 0; k < K; ++k) b[n * K + k] = decode_one(fmt, B, n * ldb + k);
+    for (int64_t k = 0; k < K; ++k) b[n * K + k] = decode_one(fmt, B, k * sbk + n * sbn);
 
   if (nthreads < 1) nthreads = 1;
   if (nthreads > N) nthreads = (int)N;
@@ -254,8 +262,8 @@ int oracle_gemm_tn(int fmt, const void *A, const void *B, double *C,
   if (!tid || !jobs) rc = 2;
   int started = 0;
   for (int t = 0; rc == 0 && t < nthreads; ++t) {
-    jobs[t].a = a; jobs[t].b = b; jobs[t].c = C;
-    jobs[t].M = M; jobs[t].K = K; jobs[t].ldc = ldc; jobs[t].scale = scale;
+    jobs[t].a = a; jobs[t].b = b; jobs[t].c = c;
+    jobs[t].M = M; jobs[t].K = K; jobs[t].ldc = M; jobs[t].scale = scale;
     jobs[t].n_begin = N * t / nthreads;
     jobs[t].n_end = N * (t + 1) / nthreads;
     if (nthreads == 1) { gemm_worker(&jobs[t]); continue; }
@@ -263,8 +271,24 @@ int oracle_gemm_tn(int fmt, const void *A, const void *B, double *C,
     ++started;
   }
   for (int t = 0; t < started; ++t) pthread_join(tid[t], NULL);
-  free(jobs); free(tid); free(a); free(b);
+  if (rc == 0)
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t m = 0; m < M; ++m) C[m * scm + n * scn] = c[m + n * M];
+  free(jobs); free(tid); free(a); free(b); free(c);
   return rc;
+}
+
+/*
+ * C[m + n*ldc] = scale * sum_k A[m*lda + k] * B[n*ldb + k]  (binary64): the TN
+ * layout of "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", section "What
+ * we compute".  Returns 0 on success.
+ */
+int oracle_gemm_tn(int fmt, const void *A, const void *B, double *C,
+                   int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldb, int64_t ldc,
+                   double scale, int nthreads) {
+  if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldc < M) return 1;
+  return oracle_gemm_strided(fmt, A, lda, 1, B, 1, ldb, C, 1, ldc, M, N, K, scale, nthreads);
 }
 
 /*
@@ -282,6 +306,23 @@ int oracle_gemm_tn_entries(int fmt, const void *A, const void *B, int64_t K,
     double acc = 0.0;
     for (int64_t k = 0; k < K; ++k)
       acc += decode_one(fmt, A, ms[i] * lda + k) * decode_one(fmt, B, ns[i] * ldb + k);
+    out[i] = acc * scale;
+  }
+  return 0;
+}
+
+/* Individual entries with general strides (see oracle_gemm_strided). */
+int oracle_gemm_strided_entries(int fmt, const void *A, int64_t sam, int64_t sak,
+                                const void *B, int64_t sbk, int64_t sbn, int64_t K,
+                                const int64_t *ms, const int64_t *ns, int64_t count,
+                                double scale, double *out) {
+  if (K < 0 || sam < 0 || sak < 0 || sbk < 0 || sbn < 0) return 1;
+  if (fmt != ORACLE_FMT_F16 && fmt != ORACLE_FMT_BF16 && fmt != ORACLE_FMT_E4M3FN)
+    return 1;
+  for (int64_t i = 0; i < count; ++i) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+      acc += decode_one(fmt, A, ms[i] * sam + k * sak) * decode_one(fmt, B, k * sbk + ns[i] * sbn);
     out[i] = acc * scale;
   }
   return 0;

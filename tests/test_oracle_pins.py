@@ -246,3 +246,52 @@ def test_input_quantiser_matches_oracle_codec():
     np.testing.assert_array_equal(oracle.encode(y.astype(np.float64), oracle.FMT_E4M3FN), codes)
     assert np.max(np.abs(oracle.decode(codes, oracle.FMT_E4M3FN))) == 448.0
     assert s == np.float32(np.float32(np.max(np.abs(x))) / np.float32(448))
+
+
+# ------------------------------------------------------ other storage layouts
+
+def test_row_major_worked_example_and_index_table():
+    """Section 11.1 stores A, B and C row-major (A[m*K + k], B[k*N + n], C[m*N + n])
+    and states that C[1,1] reads A at 3, 4, 5 and B at 1, 3, 5 (B's row stride is N)."""
+    g = json.load(open(GOLDEN))
+    M, N, K = g["M"], g["N"], g["K"]
+    A = np.asarray(g["A_rows"], dtype=np.float16).reshape(-1)
+    B = np.asarray(g["B_rows"], dtype=np.float16).reshape(-1)
+    C = oracle.gemm_strided(A, K, 1, B, N, 1, oracle.FMT_F16, M, N, K, N, 1, M * N)
+    np.testing.assert_array_equal(C.reshape(M, N), np.asarray(g["C_rows"], dtype=np.float64))
+    # Only the elements the page names are nonzero: C[1,1] keeps its value, the rest is 0.
+    A2 = np.zeros_like(A)
+    A2[[3, 4, 5]] = A[[3, 4, 5]]
+    B2 = np.zeros_like(B)
+    B2[[1, 3, 5]] = B[[1, 3, 5]]
+    C2 = oracle.gemm_strided(A2, K, 1, B2, N, 1, oracle.FMT_F16, M, N, K, N, 1, M * N)
+    np.testing.assert_array_equal(C2.reshape(M, N), [[0.0, 0.0], [0.0, 17.0]])
+
+
+@pytest.mark.parametrize("trans_a", ["T", "N"])
+@pytest.mark.parametrize("trans_b", ["T", "N"])
+def test_four_layouts_against_integer_matmul(trans_a, trans_b):
+    """Each of the four op-code layouts, with padded leading dimensions whose
+    padding is poisoned, against numpy's exact integer matmul of +-1 data."""
+    rng = np.random.default_rng(17)
+    M, N, K = 23, 19, 37
+    a = rng.choice([-1, 1], size=(M, K)).astype(np.int64)
+    b = rng.choice([-1, 1], size=(K, N)).astype(np.int64)
+    want = a @ b                                     # [M, N]
+    pad = 5
+    # A storage: 'T' = rows of K (A[m*lda + k]), 'N' = rows of M (A[m + k*lda]).
+    sa = a if trans_a == "T" else a.T
+    Astore = np.full((sa.shape[0], sa.shape[1] + pad), 1000.0, np.float16)
+    Astore[:, :sa.shape[1]] = sa
+    # B storage: 'N' = rows of K per column n (B[k + n*ldb]), 'T' = rows of N (B[k*ldb + n]).
+    sb = b.T if trans_b == "N" else b
+    Bstore = np.full((sb.shape[0], sb.shape[1] + pad), -1000.0, np.float16)
+    Bstore[:, :sb.shape[1]] = sb
+    C = oracle.gemm(Astore, Bstore, oracle.FMT_F16, M, N, K, trans_a=trans_a, trans_b=trans_b,
+                    lda=Astore.shape[1], ldb=Bstore.shape[1])
+    np.testing.assert_array_equal(C.T, want.astype(np.float64))
+    ms = rng.integers(0, M, 40)
+    ns = rng.integers(0, N, 40)
+    e = oracle.gemm_entries(Astore, Bstore, oracle.FMT_F16, K, ms, ns, M, N, trans_a=trans_a,
+                            trans_b=trans_b, lda=Astore.shape[1], ldb=Bstore.shape[1])
+    np.testing.assert_array_equal(e, want[ms, ns].astype(np.float64))
