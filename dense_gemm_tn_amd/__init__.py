@@ -25,6 +25,7 @@ DG_ERR_HIP = 3
 
 EXPORTS = (
     "gemm_f16_tn",
+    "gemm_f16",
     "gemm_f8_tn",
     "gemm_batched_qkt",
     "attention_fwd_f16",
@@ -53,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         i64, vp, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
         L.gemm_f16_tn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, vp]
+        L.gemm_f16.argtypes = [ctypes.c_char, ctypes.c_char, vp, vp, vp, i64, i64, i64, i64, i64,
+                               i64, vp]
         L.gemm_f8_tn.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, f32, f32, vp]
         L.gemm_batched_qkt.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                        i64, vp]
@@ -62,7 +65,7 @@ def lib() -> ctypes.CDLL:
         L.gemm_tile_order.argtypes = [i64, i64, i64, vp]
         L.gemm_block_tile.argtypes = []
         L.gemm_tn_config.argtypes = [ctypes.c_int, i64, i64, i64, i64]
-        for f in (L.gemm_f16_tn, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
+        for f in (L.gemm_f16_tn, L.gemm_f16, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
                   L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config):
             f.restype = ctypes.c_int
         _lib = L
@@ -102,6 +105,16 @@ def gemm_f16_tn(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
     """C[m + n*ldc] = sum_k A[m*lda + k] * B[n*ldb + k]   (fp16 in/out, fp32 accumulate)."""
     _check("gemm_f16_tn", lib().gemm_f16_tn(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                                             _stream(stream)))
+
+
+def gemm_f16(transa: str, transb: str, A, B, C, M: int, N: int, K: int, lda: int, ldb: int,
+             ldc: int, stream=None) -> None:
+    """C[m + n*ldc] = sum_k op(A)(m, k) op(B)(k, n) for BLAS op codes 'T' / 'N':
+    A 'T' = A[m*lda + k], 'N' = A[m + k*lda]; B 'N' = B[k + n*ldb], 'T' = B[k*ldb + n]."""
+    if transa not in "TtNn" or transb not in "TtNn" or len(transa) != 1 or len(transb) != 1:
+        raise ValueError("op codes are 'T' or 'N'")
+    _check("gemm_f16", lib().gemm_f16(transa.encode(), transb.encode(), _ptr(A), _ptr(B), _ptr(C),
+                                      M, N, K, lda, ldb, ldc, _stream(stream)))
 
 
 def gemm_f8_tn(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
@@ -164,6 +177,24 @@ def matmul_tn_f16(a, b, out=None, stream=None):
     if out is None:
         out = torch.empty((N, M), dtype=torch.float16, device=a.device)
     gemm_f16_tn(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), stream)
+    return out
+
+
+def matmul_f16(a, b, transa: str = "T", transb: str = "N", out=None, stream=None):
+    """fp16 C = op(A) op(B) as [N, M] (column-major C) from operands as they lie in memory:
+    a is [M, K] for transa 'T' and [K, M] for 'N'; b is [N, K] for transb 'N' and
+    [K, N] for 'T' (each with a contiguous last dimension)."""
+    import torch
+
+    if a.dtype != torch.float16 or b.dtype != torch.float16 or a.dim() != 2 or b.dim() != 2:
+        raise ValueError("matmul_f16 expects 2-D fp16 tensors")
+    M, K = a.shape if transa in "Tt" else a.shape[::-1]
+    N, Kb = b.shape if transb in "Nn" else b.shape[::-1]
+    if K != Kb or a.stride(1) != 1 or b.stride(1) != 1:
+        raise ValueError("matmul_f16: K differs or a last dimension is strided")
+    if out is None:
+        out = torch.empty((N, M), dtype=torch.float16, device=a.device)
+    gemm_f16(transa, transb, a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), stream)
     return out
 
 

@@ -918,9 +918,64 @@ __device__ __forceinline__ float4_t_v mma_c(const int8_t_v &a, const int8_t_v &b
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-template <int KIND>
+// An operand of the 128 x 128 kernel in LDS.  K-major operands (K
+// contiguous: A of a 'T' op, B of an 'N' op) use the 128 x 128-byte strip of
+// the 256-row kernel.  M/N-major fp16 operands (A of an 'N' op: A[m + k*lda];
+// B of a 'T' op: B[k*ldb + n]) keep their own layout: 64 K-rows of 128
+// elements (256 B), the 16-byte chunk c of K-row k stored in slot
+// c ^ (2 (k & 3) + 8 ((k >> 3) & 1)), and fragments come from gfx950's
+// transposing LDS read: within each 16-lane group, ds_read_b64_tr_b16 gives
+// lane 4a + b element b of the 8 bytes addressed by lane 4e + a as its value e
+// (measured), so lanes 4e + a pointing at K-row k0 + e, elements 4a .. 4a + 3
+// of a 16-wide tile leave lane j holding K-rows k0 .. k0 + 3 of column j --
+// the MFMA operand layout.  The swizzle spreads the sixteen K-rows one such
+// read touches (two 16-lane groups per LDS pass) over distinct slots.
+template <bool MN>
+struct MidOperand {
+  uint32_t off[4];     // copy offsets of loads q = 0..3 (lane constant)
+  int krow[4];         // M/N-major: K-row of load q; K-major: unused
+  bool cvalid[4];      // M/N-major: the load's chunk lies inside M (or N)
+  uint32_t frag[4];    // fragment read offsets (see read)
+};
+
+__device__ __forceinline__ int mn_swz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+
+// Copies of one operand of the 128 x 128 kernel for K-step t into this
+// wave's KiB `st` of each 4 KiB quarter of the operand's LDS strip.
+template <int KIND, bool MN>
+__device__ __forceinline__ void mid_copy(const uint8_t *base, int64_t ld_b, int64_t K,
+                                         uint32_t rec, uint32_t voff, uint32_t qs, int kchunk,
+                                         const MidOperand<MN> &op, int64_t t, lds_u8 *st) {
+  typedef Traits<KIND> T;
+  const int64_t k0 = t * T::kstep;
+  if constexpr (MN) {
+    // Rebased on the step's first K-row; rows at or past K and chunks past
+    // M / N read zero.  The descriptor covers the step's 64 K-rows.
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + k0 * ld_b, (uint32_t)(T::kstep * ld_b));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool ok = op.cvalid[q] && k0 + op.krow[q] < K;
+      const uint32_t off = ok ? op.off[q] : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(st + q * 4096), 16, off, 0, 0,
+                                               0);
+    }
+  } else {
+    const int64_t rem = K - k0;
+    const int left = rem >= T::kstep ? T::kstep : (int)rem;
+    const uint32_t kb = (uint32_t)(k0 * T::es);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + kb, rec - kb);
+    const uint32_t v = kchunk < left ? voff : kOob;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(st + q * 4096), 16,
+                                               v + q * qs, 0, 0, 0);
+  }
+}
+
+template <int KIND, bool AMN, bool BMN>
 __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   typedef Traits<KIND> T;
+  static_assert(KIND == kF16 || (!AMN && !BMN), "M/N-major operands are fp16 only");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * kMidStrip];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -928,50 +983,58 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   int head, tm, tn;
   tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
   const int64_t m0 = (int64_t)tm * kMidTile, n0 = (int64_t)tn * kMidTile;
-  const uint8_t *Ab = p.A + head * p.stride_a_b + m0 * p.lda_b;
-  const uint8_t *Bb = p.B + head * p.stride_b_b + n0 * p.ldb_b;
+  // Block bases: K-major operands at their first row, M/N-major ones at their
+  // first column (element m0 / n0 of K-row 0).
+  const uint8_t *Ab = p.A + head * p.stride_a_b + (AMN ? m0 * 2 : m0 * p.lda_b);
+  const uint8_t *Bb = p.B + head * p.stride_b_b + (BMN ? n0 * 2 : n0 * p.ldb_b);
   uint8_t *Cb = p.C + head * p.stride_c_b;
   const int64_t rows_a = (p.M - m0) < kMidTile ? (p.M - m0) : kMidTile;
   const int64_t rows_b = (p.N - n0) < kMidTile ? (p.N - n0) : kMidTile;
   const uint32_t kbytes = (uint32_t)(p.K * T::es);
-  const uint32_t rec_a = (uint32_t)((rows_a - 1) * p.lda_b) + kbytes;
-  const uint32_t rec_b = (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes;
 
-  // Copies: load q (0..3) of wave w fills strip rows 32q + 8w .. +7 (1 KiB);
-  // lane l lands in row 32q + 8w + (l >> 3), slot l & 7, and fetches the
-  // global chunk the swizzle keeps there.  Rows past the matrix and chunks at
-  // or past K read zero.
+  // K-major copies: load q (0..3) of wave w fills strip rows 32q + 8w .. +7;
+  // lane l lands in row 32q + 8w + (l >> 3), slot l & 7, and fetches the chunk
+  // the swizzle keeps there.  Rows past the matrix and chunks at or past K
+  // read zero.
   const int crow = 8 * wave + (lane >> 3);
   const int gchunk = (lane & 7) ^ ((crow >> 1) & 7);
+  const int kchunk = gchunk * (16 / T::es);
+  // M/N-major copies: load q fills K-rows 16q + 4w .. +3 (1 KiB); lane l
+  // lands in K-row 16q + 4w + (l >> 4), slot l & 15.
+  auto mn_operand = [&](int64_t ld_b, int64_t rows) {
+    MidOperand<true> o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = 16 * q + 4 * wave + (lane >> 4);
+      const int c = (lane & 15) ^ mn_swz(k);
+      o.krow[q] = k;
+      o.off[q] = (uint32_t)(k * ld_b) + c * 16;
+      o.cvalid[q] = 8 * c < rows;
+    }
+    return o;
+  };
+  MidOperand<AMN> opa;
+  MidOperand<BMN> opb;
+  if constexpr (AMN) opa = mn_operand(p.lda_b, rows_a);
+  if constexpr (BMN) opb = mn_operand(p.ldb_b, rows_b);
   const uint32_t voff_a = (uint32_t)(crow * p.lda_b) + gchunk * 16;
   const uint32_t voff_b = (uint32_t)(crow * p.ldb_b) + gchunk * 16;
   const uint32_t qs_a = (uint32_t)(32 * p.lda_b), qs_b = (uint32_t)(32 * p.ldb_b);
-  const int kchunk = gchunk * (16 / T::es);
+  const uint32_t rec_a = AMN ? 0u : (uint32_t)((rows_a - 1) * p.lda_b) + kbytes;
+  const uint32_t rec_b = BMN ? 0u : (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes;
   const int64_t nk = (p.K + T::kstep - 1) / T::kstep;
+
   auto copy_step = [&](int64_t t) {
-    const int64_t k0 = t * T::kstep;
-    const int64_t rem = p.K - k0;
-    const int left = rem >= T::kstep ? T::kstep : (int)rem;
-    const uint32_t kb = (uint32_t)(k0 * T::es);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + kb, rec_a - kb);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, rec_b - kb);
-    const bool valid = kchunk < left;
-    const uint32_t va = valid ? voff_a : kOob, vb = valid ? voff_b : kOob;
-    __attribute__((address_space(3))) uint8_t *st =
-        (__attribute__((address_space(3))) uint8_t *)smem + (t & 1) * 2 * kMidStrip + wave * 1024;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(st + q * 4096), 16,
-                                               va + q * qs_a, 0, 0, 0);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + kMidStrip + q * 4096), 16,
-                                               vb + q * qs_b, 0, 0, 0);
+    lds_u8 *st = (lds_u8 *)smem + (t & 1) * 2 * kMidStrip + wave * 1024;
+    mid_copy<KIND>(Ab, p.lda_b, p.K, rec_a, voff_a, qs_a, kchunk, opa, t, st);
+    mid_copy<KIND>(Bb, p.ldb_b, p.K, rec_b, voff_b, qs_b, kchunk, opb, t, st + kMidStrip);
   };
 
-  // Fragments: lane l reads row l % 16 of a 16-row tile; fp16 takes chunk
-  // 4s + g of sub-step s, fp8 chunks g and g + 4 (g = l / 16), as in the
-  // 256 x 256 kernel.
+  // Fragments.  K-major: lane l reads row l % 16 of a 16-row tile; fp16 takes
+  // chunk 4s + g of sub-step s, fp8 chunks g and g + 4 (g = l / 16), as in the
+  // 256 x 256 kernel.  M/N-major: two transposing reads per sub-step (K-rows
+  // 32s + 8g + 4h + (l % 16) / 4, h = 0, 1) at elements 4 ((l % 16) % 4) of
+  // the tile.
   const int wm = wave & 1, wn = wave >> 1;
   const int rl = lane & 15, grp = lane >> 4;
   uint32_t a_off[4] = {0, 0, 0, 0}, b_off[4] = {0, 0, 0, 0};
@@ -982,6 +1045,22 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
     a_off[x] = lo + wm * 64 * kRowBytes;
     b_off[x] = lo + kMidStrip + wn * 64 * kRowBytes;
   }
+  // M/N-major: lane constants of the read address (see the layout above):
+  // K-row 8g + (rl >> 2) (+ 32s + 4h), slot of the tile's first chunk
+  // (8 w + 2i) ^ swz with swz = 2 (rl >> 2) + 8 (g & 1), plus chunk half and
+  // 8-byte half from rl & 3.
+  const int mn_k = 8 * grp + (rl >> 2);
+  const int mn_swz_l = mn_swz(mn_k);
+  auto mn_frag = [&](lds_cptr strip, int w8, int i, int s) -> half8_t {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int slot = ((w8 + 2 * i) ^ mn_swz_l) + ((rl & 3) >> 1);
+    const uint32_t off = (uint32_t)((32 * s + mn_k) * 256 + slot * 16 + (rl & 1) * 8);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(strip + off));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16 *)(strip + off + 4 * 256));
+    return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
 
   float4_t_v acc[4][4];
 #pragma unroll
@@ -989,7 +1068,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = float4_t_v{0.f, 0.f, 0.f, 0.f};
 
-  copy_step(0);
+  if (nk > 0) copy_step(0);
   for (int64_t t = 0; t < nk; ++t) {
     // This wave's copies of step t have landed; after the barrier every
     // wave's have, and every wave is done reading the other stage.
@@ -1002,8 +1081,14 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
       typename T::frag_t fa[4], fb[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        fa[i] = read_frag<KIND>(st + i * 16 * kRowBytes, a_off, s);
-        fb[i] = read_frag<KIND>(st + i * 16 * kRowBytes, b_off, s);
+        if constexpr (AMN)
+          fa[i] = mn_frag(st, 8 * wm, i, s);
+        else
+          fa[i] = read_frag<KIND>(st + i * 16 * kRowBytes, a_off, s);
+        if constexpr (BMN)
+          fb[i] = mn_frag(st + kMidStrip, 8 * wn, i, s);
+        else
+          fb[i] = read_frag<KIND>(st + i * 16 * kRowBytes, b_off, s);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -1146,7 +1231,7 @@ static int launch(const Problem &pr, hipStream_t stream) {
     hipLaunchKernelGGL(gemm_tn_skinny_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, p);
   else if (mid)
-    hipLaunchKernelGGL(gemm_tn_mid_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0,
+    hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, p);
   else if (ntn == 8)
     hipLaunchKernelGGL((gemm_tn_kernel<KIND, 8>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
@@ -1155,9 +1240,81 @@ static int launch(const Problem &pr, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
+// fp16 products in any of the four op-code layouts.  TN goes through
+// launch<> and its configurations; the others take the 128 x 128 kernel with
+// each M- or N-contiguous operand (A of an 'N' op, B of a 'T' op) staged as it
+// lies in memory and turned in the fragment reads -- no transpose pass.
+static int launch_f16_layout(char ta, char tb, const Problem &pr, hipStream_t stream) {
+  const bool a_t = ta == 'T' || ta == 't', a_n = ta == 'N' || ta == 'n';
+  const bool b_t = tb == 'T' || tb == 't', b_n = tb == 'N' || tb == 'n';
+  if (!(a_t || a_n) || !(b_t || b_n)) return DG_ERR_INVALID_ARGUMENT;
+  if (a_t && b_n) return launch<kF16>(pr, stream);
+  const bool amn = a_n, bmn = b_t;
+  if (pr.M < 0 || pr.N < 0 || pr.K < 0) return DG_ERR_INVALID_ARGUMENT;
+  if (pr.lda < (amn ? pr.M : pr.K) || pr.ldb < (bmn ? pr.N : pr.K) || pr.ldc < pr.M)
+    return DG_ERR_INVALID_ARGUMENT;
+  if (pr.M == 0 || pr.N == 0) return DG_OK;
+  if (!pr.A || !pr.B || !pr.C) return DG_ERR_INVALID_ARGUMENT;
+  const uint64_t a_all = amn ? span_bytes(pr.K, pr.M, pr.lda, 2) : span_bytes(pr.M, pr.K, pr.lda, 2);
+  const uint64_t b_all = bmn ? span_bytes(pr.K, pr.N, pr.ldb, 2) : span_bytes(pr.N, pr.K, pr.ldb, 2);
+  const uint64_t c_all = span_bytes(pr.N, pr.M, pr.ldc, 2);
+  if (overlaps(pr.C, c_all, pr.A, a_all) || overlaps(pr.C, c_all, pr.B, b_all))
+    return DG_ERR_INVALID_ARGUMENT;
+
+  // 16-byte chunks along each operand's contiguous dimension; K only has to be
+  // a multiple of 8 when an operand is K-contiguous.
+  if (pr.lda % 8 || pr.ldb % 8) return DG_ERR_UNSUPPORTED;
+  if ((!amn || !bmn) && pr.K % 8) return DG_ERR_UNSUPPORTED;
+  if ((amn && pr.M % 8) || (bmn && pr.N % 8)) return DG_ERR_UNSUPPORTED;
+  if (!aligned16(pr.A) || !aligned16(pr.B) || !aligned16(pr.C)) return DG_ERR_UNSUPPORTED;
+  // Offsets inside one block's descriptors stay below kOob: 128 rows of a
+  // K-contiguous operand, 64 K-rows (one step) of an M/N-contiguous one.
+  auto reach = [&](bool mn, int64_t ld) {
+    return mn ? 64 * ld * 2 + 256 : kMidTile * ld * 2 + kRowBytes;
+  };
+  if (reach(amn, pr.lda) >= (int64_t)kOob || reach(bmn, pr.ldb) >= (int64_t)kOob)
+    return DG_ERR_UNSUPPORTED;
+  if (!amn && (int64_t)span_bytes(pr.M < kMidTile ? pr.M : kMidTile, pr.K, pr.lda, 2) >= (int64_t)kOob)
+    return DG_ERR_UNSUPPORTED;
+  if (!bmn && (int64_t)span_bytes(pr.N < kMidTile ? pr.N : kMidTile, pr.K, pr.ldb, 2) >= (int64_t)kOob)
+    return DG_ERR_UNSUPPORTED;
+
+  const int64_t tiles_m = (pr.M + kMidTile - 1) / kMidTile;
+  const int64_t tiles_n = (pr.N + kMidTile - 1) / kMidTile;
+  const int64_t blocks = tiles_m * tiles_n;
+  if (blocks > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;
+
+  Params p;
+  p.A = (const uint8_t *)pr.A;
+  p.B = (const uint8_t *)pr.B;
+  p.C = (uint8_t *)pr.C;
+  p.M = pr.M; p.N = pr.N; p.K = pr.K;
+  p.lda_b = pr.lda * 2; p.ldb_b = pr.ldb * 2; p.ldc = pr.ldc;
+  p.stride_a_b = 0; p.stride_b_b = 0; p.stride_c_b = 0;
+  p.tiles_m = (int32_t)tiles_m; p.tiles_n = (int32_t)tiles_n;
+  p.scale = 1.0f;
+  p.c_vec_ok = (pr.ldc % 4 == 0) ? 1 : 0;
+  p.c_vec16_ok = (pr.ldc % 8 == 0) ? 1 : 0;
+  p.sk_walk = 1;
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (amn && bmn)
+    hipLaunchKernelGGL((gemm_tn_mid_kernel<kF16, true, true>), grid, block, 0, stream, p);
+  else if (amn)
+    hipLaunchKernelGGL((gemm_tn_mid_kernel<kF16, true, false>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_tn_mid_kernel<kF16, false, true>), grid, block, 0, stream, p);
+  return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
+}
+
 }  // namespace dg
 
 extern "C" {
+
+int gemm_f16(char transa, char transb, const void *A, const void *B, void *C, int64_t M,
+             int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void *stream) {
+  dg::Problem pr{A, B, C, 1, M, N, K, lda, ldb, ldc, 0, 0, 0, 1.0f};
+  return dg::launch_f16_layout(transa, transb, pr, (hipStream_t)stream);
+}
 
 int gemm_f16_tn(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
                 int64_t lda, int64_t ldb, int64_t ldc, void *stream) {

@@ -67,6 +67,36 @@ int gemm_f16_tn(const void *A, const void *B, void *C,
                 void *stream);
 
 /*
+ * FP16 GEMM in any of the four BLAS op-code layouts, without a transpose pass.
+ * C = op(A) op(B) is M x N, column-major at C[m + n*ldc] as above; op(A) is
+ * M x K and op(B) is K x N:
+ *   transa 'T': A[m*lda + k]  (K contiguous, lda >= K; the TN case's A)
+ *   transa 'N': A[m + k*lda]  (M contiguous, lda >= M)
+ *   transb 'N': B[k + n*ldb]  (K contiguous, ldb >= K; the TN case's B)
+ *   transb 'T': B[k*ldb + n]  (N contiguous, ldb >= N)
+ * Lower-case codes are accepted.  ('T', 'N') is exactly gemm_f16_tn, with its
+ * tile configurations; the other three run 128 x 128 tiles.  Rounding, tails,
+ * ownership and ordering are those of gemm_f16_tn.  Row-major C = A B with
+ * A row-major M x K and B row-major K x N (the NN indexing of section 11.1 of
+ * the hello-gpu chapter) is this call with transa = transb = 'N' on the
+ * operands swapped: C^T = B^T A^T, computed as gemm_f16('N', 'N', B, A, C,
+ * N, M, K, ldb, lda, ldc).
+ * Source: "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", section "What we
+ * compute" (data in other layouts would otherwise be transposed first), and
+ * "hello-gpu, chapter 11 (GEMM-like)", section 11.1.
+ * Errors: DG_ERR_INVALID_ARGUMENT also for a code other than T/t/N/n and for
+ * lda or ldb below the contiguous extent listed above.  DG_ERR_UNSUPPORTED
+ * for lda or ldb not a multiple of 8; K not a multiple of 8 when an operand is
+ * K-contiguous; M (transa 'N') or N (transb 'T') not a multiple of 8; A, B or
+ * C not 16-byte aligned; 64 rows of an M/N-contiguous operand or 128 rows of
+ * a K-contiguous one spanning 2^31 bytes or more.
+ */
+int gemm_f16(char transa, char transb, const void *A, const void *B, void *C,
+             int64_t M, int64_t N, int64_t K,
+             int64_t lda, int64_t ldb, int64_t ldc,
+             void *stream);
+
+/*
  * FP8 TN GEMM: A and B are OCP FP8 E4M3FN codes (one byte each) carrying the
  * per-tensor fp32 scales scale_a and scale_b; C is bfloat16.
  *   C[m + n*ldc] = bf16_rne( fp32(scale_a * scale_b) * sum_k a(m,k) * b(k,n) )

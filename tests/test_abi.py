@@ -91,6 +91,41 @@ def test_f16_validation(args, status):
     assert f16(*args) == status
 
 
+def f16_any(ta, tb, *args):
+    return dg.lib().gemm_f16(ta, tb, *args, None)
+
+
+@pytest.mark.parametrize("codes,args,status", [
+    ((b"X", b"N"), (A_ADDR, B_ADDR, C_ADDR, 8, 8, 8, 8, 8, 8), dg.DG_ERR_INVALID_ARGUMENT),
+    ((b"N", b"Q"), (A_ADDR, B_ADDR, C_ADDR, 8, 8, 8, 8, 8, 8), dg.DG_ERR_INVALID_ARGUMENT),
+    ((b"N", b"N"), (A_ADDR, B_ADDR, C_ADDR, 16, 8, 8, 8, 8, 16), dg.DG_ERR_INVALID_ARGUMENT),  # lda < M
+    ((b"T", b"T"), (A_ADDR, B_ADDR, C_ADDR, 8, 16, 8, 8, 8, 8), dg.DG_ERR_INVALID_ARGUMENT),  # ldb < N
+    ((b"n", b"t"), (A_ADDR, B_ADDR, C_ADDR, 8, 8, 8, 8, 8, 4), dg.DG_ERR_INVALID_ARGUMENT),   # ldc < M
+    ((b"N", b"N"), (A_ADDR, B_ADDR, A_ADDR + 32, 8, 8, 8, 8, 8, 8),
+     dg.DG_ERR_INVALID_ARGUMENT),                                                     # C overlaps A
+    ((b"N", b"T"), (None, B_ADDR, C_ADDR, 8, 8, 8, 8, 8, 8), dg.DG_ERR_INVALID_ARGUMENT),
+    ((b"N", b"N"), (A_ADDR, B_ADDR, C_ADDR, 12, 8, 8, 16, 8, 12), dg.DG_ERR_UNSUPPORTED),  # M % 8
+    ((b"T", b"T"), (A_ADDR, B_ADDR, C_ADDR, 8, 12, 8, 8, 16, 8), dg.DG_ERR_UNSUPPORTED),   # N % 8
+    ((b"N", b"N"), (A_ADDR, B_ADDR, C_ADDR, 8, 8, 12, 8, 16, 8), dg.DG_ERR_UNSUPPORTED),   # K % 8, B K-major
+    ((b"N", b"T"), (A_ADDR, B_ADDR, C_ADDR, 8, 8, 8, 12, 8, 8), dg.DG_ERR_UNSUPPORTED),    # lda % 8
+    ((b"N", b"T"), (A_ADDR, B_ADDR + 2, C_ADDR, 8, 8, 8, 8, 8, 8), dg.DG_ERR_UNSUPPORTED),  # misaligned
+    ((b"N", b"N"), (1 << 44, 2 << 44, 3 << 44, 8, 8, 8, 16 << 20, 8, 8),
+     dg.DG_ERR_UNSUPPORTED),                                                          # 64 rows >= 2 GiB
+    ((b"T", b"N"), (A_ADDR, B_ADDR, C_ADDR, 8, 8, 12, 16, 16, 8), dg.DG_ERR_UNSUPPORTED),  # TN rules
+    ((b"N", b"T"), (None, None, None, 0, 8, 8, 8, 8, 8), dg.DG_OK),                    # M = 0: no-op
+    ((b"T", b"T"), (None, None, None, 8, 0, 8, 8, 8, 8), dg.DG_OK),                    # N = 0: no-op
+])
+def test_f16_any_layout_validation(codes, args, status):
+    assert f16_any(*codes, *args) == status
+
+
+def test_f16_binding_rejects_bad_codes():
+    with pytest.raises(ValueError):
+        dg.gemm_f16("X", "N", A_ADDR, B_ADDR, C_ADDR, 8, 8, 8, 8, 8, 8)
+    with pytest.raises(ValueError):
+        dg.gemm_f16("NN", "N", A_ADDR, B_ADDR, C_ADDR, 8, 8, 8, 8, 8, 8)
+
+
 def test_f8_validation():
     L = dg.lib()
     assert L.gemm_f8_tn(A_ADDR, B_ADDR, C_ADDR, 8, 8, 8, 16, 16, 8, 1.0, 1.0, None) == \
