@@ -48,9 +48,18 @@ def kernel_name(w):
     if w.kind == "attn":
         return "attention_fwd_kernel"
     kind = 1 if w.kind == "f8" else 0
+    layout = w.extra.get("layout", "TN")
+    if layout != "TN":
+        amn = "true" if layout[0] == "N" else "false"
+        bmn = "true" if layout[1] == "T" else "false"
+        if dg.f16_config(layout[0], layout[1], w.M, w.N, w.K) == 2:
+            return "gemm_tn_mid_kernel<0, %s, %s>" % (amn, bmn)
+        return "gemm_tn_kernel<0, 8, %s, %s>" % (amn, bmn)
     cfg = dg.tn_config(w.M, w.N, w.K, w.batch, fp8=(w.kind == "f8"))
-    return {0: "gemm_tn_kernel<%d, 8>" % kind, 1: "gemm_tn_kernel<%d, 7>" % kind,
-            2: "gemm_tn_mid_kernel<%d>" % kind, 3: "gemm_tn_skinny_kernel<%d>" % kind}[cfg]
+    return {0: "gemm_tn_kernel<%d, 8, false, false>" % kind,
+            1: "gemm_tn_kernel<%d, 7, false, false>" % kind,
+            2: "gemm_tn_mid_kernel<%d, false, false>" % kind,
+            3: "gemm_tn_skinny_kernel<%d>" % kind}[cfg]
 
 
 CSRC = os.path.join(ROOT, "dense_gemm_tn_amd", "csrc")
@@ -91,6 +100,7 @@ def make_launcher(w, dev):
 
     x = inputs.make(w)
     R = rotation_sets(w)
+    layout = w.extra.get("layout", "TN")
     sets = []
     for r in range(R):
         if w.kind == "attn":
@@ -105,8 +115,11 @@ def make_launcher(w, dev):
             s = torch.empty((w.batch, w.N, w.M), dtype=torch.float16, device=dev)
             sets.append((q, k, s))
         else:
-            a = torch.from_numpy(np.ascontiguousarray(x["A"])).to(dev)
-            b = torch.from_numpy(np.ascontiguousarray(x["B"])).to(dev)
+            # Operands as they lie for the workload's op codes: A 'N' is stored
+            # [K, M] (M contiguous), B 'T' [K, N] (N contiguous).
+            a = torch.from_numpy(np.ascontiguousarray(x["A"] if layout[0] == "T" else x["A"].T))
+            b = torch.from_numpy(np.ascontiguousarray(x["B"] if layout[1] == "N" else x["B"].T))
+            a, b = a.to(dev), b.to(dev)
             cdt = torch.float16 if w.kind == "f16" else torch.bfloat16
             c = torch.empty((w.N, w.M), dtype=cdt, device=dev)
             sets.append((a, b, c))
@@ -120,7 +133,10 @@ def make_launcher(w, dev):
                                  w.M * w.K, w.N * w.K, w.K * w.N, w.M * w.K, scale)
             return
         a, b, c = sets[i % R]
-        if w.kind == "f16":
+        if w.kind == "f16" and layout != "TN":
+            dg.gemm_f16(layout[0], layout[1], a, b, c, w.M, w.N, w.K, a.stride(0), b.stride(0),
+                        w.M)
+        elif w.kind == "f16":
             dg.gemm_f16_tn(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M)
         elif w.kind == "f8":
             dg.gemm_f8_tn(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M, x["scale_a"], x["scale_b"])

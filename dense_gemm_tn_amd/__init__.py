@@ -33,6 +33,7 @@ EXPORTS = (
     "gemm_tile_order",
     "gemm_block_tile",
     "gemm_tn_config",
+    "gemm_f16_config",
 )
 
 _lib = None
@@ -65,8 +66,9 @@ def lib() -> ctypes.CDLL:
         L.gemm_tile_order.argtypes = [i64, i64, i64, vp]
         L.gemm_block_tile.argtypes = []
         L.gemm_tn_config.argtypes = [ctypes.c_int, i64, i64, i64, i64]
+        L.gemm_f16_config.argtypes = [ctypes.c_char, ctypes.c_char, i64, i64, i64]
         for f in (L.gemm_f16_tn, L.gemm_f16, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
-                  L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config):
+                  L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config, L.gemm_f16_config):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -162,6 +164,11 @@ CONFIG_NAMES = {0: "256x256", 1: "256x224", 2: "128x128", 3: "skinny-K"}
 def tn_config(M: int, N: int, K: int, batch: int = 1, fp8: bool = False) -> int:
     """Kernel configuration code the GEMM entry points choose (see gemm_tn_config)."""
     return lib().gemm_tn_config(1 if fp8 else 0, M, N, K, batch)
+
+
+def f16_config(transa: str, transb: str, M: int, N: int, K: int) -> int:
+    """Kernel configuration gemm_f16 chooses for a layout (see gemm_f16_config)."""
+    return lib().gemm_f16_config(transa.encode(), transb.encode(), M, N, K)
 
 
 # ----------------------------------------------------------- tensor helpers

@@ -50,6 +50,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "dense_gemm_tn.h"
 
@@ -208,15 +209,97 @@ struct StepCopy {
   __attribute__((address_space(3))) uint8_t *la, *lb;  // LDS strip bases (+ wave KiB)
 };
 
-// Issue copy d (0..15) of a step: d < 8 is load q = d of A, else load q = d - 8 of B.
+// The same copies issued from inline assembly, in the kernels with an
+// M/N-contiguous operand.  The compiler's wait-count insertion makes each
+// ds_read_b64_tr_b16 wait for every LDS-writing buffer load it can see
+// (vmcnt(0) before each transposing read), which would drain the copy
+// pipeline several times per K-step; it does not see these.  The kernels'
+// barriers wait for the copies explicitly (vmcnt), as they do for the others.
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
+struct StepCopyAsm {
+  v4u32 ra, rb;        // raw buffer descriptors (the words make_rsrc builds)
+  uint32_t va, vb;     // lane offsets for q = 0
+  uint32_t la, lb;     // LDS byte addresses of the strips (+ this wave's part)
+};
+__device__ __forceinline__ v4u32 rsrc_words(const void *base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return v4u32{(uint32_t)b, (uint32_t)(b >> 32) & 0xffffu, bytes, kRsrcWord3};
+}
+// One 16-byte-per-lane buffer load into LDS at M0 = `lds` (+ 16 * lane); one
+// wait state separates the M0 write from the load.
+__device__ __forceinline__ void dma16(const v4u32 &r, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(voff), "s"(r), "{m0}"(lds) : "memory");
+}
+
+// M/N-contiguous fp16 operands of the 256 x 256 kernel (A of an 'N' op, B of
+// a 'T' op) are staged as they lie: a stage strip is 64 K-rows of 256
+// elements (512 B), the 16-byte chunk c of K-row k in slot c ^ mn_key(k).
+// Load q of wave w fills K-rows mn_wave_row(w) + mn_load_row(q) + {0, 1}
+// (lanes 0..31 the first, 32..63 the second): w supplies row bits 1 and 3, q
+// bits 2, 4 and 5, so a lane's key is the same for all eight of its loads.
+__host__ __device__ constexpr int mn_key(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+__host__ __device__ constexpr int mn_wave_row(int w) { return 2 * (w & 1) + 8 * (w >> 1); }
+__host__ __device__ constexpr int mn_load_row(int q) {
+  return 4 * (q & 1) + 16 * ((q >> 1) & 1) + 32 * (q >> 2);
+}
+constexpr int kMnRowBytes = 512;
+
+// Issue copy d of a step: d < 8 is load q = d of A, else load q = d - 8 of B.
+// K-contiguous operands: load q is 32 rows further (q_stride = 32 rows).
+// M/N-contiguous ones: load q starts mn_load_row(q) K-rows further
+// (q_stride = one K-row).
+template <bool AMN, bool BMN>
 __device__ __forceinline__ void copy_one(const StepCopy &c, int d, uint32_t qs_a, uint32_t qs_b) {
   if (d < 8) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, (lds_void_t *)(c.la + d * 4096), 16,
-                                             c.va + d * qs_a, 0, 0, 0);
+    const int lds_off = AMN ? mn_load_row(d) * kMnRowBytes : d * 4096;
+    const uint32_t step = (uint32_t)(AMN ? mn_load_row(d) : d) * qs_a;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, (lds_void_t *)(c.la + lds_off), 16,
+                                             c.va + step, 0, 0, 0);
   } else {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, (lds_void_t *)(c.lb + (d - 8) * 4096), 16,
-                                             c.vb + (d - 8) * qs_b, 0, 0, 0);
+    const int q = d - 8;
+    const int lds_off = BMN ? mn_load_row(q) * kMnRowBytes : q * 4096;
+    const uint32_t step = (uint32_t)(BMN ? mn_load_row(q) : q) * qs_b;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, (lds_void_t *)(c.lb + lds_off), 16,
+                                             c.vb + step, 0, 0, 0);
   }
+}
+
+template <bool AMN, bool BMN>
+__device__ __forceinline__ void copy_one(const StepCopyAsm &c, int d, uint32_t qs_a,
+                                         uint32_t qs_b) {
+  if (d < 8) {
+    const int lds_off = AMN ? mn_load_row(d) * kMnRowBytes : d * 4096;
+    dma16(c.ra, c.va + (uint32_t)(AMN ? mn_load_row(d) : d) * qs_a, c.la + lds_off);
+  } else {
+    const int q = d - 8;
+    const int lds_off = BMN ? mn_load_row(q) * kMnRowBytes : q * 4096;
+    dma16(c.rb, c.vb + (uint32_t)(BMN ? mn_load_row(q) : q) * qs_b, c.lb + lds_off);
+  }
+}
+
+// Descriptor bytes of an M/N-contiguous operand's K-step starting at K-row k0
+// (rows of ld_b bytes, `cols` elements of the block inside the matrix): all
+// 64 rows while the step is not the last, else up to the block's last element
+// of K-row K - 1, so rows at or past K and columns past the matrix in that
+// row read zero.  Other out-of-matrix columns only feed outputs that are never
+// stored.
+__device__ __forceinline__ uint32_t mn_records(int64_t K, int64_t k0, int64_t ld_b,
+                                               int64_t cols) {
+  return K - k0 > 64 ? (uint32_t)(64 * ld_b) : (uint32_t)((K - k0 - 1) * ld_b + cols * 2);
+}
+
+// An fp16 MFMA operand fragment of an M/N-contiguous strip: lanes 16g .. 16g+15
+// take K-rows 8g .. 8g+7 of sub-step s from two ds_read_b64_tr_b16 (rows
+// 32s + 8g + 4h + (l % 16) / 4, h = 0, 1).  `off` is the lane's byte offset for
+// s = 0, h = 0 (swizzle applied).
+__device__ __forceinline__ half8_t mn_frag(lds_cptr strip, uint32_t off, int s) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  lds_cptr at = strip + off + s * 32 * kMnRowBytes;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)at);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(at + 4 * kMnRowBytes));
+  return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // One MFMA operand fragment: 32 rows x (16 fp16 or 64 fp8) of K.  Lane l reads
@@ -379,9 +462,10 @@ static_assert(extra_slot<8>(8) == 25 && extra_slot<7>(0) == 8 && extra_slot<7>(3
 // NTN = 16-column MFMA tiles per wave along N: 8 (256 x 256 block tiles) or 7
 // (256 x 224, which the host picks when it packs the grid into fewer rounds
 // of one block per CU).
-template <int KIND, int NTN>
+template <int KIND, int NTN, bool AMN, bool BMN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   typedef Traits<KIND> T;
+  static_assert(KIND == kF16 || (!AMN && !BMN), "M/N-contiguous operands are fp16 only");
   constexpr int kTileN = 2 * 16 * NTN;   // block tile width (columns of B / C)
   // Two stages of [A strip | B strip], 64 KiB each.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * 2 * kStageBytes];
@@ -394,8 +478,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTileN;
 
-  const uint8_t *Ab = p.A + head * p.stride_a_b + m0 * p.lda_b;
-  const uint8_t *Bb = p.B + head * p.stride_b_b + n0 * p.ldb_b;
+  // Block bases: K-contiguous operands at their first row, M/N-contiguous ones
+  // at their first column (element m0 / n0 of K-row 0).
+  const uint8_t *Ab = p.A + head * p.stride_a_b + (AMN ? m0 * 2 : m0 * p.lda_b);
+  const uint8_t *Bb = p.B + head * p.stride_b_b + (BMN ? n0 * 2 : n0 * p.ldb_b);
   uint8_t *Cb = p.C + head * p.stride_c_b;
   const int64_t rows_a = (p.M - m0) < kTile ? (p.M - m0) : kTile;
   const int64_t rows_b = (p.N - n0) < kTileN ? (p.N - n0) : kTileN;
@@ -408,11 +494,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   // the MI355X FP8 GEMM page: a ds_read_b128 phase (16 lanes, 16 consecutive
   // rows, one chunk) covers all 16 slots of the 256-byte bank period.
   // Copy geometry of this lane (same for A and B, see copy_one).
+  // M/N-contiguous copies: K-row mn_wave_row(w) + (l >> 5) (+ mn_load_row(q)),
+  // slot l & 31, fetching the chunk the swizzle keeps there.
   const int crow = 8 * wave + (lane >> 3);            // row within a 32-row band
   const int gchunk = (lane & 7) ^ ((crow >> 1) & 7);  // global 16-B chunk of that row
-  const uint32_t voff_a = (uint32_t)(crow * p.lda_b) + gchunk * 16;
-  const uint32_t voff_b = (uint32_t)(crow * p.ldb_b) + gchunk * 16;
-  const uint32_t qs_a = (uint32_t)(32 * p.lda_b), qs_b = (uint32_t)(32 * p.ldb_b);
+  const int mrow = mn_wave_row(wave) + (lane >> 5);
+  const uint32_t mchunk16 = (uint32_t)(((lane & 31) ^ mn_key(mrow)) * 16);
+  const uint32_t voff_a = AMN ? (uint32_t)(mrow * p.lda_b) + mchunk16
+                              : (uint32_t)(crow * p.lda_b) + gchunk * 16;
+  const uint32_t voff_b = BMN ? (uint32_t)(mrow * p.ldb_b) + mchunk16
+                              : (uint32_t)(crow * p.ldb_b) + gchunk * 16;
+  const uint32_t qs_a = (uint32_t)((AMN ? 1 : 32) * p.lda_b);
+  const uint32_t qs_b = (uint32_t)((BMN ? 1 : 32) * p.ldb_b);
   const int kchunk = gchunk * (16 / T::es);           // K offset of the chunk in a step
 
   // Fragment geometry: an MFMA operand covers 16 rows; lane l reads row l % 16
@@ -434,6 +527,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     a_off[x] = lo + wm * kWaveTile * kRowBytes;
     b_off[x] = lo + kStageBytes + wn * S::WN * kRowBytes;
   }
+  // M/N-contiguous fragments: lane (rl, grp) reads K-row 8 grp + rl / 4 at
+  // elements 4 (rl % 4) .. +3 of the 16-wide tile whose first chunk is c0, i.e.
+  // slot (c0 + (rl % 4) / 2) ^ key, byte 8 (rl % 2).  c0 is even and the key
+  // only has bits 1..3, so the address is mn_lane ^ (16 c0): one XOR per read.
+  const int mk = 8 * grp + (rl >> 2);
+  const uint32_t mn_lane = (uint32_t)(mk * kMnRowBytes + 16 * mn_key(mk) +
+                                      16 * ((rl & 3) >> 1) + 8 * (rl & 1));
+  typedef typename T::frag_t frag_t;
+  constexpr int kTileBytes = MT * kRowBytes;      // LDS bytes between MFMA tiles
+  // Fragment g of A (16 rows at wave row 16 g) and j of B, sub-step s, from the
+  // stage at `st`.
+  auto frag_a = [&](lds_cptr st, int g, int s) -> frag_t {
+    if constexpr (AMN)
+      return mn_frag(st, mn_lane ^ (uint32_t)(16 * (kWaveTile / 8 * wm + 2 * g)), s);
+    else
+      return read_frag<KIND>(st + g * kTileBytes, a_off, s);
+  };
+  auto frag_b = [&](lds_cptr st, int j, int s) -> frag_t {
+    if constexpr (BMN)
+      return mn_frag(st + kStageBytes, mn_lane ^ (uint32_t)(16 * (S::WN / 8 * wn + 2 * j)), s);
+    else
+      return read_frag<KIND>(st + j * kTileBytes, b_off, s);
+  };
 
   typename S::acc_t acc[NTM][NTN];
 #pragma unroll
@@ -455,9 +571,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   // pad step, and the steps past the end issued unconditionally by the last
   // iterations) read zeros and touch no memory.
   struct StepScalars {
-    uint32_t kb;   // byte offset of the step's K range
+    uint32_t kb;   // byte offset of the step's K range (K-contiguous operands)
     int left;      // K elements of the step inside the matrix (0 .. kstep)
     int stage;
+    int64_t k0;    // first K index of the step (M/N-contiguous operands)
   };
   auto step_scalars = [&](int64_t t) {
     const int64_t k0 = (t - pad) * T::kstep;
@@ -467,23 +584,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     u.kb = inside ? (uint32_t)(k0 * T::es) : 0u;
     u.left = !inside ? 0 : (rem >= T::kstep ? T::kstep : (int)rem);
     u.stage = (int)(t & 1);
+    if constexpr (AMN || BMN) u.k0 = inside ? k0 : -1;
     return u;
   };
-  auto step_rsrc = [&](const StepScalars &u, StepCopy &c) {
-    c.ra = make_rsrc(Ab + u.kb, rec_a - u.kb);
-    c.rb = make_rsrc(Bb + u.kb, rec_b - u.kb);
-    lds_u8 *st = (lds_u8 *)smem + u.stage * 2 * kStageBytes + wave * 1024;
-    c.la = st;
-    c.lb = st + kStageBytes;
+  typedef std::conditional_t<AMN || BMN, StepCopyAsm, StepCopy> Copy;
+  auto step_rsrc = [&](const StepScalars &u, Copy &c) {
+    if constexpr (AMN || BMN) {
+      // M/N-contiguous: rebased on the step's first K-row; a step outside the
+      // matrix gets an empty descriptor (every load reads zero).
+      if constexpr (AMN)
+        c.ra = u.k0 < 0 ? rsrc_words(Ab, 0u)
+                        : rsrc_words(Ab + u.k0 * p.lda_b, mn_records(p.K, u.k0, p.lda_b, rows_a));
+      else
+        c.ra = rsrc_words(Ab + u.kb, rec_a - u.kb);
+      if constexpr (BMN)
+        c.rb = u.k0 < 0 ? rsrc_words(Bb, 0u)
+                        : rsrc_words(Bb + u.k0 * p.ldb_b, mn_records(p.K, u.k0, p.ldb_b, rows_b));
+      else
+        c.rb = rsrc_words(Bb + u.kb, rec_b - u.kb);
+      const uint32_t st = (uint32_t)(uintptr_t)((lds_u8 *)smem + u.stage * 2 * kStageBytes);
+      c.la = st + (AMN ? mn_wave_row(wave) * kMnRowBytes : wave * 1024);
+      c.lb = st + kStageBytes + (BMN ? mn_wave_row(wave) * kMnRowBytes : wave * 1024);
+    } else {
+      c.ra = make_rsrc(Ab + u.kb, rec_a - u.kb);
+      c.rb = make_rsrc(Bb + u.kb, rec_b - u.kb);
+      lds_u8 *st = (lds_u8 *)smem + u.stage * 2 * kStageBytes + wave * 1024;
+      c.la = st;
+      c.lb = st + kStageBytes;
+    }
   };
-  auto step_lanes = [&](const StepScalars &u, StepCopy &c) {
+  auto step_lanes = [&](const StepScalars &u, Copy &c) {
     const bool valid = kchunk < u.left;   // this lane's chunk is inside K
-    c.va = valid ? voff_a : kOob;
-    c.vb = valid ? voff_b : kOob;
+    c.va = (AMN || valid) ? voff_a : kOob;
+    c.vb = (BMN || valid) ? voff_b : kOob;
   };
   auto step_copy = [&](int64_t t) {
     const StepScalars u = step_scalars(t);
-    StepCopy c;
+    Copy c;
     step_rsrc(u, c);
     step_lanes(u, c);
     return c;
@@ -498,8 +635,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  typedef typename T::frag_t frag_t;
-  constexpr int kTileBytes = MT * kRowBytes;      // LDS bytes between MFMA tiles
 
   // 8 x NTN MFMA tiles per wave; a K-step is `subs` sub-steps (fp16: two
   // 32-deep, fp8: one 128-deep) of 8 * NTN MFMA slots, MFMA (g, j) in slot
@@ -520,7 +655,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   constexpr int kQ = 8 * NTN, kBarQ = NTN;
   constexpr int kBarSlot = (T::subs - 1) * kQ + kBarQ;
   constexpr int kAfter = T::subs * kQ - kBarSlot;  // window slots in the barrier's step
-  constexpr int kCopies = 8 + NTN;                 // copy instructions per wave per step
+  constexpr int kCopies = 8 + (BMN ? 8 : NTN);     // copy instructions per wave per step
   // Copy window in slots (about 1000 cycles of MFMA for either), chosen by
   // measurement (fp16 4096^3, fp8 8192^3), capped by the slots before the
   // next step's barrier.
@@ -533,25 +668,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   if (nk2 > 0) {
     // Copies of all of step 0 and the first kPost of step 1; wait for step 0
     // only (loads complete in order) and publish it.
-    const StepCopy c0 = step_copy(0);
+    const Copy c0 = step_copy(0);
 #pragma unroll
-    for (int d = 0; d < kCopies; ++d) copy_one(c0, d, qs_a, qs_b);
-    const StepCopy c1 = step_copy(1);
+    for (int d = 0; d < kCopies; ++d) copy_one<AMN, BMN>(c0, d, qs_a, qs_b);
+    const Copy c1 = step_copy(1);
 #pragma unroll
-    for (int d = 0; d < kPost; ++d) copy_one(c1, d, qs_a, qs_b);
+    for (int d = 0; d < kPost; ++d) copy_one<AMN, BMN>(c1, d, qs_a, qs_b);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPost));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     lds_cptr st0 = (lds_cptr)smem;
 #pragma unroll
-    for (int j = 0; j < NTN; ++j) fb[0][j] = read_frag<KIND>(st0 + j * kTileBytes, b_off, 0);
+    for (int j = 0; j < NTN; ++j) fb[0][j] = frag_b(st0, j, 0);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) fa[g] = read_frag<KIND>(st0 + g * kTileBytes, a_off, 0);
+    for (int g = 0; g < 8; ++g) fa[g] = frag_a(st0, g, 0);
   }
   // cn: copies of step t + 1 (its last ones are issued early in step t);
   // cnn: step t + 2's, planned in slots kPlan .. kPlan + 2 of step t.
-  StepCopy cn = step_copy(1), cnn;
+  Copy cn = step_copy(1), cnn;
   StepScalars un;
   constexpr int kPlan = kBarSlot - 6;
   static_assert(kPlan >= 0 && kPlan >= kWin - kAfter, "plan after the last copy of step t + 1");
@@ -573,25 +708,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
           for (int j = 0; j < NTN; ++j) {
             const int q = NTN * g + j;
             const int slot = kQ * s + q;
-            if (j == 0 && g >= 1)
-              fa[g - 1] = read_frag<KIND>(src + (g - 1) * kTileBytes, a_off, s_n);
+            if (j == 0 && g >= 1) fa[g - 1] = frag_a(src, g - 1, s_n);
             if (q == extra_slot<NTN>(0)) {
-              if (par == 0) fx = read_frag<KIND>(src + 7 * kTileBytes, a_off, s_n);
-              else fa[7] = read_frag<KIND>(src + 7 * kTileBytes, a_off, s_n);
+              if (par == 0) fx = frag_a(src, 7, s_n);
+              else fa[7] = frag_a(src, 7, s_n);
             }
 #pragma unroll
             for (int jj = 0; jj < NTN; ++jj)
-              if (q == extra_slot<NTN>(jj + 1))
-                fb[par ^ 1][jj] = read_frag<KIND>(src + jj * kTileBytes, b_off, s_n);
+              if (q == extra_slot<NTN>(jj + 1)) fb[par ^ 1][jj] = frag_b(src, jj, s_n);
             if (slot == kPlan) un = step_scalars(t + 2);
             if (slot == kPlan + 1) step_rsrc(un, cnn);
             if (slot == kPlan + 2) step_lanes(un, cnn);
             if (slot < kWin - kAfter) {
               const int x = slot + kAfter;     // at most one copy per slot
-              if (first_copy(x) < first_copy(x + 1)) copy_one(cn, first_copy(x), qs_a, qs_b);
+              if (first_copy(x) < first_copy(x + 1)) copy_one<AMN, BMN>(cn, first_copy(x), qs_a, qs_b);
             } else if (slot >= kBarSlot && slot - kBarSlot < kWin) {
               const int x = slot - kBarSlot;
-              if (first_copy(x) < first_copy(x + 1)) copy_one(cnn, first_copy(x), qs_a, qs_b);
+              if (first_copy(x) < first_copy(x + 1)) copy_one<AMN, BMN>(cnn, first_copy(x), qs_a, qs_b);
             }
             if (g == 7 && par == 1) acc[g][j] = mma(fx, fb[par][j], acc[g][j]);
             else acc[g][j] = mma(fa[g], fb[par][j], acc[g][j]);
@@ -624,10 +757,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   }
 }
 
-template __global__ void gemm_tn_kernel<kF16, 8>(Params);
-template __global__ void gemm_tn_kernel<kF16, 7>(Params);
-template __global__ void gemm_tn_kernel<kF8, 8>(Params);
-template __global__ void gemm_tn_kernel<kF8, 7>(Params);
+template __global__ void gemm_tn_kernel<kF16, 8, false, false>(Params);
+template __global__ void gemm_tn_kernel<kF16, 7, false, false>(Params);
+template __global__ void gemm_tn_kernel<kF8, 8, false, false>(Params);
+template __global__ void gemm_tn_kernel<kF8, 7, false, false>(Params);
 
 // ----------------------------------------------------------------- skinny K
 // Kernels for K * es <= 256 bytes (the QK^T shape: K = head dim 128): the whole
@@ -942,33 +1075,47 @@ __device__ __forceinline__ int mn_swz(int k) { return 2 * (k & 3) + 8 * ((k >> 3
 
 // Copies of one operand of the 128 x 128 kernel for K-step t into this
 // wave's KiB `st` of each 4 KiB quarter of the operand's LDS strip.
-template <int KIND, bool MN>
+// ASM: issue the loads from inline assembly (kernels with an M/N-contiguous
+// operand; see StepCopyAsm).
+template <int KIND, bool MN, bool ASM>
 __device__ __forceinline__ void mid_copy(const uint8_t *base, int64_t ld_b, int64_t K,
                                          uint32_t rec, uint32_t voff, uint32_t qs, int kchunk,
                                          const MidOperand<MN> &op, int64_t t, lds_u8 *st) {
   typedef Traits<KIND> T;
   const int64_t k0 = t * T::kstep;
+  uint32_t off[4];
+  const uint8_t *rbase;
+  uint32_t rbytes;
   if constexpr (MN) {
     // Rebased on the step's first K-row; rows at or past K and chunks past
     // M / N read zero.  The descriptor covers the step's 64 K-rows.
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + k0 * ld_b, (uint32_t)(T::kstep * ld_b));
+    rbase = base + k0 * ld_b;
+    rbytes = (uint32_t)(T::kstep * ld_b);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const bool ok = op.cvalid[q] && k0 + op.krow[q] < K;
-      const uint32_t off = ok ? op.off[q] : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(st + q * 4096), 16, off, 0, 0,
-                                               0);
+      off[q] = ok ? op.off[q] : kOob;
     }
   } else {
     const int64_t rem = K - k0;
     const int left = rem >= T::kstep ? T::kstep : (int)rem;
     const uint32_t kb = (uint32_t)(k0 * T::es);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + kb, rec - kb);
+    rbase = base + kb;
+    rbytes = rec - kb;
     const uint32_t v = kchunk < left ? voff : kOob;
 #pragma unroll
+    for (int q = 0; q < 4; ++q) off[q] = v + q * qs;
+  }
+  if constexpr (ASM) {
+    const v4u32 r = rsrc_words(rbase, rbytes);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(r, off[q], (uint32_t)(uintptr_t)(st + q * 4096));
+  } else {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(rbase, rbytes);
+#pragma unroll
     for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(st + q * 4096), 16,
-                                               v + q * qs, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)(st + q * 4096), 16, off[q], 0,
+                                               0, 0);
   }
 }
 
@@ -1026,8 +1173,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
 
   auto copy_step = [&](int64_t t) {
     lds_u8 *st = (lds_u8 *)smem + (t & 1) * 2 * kMidStrip + wave * 1024;
-    mid_copy<KIND>(Ab, p.lda_b, p.K, rec_a, voff_a, qs_a, kchunk, opa, t, st);
-    mid_copy<KIND>(Bb, p.ldb_b, p.K, rec_b, voff_b, qs_b, kchunk, opb, t, st + kMidStrip);
+    mid_copy<KIND, AMN, AMN || BMN>(Ab, p.lda_b, p.K, rec_a, voff_a, qs_a, kchunk, opa, t, st);
+    mid_copy<KIND, BMN, AMN || BMN>(Bb, p.ldb_b, p.K, rec_b, voff_b, qs_b, kchunk, opb, t,
+                                    st + kMidStrip);
   };
 
   // Fragments.  K-major: lane l reads row l % 16 of a 16-row tile; fp16 takes
@@ -1139,11 +1287,15 @@ struct Config {
 // time = (blocks per CU, rounded up) x tile area, the small tile's area
 // weighted by kMidCost / 64.  DG_GEMM_TILE = 256, 224 or 128 in the
 // environment forces the tile of a non-skinny problem (measurement and tests).
-static Config choose_config(int es, int64_t M, int64_t N, int64_t K, int64_t batch) {
-  if (K * es <= kSkRow) return Config{kCfgSkinny};
+// tn = false: a layout with an M/N-contiguous operand, which has neither the
+// skinny-K kernel (its problems take the 128 x 128 tiles) nor the 224-wide
+// tiles.
+static Config choose_config(int es, int64_t M, int64_t N, int64_t K, int64_t batch,
+                            bool tn = true) {
+  if (K * es <= kSkRow) return Config{tn ? kCfgSkinny : kCfgMid};
   if (const char *force = getenv("DG_GEMM_TILE")) {
     if (!strcmp(force, "256")) return Config{kCfg256};
-    if (!strcmp(force, "224")) return Config{kCfg224};
+    if (!strcmp(force, "224")) return Config{tn ? kCfg224 : kCfg256};
     if (!strcmp(force, "128")) return Config{kCfgMid};
   }
   const int64_t cus = cu_count();
@@ -1152,7 +1304,7 @@ static Config choose_config(int es, int64_t M, int64_t N, int64_t K, int64_t bat
     const int64_t blocks = tm * ((N + 32 * w - 1) / (32 * w)) * batch;
     return ((blocks + cus - 1) / cus) * w;
   };
-  const int64_t ntn = cost(7) < cost(8) ? 7 : 8;
+  const int64_t ntn = tn && cost(7) < cost(8) ? 7 : 8;
   const int64_t mid_blocks = ((M + kMidTile - 1) / kMidTile) * ((N + kMidTile - 1) / kMidTile) * batch;
   const int64_t t_big = cost(ntn) * kTile * 32 * 64;  // x 64: the scale of kMidCost
   const int64_t t_mid = ((mid_blocks + cus - 1) / cus) * kMidTile * kMidTile * kMidCost;
@@ -1234,16 +1386,20 @@ static int launch(const Problem &pr, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, p);
   else if (ntn == 8)
-    hipLaunchKernelGGL((gemm_tn_kernel<KIND, 8>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_tn_kernel<KIND, 8, false, false>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_tn_kernel<KIND, 7>), dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((gemm_tn_kernel<KIND, 7, false, false>), dim3((unsigned)blocks),
+                       dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
 // fp16 products in any of the four op-code layouts.  TN goes through
-// launch<> and its configurations; the others take the 128 x 128 kernel with
-// each M- or N-contiguous operand (A of an 'N' op, B of a 'T' op) staged as it
-// lies in memory and turned in the fragment reads -- no transpose pass.
+// launch<> and its configurations; for the others each M- or N-contiguous
+// operand (A of an 'N' op, B of a 'T' op) is staged as it lies in memory and
+// turned by the fragment reads -- no transpose pass -- in the 256-row kernel
+// or the 128 x 128 one, picked by the same selector (the skinny-K kernel is
+// TN-only; its problems take the 128 x 128 tiles).
 static int launch_f16_layout(char ta, char tb, const Problem &pr, hipStream_t stream) {
   const bool a_t = ta == 'T' || ta == 't', a_n = ta == 'N' || ta == 'n';
   const bool b_t = tb == 'T' || tb == 't', b_n = tb == 'N' || tb == 'n';
@@ -1267,20 +1423,21 @@ static int launch_f16_layout(char ta, char tb, const Problem &pr, hipStream_t st
   if ((!amn || !bmn) && pr.K % 8) return DG_ERR_UNSUPPORTED;
   if ((amn && pr.M % 8) || (bmn && pr.N % 8)) return DG_ERR_UNSUPPORTED;
   if (!aligned16(pr.A) || !aligned16(pr.B) || !aligned16(pr.C)) return DG_ERR_UNSUPPORTED;
-  // Offsets inside one block's descriptors stay below kOob: 128 rows of a
-  // K-contiguous operand, 64 K-rows (one step) of an M/N-contiguous one.
-  auto reach = [&](bool mn, int64_t ld) {
-    return mn ? 64 * ld * 2 + 256 : kMidTile * ld * 2 + kRowBytes;
+  // Offsets inside one block's descriptors stay below kOob: 256 rows of a
+  // K-contiguous operand (and its strip), 64 K-rows (one step, 512 bytes of
+  // columns) of an M/N-contiguous one.
+  auto fits = [&](bool mn, int64_t ld, int64_t rows) {
+    if (mn) return 64 * ld * 2 + 2 * kMnRowBytes < (int64_t)kOob;
+    const int64_t strip = (int64_t)span_bytes(rows < kTile ? rows : kTile, pr.K, ld, 2);
+    return kTile * ld * 2 + kRowBytes < (int64_t)kOob && strip < (int64_t)kOob;
   };
-  if (reach(amn, pr.lda) >= (int64_t)kOob || reach(bmn, pr.ldb) >= (int64_t)kOob)
-    return DG_ERR_UNSUPPORTED;
-  if (!amn && (int64_t)span_bytes(pr.M < kMidTile ? pr.M : kMidTile, pr.K, pr.lda, 2) >= (int64_t)kOob)
-    return DG_ERR_UNSUPPORTED;
-  if (!bmn && (int64_t)span_bytes(pr.N < kMidTile ? pr.N : kMidTile, pr.K, pr.ldb, 2) >= (int64_t)kOob)
-    return DG_ERR_UNSUPPORTED;
+  if (!fits(amn, pr.lda, pr.M) || !fits(bmn, pr.ldb, pr.N)) return DG_ERR_UNSUPPORTED;
 
-  const int64_t tiles_m = (pr.M + kMidTile - 1) / kMidTile;
-  const int64_t tiles_n = (pr.N + kMidTile - 1) / kMidTile;
+  const bool mid = choose_config(2, pr.M, pr.N, pr.K, 1, false).kind == kCfgMid;
+  const int64_t tile_m = mid ? kMidTile : kTile;
+  const int64_t tile_n = mid ? kMidTile : kTile;
+  const int64_t tiles_m = (pr.M + tile_m - 1) / tile_m;
+  const int64_t tiles_n = (pr.N + tile_n - 1) / tile_n;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;
 
@@ -1297,12 +1454,17 @@ static int launch_f16_layout(char ta, char tb, const Problem &pr, hipStream_t st
   p.c_vec16_ok = (pr.ldc % 8 == 0) ? 1 : 0;
   p.sk_walk = 1;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (amn && bmn)
-    hipLaunchKernelGGL((gemm_tn_mid_kernel<kF16, true, true>), grid, block, 0, stream, p);
-  else if (amn)
-    hipLaunchKernelGGL((gemm_tn_mid_kernel<kF16, true, false>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm_tn_mid_kernel<kF16, false, true>), grid, block, 0, stream, p);
+  // One kernel per (layout, configuration).
+  typedef void (*kernel_t)(Params);
+  static const kernel_t mids[3] = {gemm_tn_mid_kernel<kF16, true, false>,
+                                   gemm_tn_mid_kernel<kF16, false, true>,
+                                   gemm_tn_mid_kernel<kF16, true, true>};
+  static const kernel_t bigs[3] = {gemm_tn_kernel<kF16, 8, true, false>,
+                                   gemm_tn_kernel<kF16, 8, false, true>,
+                                   gemm_tn_kernel<kF16, 8, true, true>};
+  const int li = amn && bmn ? 2 : amn ? 0 : 1;
+  const kernel_t k = mid ? mids[li] : bigs[li];
+  hipLaunchKernelGGL(k, grid, block, 0, stream, p);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
@@ -1362,6 +1524,13 @@ int gemm_tile_order(int64_t tiles_m, int64_t tiles_n, int64_t batch, int64_t *ou
 }
 
 int gemm_block_tile(void) { return dg::kTile; }
+
+int gemm_f16_config(char transa, char transb, int64_t M, int64_t N, int64_t K) {
+  const bool a_t = transa == 'T' || transa == 't', a_n = transa == 'N' || transa == 'n';
+  const bool b_t = transb == 'T' || transb == 't', b_n = transb == 'N' || transb == 'n';
+  if (!(a_t || a_n) || !(b_t || b_n) || M < 0 || N < 0 || K < 0) return -1;
+  return dg::choose_config(2, M, N, K, 1, a_t && b_n).kind;
+}
 
 int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch) {
   if (M < 0 || N < 0 || K < 0 || batch < 0) return -1;

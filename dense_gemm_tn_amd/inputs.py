@@ -56,6 +56,14 @@ WORKLOADS = {
         Workload("f16_1920x13900x4096", "f16", 1920, 13900, 4096, "normal", seed=0),
         Workload("f16_1920x13900x4096_pm1", "f16", 1920, 13900, 4096, "pm1", seed=1),
         Workload("f8_8192", "f8", 8192, 8192, 8192, "normal", seed=0),
+        # The other op-code layouts (A 'T' = K-contiguous rows, 'N' = M-contiguous;
+        # B 'N' = K-contiguous, 'T' = N-contiguous), same values as f16_4096.
+        Workload("f16_nn_4096", "f16", 4096, 4096, 4096, "normal", seed=0,
+                 extra={"layout": "NN"}),
+        Workload("f16_tt_4096", "f16", 4096, 4096, 4096, "normal", seed=0,
+                 extra={"layout": "TT"}),
+        Workload("f16_nt_4096", "f16", 4096, 4096, 4096, "normal", seed=0,
+                 extra={"layout": "NT"}),
         Workload("qkt_64x4096x4096x128", "qkt", 4096, 4096, 128, "normal", seed=0, batch=64,
                  std=1.0 / math.sqrt(128.0)),
         Workload("attn_64x4096x4096x128", "attn", 4096, 4096, 128, "normal", seed=0, batch=64),

@@ -75,7 +75,9 @@ int gemm_f16_tn(const void *A, const void *B, void *C,
  *   transb 'N': B[k + n*ldb]  (K contiguous, ldb >= K; the TN case's B)
  *   transb 'T': B[k*ldb + n]  (N contiguous, ldb >= N)
  * Lower-case codes are accepted.  ('T', 'N') is exactly gemm_f16_tn, with its
- * tile configurations; the other three run 128 x 128 tiles.  Rounding, tails,
+ * tile configurations; the other three run 256 x 256 or 128 x 128 tiles (see
+ * gemm_f16_config), each M- or N-contiguous operand staged in LDS as it lies
+ * and turned by transposing LDS reads.  Rounding, tails,
  * ownership and ordering are those of gemm_f16_tn.  Row-major C = A B with
  * A row-major M x K and B row-major K x N (the NN indexing of section 11.1 of
  * the hello-gpu chapter) is this call with transa = transb = 'N' on the
@@ -202,6 +204,17 @@ int gemm_block_tile(void);
  * 128 forces configuration 0, 1 or 2 for every non-skinny problem.
  */
 int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch);
+
+/*
+ * Kernel configuration gemm_f16 picks for op codes (transa, transb) and an
+ * M x N x K problem: for ('T', 'N') that of gemm_tn_config; for the other
+ * layouts 0 (256 x 256) or 2 (128 x 128) -- the 224-wide and skinny-K
+ * kernels take K-contiguous operands only, and the selector's choice between
+ * the remaining two is the same cost comparison.  Returns -1 for an invalid
+ * code or a negative size.  DG_GEMM_TILE = 256 or 224 forces configuration 0
+ * and 128 configuration 2 for the other layouts (K > 128).
+ */
+int gemm_f16_config(char transa, char transb, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
 }

@@ -119,6 +119,29 @@ def test_f16_any_layout_validation(codes, args, status):
     assert f16_any(*codes, *args) == status
 
 
+def test_f16_layout_selector(monkeypatch):
+    """Layouts with an M/N-contiguous operand take 256 x 256 or 128 x 128 tiles only;
+    TN keeps gemm_tn_config's choice."""
+    monkeypatch.delenv("DG_GEMM_TILE", raising=False)
+    for M, N, K in [(4096, 4096, 4096), (2048, 2048, 2048), (1920, 13900, 4096),
+                    (256, 256, 64), (8192, 8192, 8192), (1000, 1000, 136)]:
+        tn = dg.lib().gemm_tn_config(0, M, N, K, 1)
+        assert dg.f16_config("T", "N", M, N, K) == tn
+        for ta, tb in [("N", "N"), ("T", "T"), ("N", "T")]:
+            c = dg.f16_config(ta, tb, M, N, K)
+            assert c in (0, 2)
+            if tn in (0, 2):
+                assert c == tn
+            if K <= 128:
+                assert c == 2
+    assert dg.f16_config("N", "T", 4096, 4096, 4096) == 0
+    assert dg.lib().gemm_f16_config(b"X", b"N", 8, 8, 8) == -1
+    assert dg.lib().gemm_f16_config(b"N", b"N", -1, 8, 8) == -1
+    monkeypatch.setenv("DG_GEMM_TILE", "224")
+    assert dg.f16_config("N", "N", 512, 512, 512) == 0
+    assert dg.f16_config("T", "N", 512, 512, 512) == 1
+
+
 def test_f16_binding_rejects_bad_codes():
     with pytest.raises(ValueError):
         dg.gemm_f16("X", "N", A_ADDR, B_ADDR, C_ADDR, 8, 8, 8, 8, 8, 8)

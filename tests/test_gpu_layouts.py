@@ -10,10 +10,11 @@ which reads the same stored buffers through the layout's own strides.
 
 Bars (as for the TN path): +-1 inputs bit-exact; N(0,1) inputs within
 max|C - C_ref| / max|C_ref| <= 4e-3; memory around C and the ldc padding never
-written; operand padding (NaN) never read into a stored element.  The three
-non-TN layouts run the same 128 x 128 kernel as TN with that configuration
-forced, with only the staging and fragment reads changed, so on the same
-logical operands all four give the same bits.
+written; operand padding (NaN) never read into a stored element.  The non-TN
+layouts run the TN kernels (256 x 256 or 128 x 128 tiles) with only the staging
+and fragment reads changed, so on the same logical operands, with the same
+configuration forced, all four give the same bits.  Every shape runs under the
+library's own choice and with each configuration forced (DG_GEMM_TILE).
 """
 import numpy as np
 import pytest
@@ -98,9 +99,23 @@ def exact(got_codes, ref):
         bad.sum(), bad.size, np.argwhere(bad)[0], got[bad][0], want[bad][0])
 
 
+@pytest.fixture(params=[None, "256", "128"], ids=["auto", "tile256", "tile128"])
+def tile(request, monkeypatch):
+    if request.param is None:
+        monkeypatch.delenv("DG_GEMM_TILE", raising=False)
+    else:
+        monkeypatch.setenv("DG_GEMM_TILE", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("ta,tb,M,N,K", CASES)
-def test_layout_pm1_exact(ta, tb, M, N, K):
-    print("layout %s%s %dx%dx%d" % (ta, tb, M, N, K), flush=True)
+def test_layout_pm1_exact(tile, ta, tb, M, N, K):
+    cfg = dg.f16_config(ta, tb, M, N, K)
+    if tile == "256" and K > 128:
+        assert cfg == 0
+    if tile == "128" and not (ta == "T" and tb == "N" and K <= 128):
+        assert cfg == 2
+    print("layout %s%s %dx%dx%d config %d" % (ta, tb, M, N, K, cfg), flush=True)
     x, As, Bs, lda, ldb = case(ta, tb, M, N, K, "pm1", seed=M + 3 * N + 7 * K)
     got, canary = run_layout(ta, tb, As, Bs, M, N, K, lda, ldb)
     assert canary
@@ -108,7 +123,7 @@ def test_layout_pm1_exact(ta, tb, M, N, K):
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
-def test_layout_padding_and_odd_ldc(ta, tb):
+def test_layout_padding_and_odd_ldc(tile, ta, tb):
     """Padded rows (NaN-filled) on both operands and an odd ldc (narrow stores)."""
     M, N, K = 272, 296, 520
     print("layout padding %s%s" % (ta, tb), flush=True)
@@ -131,13 +146,14 @@ def test_layout_k_zero_writes_zeros(ta, tb):
     assert np.all(oracle.decode(got, oracle.FMT_F16) == 0)
 
 
-def test_layouts_agree_bit_for_bit(monkeypatch):
+@pytest.mark.parametrize("force", ["128", "256"])
+def test_layouts_agree_bit_for_bit(monkeypatch, force):
     """N(0,1) data: every layout within the tolerance of the binary64 oracle, and the
-    three transposed-read layouts equal to TN on the 128 x 128 tiles bit for bit."""
+    three transposed-read layouts equal to TN on the same tiles bit for bit."""
     M, N, K = 520, 392, 1544
     x = inputs.make_shape("f16", M, N, K, dist="normal", seed=9)
     ref = oracle.gemm_tn(x["A"], x["B"], oracle.FMT_F16, M, N, K)
-    monkeypatch.setenv("DG_GEMM_TILE", "128")
+    monkeypatch.setenv("DG_GEMM_TILE", force)
     results = {}
     for ta, tb in LAYOUTS:
         print("layout normal %s%s" % (ta, tb), flush=True)
@@ -155,10 +171,13 @@ def test_layouts_agree_bit_for_bit(monkeypatch):
 
 
 @pytest.mark.parametrize("ta,tb", [("N", "N"), ("T", "T"), ("N", "T")])
-def test_layout_full_4096_sampled(ta, tb):
-    """The 4096^3 product in each transposed layout: +-1 data exact on sampled entries
-    (every entry an integer), N(0,1) data on sampled entries within the tolerance."""
+def test_layout_full_4096_sampled(monkeypatch, ta, tb):
+    """The 4096^3 product in each transposed layout, in the configuration the library
+    picks (256 x 256 tiles): +-1 data exact on sampled entries (every entry an
+    integer), N(0,1) data on sampled entries within the tolerance."""
+    monkeypatch.delenv("DG_GEMM_TILE", raising=False)
     M = N = K = 4096
+    assert dg.f16_config(ta, tb, M, N, K) == 0
     rng = np.random.default_rng(17)
     ms = np.concatenate([[0, M - 1, 127, 128], rng.integers(0, M, 1500)])
     ns = np.concatenate([[0, N - 1, 128, 127], rng.integers(0, N, 1500)])
