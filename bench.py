@@ -16,8 +16,10 @@ two flops).
 Prints ONE JSON line.  The headline `value` is the FP16 TN 4096^3 workload; the
 FP8 8192^3 workload, the fused attention forward over 64 heads x 4096 queries x
 4096 keys x head dim 128 (4*M*N*D flops per head: two products), FP16 2048^3
-(a grid the 256-wide tiles cannot fill, served by the 128 x 128 kernel), and any
-other requested workload are reported under "workloads" in the same line.  `roofline` is for the FP16 kernel; `traffic`
+(a grid the 256-wide tiles cannot fill, served by the 128 x 128 kernel), FP16
+4096^3 in the NN, TT and NT op codes (operands read as they lie, no transpose
+pass), and any other requested workload are reported under "workloads" in the
+same line.  `roofline` is for the FP16 kernel; `traffic`
 comes from a stored rocprofv3 counter summary and is null when the kernel
 source changed after the counters were taken.  `cpu_baseline` times the CPU
 oracle on a bounded column sample of the same workload.
@@ -72,7 +74,15 @@ def source_file(kind: str) -> str:
 
 
 def source_hash(kind: str = "f16") -> str:
-    return hashlib.sha256(open(source_file(kind), "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments, blank lines and trailing blanks
+    are dropped first, so a documentation-only edit keeps stored counters valid."""
+    import re
+
+    text = open(source_file(kind)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    code = "\n".join(ln for ln in lines if ln)
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def algorithmic_bytes(w) -> int:
@@ -249,7 +259,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", action="append", default=None,
                     help="workload names (default: f16_4096, f8_8192, "
-                         "attn_64x4096x4096x128 and f16_2048)")
+                         "attn_64x4096x4096x128, f16_2048 and the NN/TT/NT 4096^3 layouts)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (a known-size kernel for "
@@ -278,7 +288,8 @@ def main():
     from dense_gemm_tn_amd import inputs
 
     dev = torch.device("cuda:0")
-    names = args.workload or ["f16_4096", "f8_8192", "attn_64x4096x4096x128", "f16_2048"]
+    names = args.workload or ["f16_4096", "f8_8192", "attn_64x4096x4096x128", "f16_2048",
+                              "f16_nn_4096", "f16_tt_4096", "f16_nt_4096"]
     head = "f16_4096" if "f16_4096" in names else names[0]
     results = {}
     keep = {}

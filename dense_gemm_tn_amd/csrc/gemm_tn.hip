@@ -44,6 +44,16 @@
 // gemm_tn_skinny_kernel (K * es <= 256 bytes, e.g. QK^T with head dim 128):
 //   all of K fits one LDS row, so there is no K pipeline; blocks walk a column
 //   of 128 x 128 tiles with B's strip resident, bound by writing C.
+//
+// gemm_tn_mid_kernel: 128 x 128 tiles, two blocks per CU, for grids the
+//   256-wide tiles cannot fill; a host selector picks the configuration.
+//
+// Other op-code layouts (fp16, gemm_f16): the 256 x 256 and 128 x 128 kernels
+//   take template flags AMN / BMN for an M- or N-contiguous operand, staged in
+//   LDS as it lies (K-rows of the tile's columns) and turned into MFMA operand
+//   fragments by gfx950's transposing LDS read, so data in those layouts needs
+//   no transpose pass ("FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4",
+//   section "What we compute", notes real data may otherwise need one).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
