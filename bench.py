@@ -18,8 +18,9 @@ FP8 8192^3 workload, the fused attention forward over 64 heads x 4096 queries x
 4096 keys x head dim 128 (4*M*N*D flops per head: two products), FP16 2048^3
 (a grid the 256-wide tiles cannot fill, served by the 128 x 128 kernel), FP16
 4096^3 in the NN, TT and NT op codes (operands read as they lie, no transpose
-pass), and any other requested workload are reported under "workloads" in the
-same line.  `roofline` is for the FP16 kernel; `traffic`
+pass), the 8-wave ping-pong kernel forced on the FP16 4096^3 and FP8 8192^3
+problems (a measured counter-design), and any other requested workload are
+reported under "workloads" in the same line.  `roofline` is for the FP16 kernel; `traffic`
 comes from a stored rocprofv3 counter summary and is null when the kernel
 source changed after the counters were taken.  `cpu_baseline` times the CPU
 oracle on a bounded column sample of the same workload.
@@ -61,7 +62,8 @@ def kernel_name(w):
     return {0: "gemm_tn_kernel<%d, 8, false, false>" % kind,
             1: "gemm_tn_kernel<%d, 7, false, false>" % kind,
             2: "gemm_tn_mid_kernel<%d, false, false>" % kind,
-            3: "gemm_tn_skinny_kernel<%d>" % kind}[cfg]
+            3: "gemm_tn_skinny_kernel<%d>" % kind,
+            4: "gemm_tn_pp_kernel<%d>" % kind}[cfg]
 
 
 CSRC = os.path.join(ROOT, "dense_gemm_tn_amd", "csrc")
@@ -259,7 +261,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", action="append", default=None,
                     help="workload names (default: f16_4096, f8_8192, "
-                         "attn_64x4096x4096x128, f16_2048 and the NN/TT/NT 4096^3 layouts)")
+                         "attn_64x4096x4096x128, f16_2048, the NN/TT/NT 4096^3 layouts and the "
+                         "ping-pong kernel on f16_4096 and f8_8192)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (a known-size kernel for "
@@ -289,13 +292,25 @@ def main():
 
     dev = torch.device("cuda:0")
     names = args.workload or ["f16_4096", "f8_8192", "attn_64x4096x4096x128", "f16_2048",
-                              "f16_nn_4096", "f16_tt_4096", "f16_nt_4096"]
+                              "f16_nn_4096", "f16_tt_4096", "f16_nt_4096",
+                              "f16_4096_pingpong", "f8_8192_pingpong"]
     head = "f16_4096" if "f16_4096" in names else names[0]
     results = {}
     keep = {}
     for name in names:
         w = inputs.WORKLOADS[name]
+        # A workload may force a tile configuration (the library reads
+        # DG_GEMM_TILE on every call); it is set only while that workload runs.
+        saved = os.environ.pop("DG_GEMM_TILE", None)
+        if "tile" in w.extra:
+            os.environ["DG_GEMM_TILE"] = w.extra["tile"]
+        elif saved is not None:
+            os.environ["DG_GEMM_TILE"] = saved
         res, x, sets = time_workload(w, args.steps, args.warmup, dev)
+        kname = kernel_name(w)
+        os.environ.pop("DG_GEMM_TILE", None)
+        if saved is not None:
+            os.environ["DG_GEMM_TILE"] = saved
         kernel_s = res["ms_per_step"] / 1e3
         tb = traffic_for(name, w, kernel_s)
         res["roofline"] = {
@@ -304,7 +319,7 @@ def main():
             "peak": HBM_PEAK_GBS if w.kind == "qkt" else PEAK_TFLOPS[w.kind],
             "unit": "GB/s" if w.kind == "qkt" else "TFLOP/s",
             "traffic": tb,
-            "kernel": kernel_name(w),
+            "kernel": kname,
         }
         r = res["roofline"]
         r["frac"] = r["achieved"] / r["peak"]

@@ -158,7 +158,8 @@ def block_tile() -> int:
     return lib().gemm_block_tile()
 
 
-CONFIG_NAMES = {0: "256x256", 1: "256x224", 2: "128x128", 3: "skinny-K"}
+CONFIG_NAMES = {0: "256x256", 1: "256x224", 2: "128x128", 3: "skinny-K",
+                4: "256x256 8-wave ping-pong"}
 
 
 def tn_config(M: int, N: int, K: int, batch: int = 1, fp8: bool = False) -> int:

@@ -1281,9 +1281,237 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// gemm_tn_pp_kernel<KIND>: the 8-wave "ping-pong" form of the 256 x 256 tile
+// (the alternative the MI355X FP8 GEMM page weighs against its 4-wave design
+// and rejects for register budget and compiler sensitivity), built here to
+// measure that choice on this hardware.
+//   * 512 threads = 8 waves, two per SIMD; waves 4g .. 4g+3 form group g and
+//     own the 128-column half g of the tile, wave w the 64-row band w % 4:
+//     4 x 8 MFMA tiles of 16 x 16 per wave (128 accumulators in AGPRs; the
+//     other 128 registers of the wave's half of the register file hold one
+//     K-step of fragments and addresses -- no room to double-buffer them).
+//   * The two groups alternate: while one group's waves run the products of
+//     a K-step, the other group's waves read their fragments of the next step
+//     from LDS (and group 0 also issues the copies), so each SIMD's matrix
+//     core is fed by one wave while the other waits on memory.  Phase p ends
+//     with a barrier of all 8 waves; group 0 reads step t in phase 2t and
+//     multiplies it in 2t + 1, group 1 one phase later.  Both groups run one
+//     loop body; group 1 is delayed by one extra barrier.
+//   * Group 0 issues the copies of step t + 1 in phase 2t (all 64 loads, 16
+//     per wave: the 4-wave kernel's copy geometry) into the stage freed by the
+//     barrier that ended phase 2t - 1, and waits for them before the barrier
+//     that ends phase 2t + 1.
+//   * Same LDS layout, swizzle and fragment map as the 4-wave kernel; the
+//     epilogue goes through LDS (16 KiB per wave) with 16-byte stores.
+constexpr int kPpThreads = 512;
+constexpr int kPpWaveM = 64;     // rows per wave
+constexpr int kPpWaveN = 128;    // columns per wave
+
+// Epilogue of a 64 x 128 wave tile through the wave's 16 KiB of LDS: column n
+// at n * 128 B, its 16-byte chunk c (8 rows) in slot c ^ (n & 7); read back as
+// 8 rows per lane, eight 128-byte column segments per store instruction.
+template <int KIND>
+__device__ __forceinline__ void store_c_pp(const Params &p, uint8_t *Cb,
+                                           const float4_t_v (&acc)[4][8],
+                                           __attribute__((address_space(3))) uint8_t *buf,
+                                           int64_t m_base, int64_t n_base, int lane) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) u32x2 lds_u2;
+  typedef __attribute__((address_space(3))) u32x4 lds_u4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int n = 16 * j + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 16 * i + 4 * (lane >> 4);
+      uint32_t w0, w1;
+      pack_run<KIND>(p, acc[i][j], 0, w0, w1);
+      u32x2 w;
+      w.x = w0;
+      w.y = w1;
+      *(lds_u2 *)(buf + n * 128 + (((m >> 3) ^ (n & 7)) * 16) + (m & 7) * 2) = w;
+    }
+  }
+  const bool full = (m_base + kPpWaveM <= p.M) && (n_base + kPpWaveN <= p.N);
+#pragma unroll
+  for (int r = 0; r < kPpWaveN / 8; ++r) {
+    const int n = 8 * r + (lane >> 3);
+    const int mc = lane & 7;
+    const u32x4 v = *(lds_u4 *)(buf + n * 128 + ((mc ^ (n & 7)) * 16));
+    const int64_t gm = m_base + 8 * mc, gn = n_base + n;
+    uint16_t *dst = (uint16_t *)Cb + (gn * p.ldc + gm);
+    if (full || (gn < p.N && gm + 7 < p.M)) {
+      __builtin_nontemporal_store(v, (u32x4 *)dst);
+    } else if (gn < p.N) {
+      const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (gm + e < p.M) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kPpThreads, 1) void gemm_tn_pp_kernel(Params p) {
+  typedef Traits<KIND> T;
+  typedef typename T::frag_t frag_t;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * 2 * kStageBytes];
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wm = wave & 3;
+
+  int head, tm, tn;
+  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
+  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+  const uint8_t *Ab = p.A + head * p.stride_a_b + m0 * p.lda_b;
+  const uint8_t *Bb = p.B + head * p.stride_b_b + n0 * p.ldb_b;
+  uint8_t *Cb = p.C + head * p.stride_c_b;
+  const int64_t rows_a = (p.M - m0) < kTile ? (p.M - m0) : kTile;
+  const int64_t rows_b = (p.N - n0) < kTile ? (p.N - n0) : kTile;
+  const uint32_t kbytes = (uint32_t)(p.K * T::es);
+  const uint32_t rec_a = (uint32_t)((rows_a - 1) * p.lda_b) + kbytes;
+  const uint32_t rec_b = (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes;
+  const int64_t nk = (p.K + T::kstep - 1) / T::kstep;
+
+  // Copies (group 0 only): wave wm's share of the 4-wave kernel's geometry.
+  const int crow = 8 * wm + (lane >> 3);
+  const int gchunk = (lane & 7) ^ ((crow >> 1) & 7);
+  const uint32_t voff_a = (uint32_t)(crow * p.lda_b) + gchunk * 16;
+  const uint32_t voff_b = (uint32_t)(crow * p.ldb_b) + gchunk * 16;
+  const uint32_t qs_a = (uint32_t)(32 * p.lda_b), qs_b = (uint32_t)(32 * p.ldb_b);
+  const int kchunk = gchunk * (16 / T::es);
+  auto copy_step = [&](int64_t t) {
+    const int64_t k0 = t * T::kstep;
+    const int64_t rem = p.K - k0;
+    const int left = rem >= T::kstep ? T::kstep : (int)rem;
+    const uint32_t kb = (uint32_t)(k0 * T::es);
+    StepCopy c;
+    c.ra = make_rsrc(Ab + kb, rec_a - kb);
+    c.rb = make_rsrc(Bb + kb, rec_b - kb);
+    lds_u8 *st = (lds_u8 *)smem + (int)(t & 1) * 2 * kStageBytes + wm * 1024;
+    c.la = st;
+    c.lb = st + kStageBytes;
+    const bool valid = kchunk < left;
+    c.va = valid ? voff_a : kOob;
+    c.vb = valid ? voff_b : kOob;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) copy_one<false, false>(c, d, qs_a, qs_b);
+  };
+
+  // Fragments: lane l reads row l % 16 of a 16-row tile (as in the 4-wave
+  // kernel); A tiles of the wave's 64-row band, B tiles of its 128 columns.
+  const int rl = lane & 15, kg = lane >> 4;
+  uint32_t a_off[4], b_off[4];
+#pragma unroll
+  for (int x = 0; x < T::subs * T::reads; ++x) {
+    const int chunk = (x / T::reads) * (8 / T::subs) + kg + 4 * (x % T::reads);
+    const uint32_t lo = (uint32_t)(rl * kRowBytes + ((chunk ^ ((rl >> 1) & 7)) * 16));
+    a_off[x] = lo + wm * kPpWaveM * kRowBytes;
+    b_off[x] = lo + kStageBytes + grp * kPpWaveN * kRowBytes;
+  }
+  constexpr int kTileBytes = 16 * kRowBytes;
+
+  float4_t_v acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = float4_t_v{0.f, 0.f, 0.f, 0.f};
+  frag_t fa[T::subs][4], fb[T::subs][8];
+
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // Read all fragments of step t; they are complete (lgkmcnt 0) before the
+  // phase's barrier, so the stage may be refilled right after the next one.
+  auto mem_phase = [&](int64_t t) {
+    lds_cptr st = (lds_cptr)smem + (int)(t & 1) * 2 * kStageBytes;
+#pragma unroll
+    for (int s = 0; s < T::subs; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[s][i] = read_frag<KIND>(st + i * kTileBytes, a_off, s);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fb[s][j] = read_frag<KIND>(st + j * kTileBytes, b_off, s);
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & 0xC0FF);  // lgkmcnt(0)
+  };
+  auto compute_phase = [&]() {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < T::subs; ++s)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = mma(fa[s][i], fb[s][j], acc[i][j]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // Prologue: step 0's copies, landed and published.  Then both groups run
+  // the same loop -- read step t, barrier, multiply step t, barrier -- group 1
+  // one barrier behind group 0 (an extra barrier before its loop, matched by
+  // one after group 0's), so one group's reads overlap the other's products.
+  if (grp == 0 && nk > 0) copy_step(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+  if (grp == 1) barrier();
+  for (int64_t t = 0; t < nk; ++t) {
+    if (grp == 0 && t + 1 < nk) copy_step(t + 1);
+    mem_phase(t);
+    __builtin_amdgcn_sched_barrier(0);
+    barrier();
+    compute_phase();
+    // Group 0's copies of step t + 1 have landed before the barrier that lets
+    // either group read them.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_sched_barrier(0);
+    barrier();
+  }
+  if (grp == 0) barrier();
+  mfma_drain();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const int64_t mb = m0 + wm * kPpWaveM, nb = n0 + grp * kPpWaveN;
+  if (p.c_vec16_ok) {
+    store_c_pp<KIND>(p, Cb, acc, (lds_u8 *)smem + wave * 16384, mb, nb, lane);
+  } else {
+    // Runs of four rows, 8-byte or 2-byte stores.
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = nb + 16 * j + rl;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = mb + 16 * i + 4 * kg;
+        uint32_t w0, w1;
+        pack_run<KIND>(p, acc[i][j], 0, w0, w1);
+        uint16_t *dst = (uint16_t *)Cb + (n * p.ldc + m);
+        if (p.c_vec_ok && m + 3 < p.M) {
+          *(uint2 *)dst = uint2{w0, w1};
+        } else {
+          const uint16_t h[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1,
+                                 (uint16_t)(w1 >> 16)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (m + e < p.M) dst[e] = h[e];
+        }
+      }
+    }
+  }
+}
+
 // Kernel configuration of a problem (the codes are the C ABI's
 // gemm_tn_config values).
-enum { kCfg256 = 0, kCfg224 = 1, kCfgMid = 2, kCfgSkinny = 3 };
+enum { kCfg256 = 0, kCfg224 = 1, kCfgMid = 2, kCfgSkinny = 3, kCfgPingPong = 4 };
 struct Config {
   int kind;
 };
@@ -1307,6 +1535,7 @@ static Config choose_config(int es, int64_t M, int64_t N, int64_t K, int64_t bat
     if (!strcmp(force, "256")) return Config{kCfg256};
     if (!strcmp(force, "224")) return Config{tn ? kCfg224 : kCfg256};
     if (!strcmp(force, "128")) return Config{kCfgMid};
+    if (!strcmp(force, "pingpong") && tn) return Config{kCfgPingPong};
   }
   const int64_t cus = cu_count();
   const int64_t tm = (M + kTile - 1) / kTile;
@@ -1359,6 +1588,7 @@ static int launch(const Problem &pr, hipStream_t stream) {
 
   const Config cfg = choose_config(es, pr.M, pr.N, pr.K, pr.batch);
   const bool skinny = cfg.kind == kCfgSkinny, mid = cfg.kind == kCfgMid;
+  const bool pp = cfg.kind == kCfgPingPong;
   const int ntn = cfg.kind == kCfg224 ? 7 : 8;
   const int64_t tile_m = skinny ? kSkTile : mid ? kMidTile : kTile;
   const int64_t tile_n = skinny ? kSkTile : mid ? kMidTile : 32 * ntn;
@@ -1391,6 +1621,9 @@ static int launch(const Problem &pr, hipStream_t stream) {
 
   if (skinny)
     hipLaunchKernelGGL(gemm_tn_skinny_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, p);
+  else if (pp)
+    hipLaunchKernelGGL(gemm_tn_pp_kernel<KIND>, dim3((unsigned)blocks), dim3(kPpThreads), 0,
                        stream, p);
   else if (mid)
     hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false>), dim3((unsigned)blocks), dim3(kThreads), 0,

@@ -64,6 +64,12 @@ WORKLOADS = {
                  extra={"layout": "TT"}),
         Workload("f16_nt_4096", "f16", 4096, 4096, 4096, "normal", seed=0,
                  extra={"layout": "NT"}),
+        # The 8-wave ping-pong form of the 256 x 256 tile, forced (a measured
+        # counter-design; the library never picks it by itself).
+        Workload("f16_4096_pingpong", "f16", 4096, 4096, 4096, "normal", seed=0,
+                 extra={"tile": "pingpong"}),
+        Workload("f8_8192_pingpong", "f8", 8192, 8192, 8192, "normal", seed=0,
+                 extra={"tile": "pingpong"}),
         Workload("qkt_64x4096x4096x128", "qkt", 4096, 4096, 128, "normal", seed=0, batch=64,
                  std=1.0 / math.sqrt(128.0)),
         Workload("attn_64x4096x4096x128", "attn", 4096, 4096, 128, "normal", seed=0, batch=64),

@@ -198,10 +198,15 @@ int gemm_block_tile(void);
  *   1  256 x 224 tiles (fewer rounds of one block per CU for some widths);
  *   2  128 x 128 tiles, two blocks per CU (grids the wide tiles leave idle);
  *   3  the skinny-K kernel (K * element bytes <= 256);
+ *   4  256 x 256 tiles computed by 8 waves in two groups that alternate
+ *      between reading fragments and multiplying ("ping-pong"; the design the
+ *      "AMD ROCm 4-wave interleave FP8 GEMM for Instinct MI355X (CDNA 4)" page
+ *      weighs against its 4-wave one); only chosen when forced;
  *  -1  negative sizes.
  * The choice is a pure function of the sizes and the device's CU count.  For
- * measurement and tests, the environment variable DG_GEMM_TILE = 256, 224 or
- * 128 forces configuration 0, 1 or 2 for every non-skinny problem.
+ * measurement and tests, the environment variable DG_GEMM_TILE = 256, 224,
+ * 128 or pingpong forces configuration 0, 1, 2 or 4 for every non-skinny
+ * problem.
  */
 int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch);
 

@@ -140,6 +140,9 @@ def test_f16_layout_selector(monkeypatch):
     monkeypatch.setenv("DG_GEMM_TILE", "224")
     assert dg.f16_config("N", "N", 512, 512, 512) == 0
     assert dg.f16_config("T", "N", 512, 512, 512) == 1
+    monkeypatch.setenv("DG_GEMM_TILE", "pingpong")     # TN only: layouts keep their choice
+    assert dg.f16_config("N", "N", 4096, 4096, 4096) == 0
+    assert dg.f16_config("T", "N", 4096, 4096, 4096) == 4
 
 
 def test_f16_binding_rejects_bad_codes():
@@ -260,7 +263,7 @@ def test_tile_config_selector(M, N, K, batch, fp8, want, monkeypatch):
 
 
 def test_tile_config_override(monkeypatch):
-    for force, code in (("256", 0), ("224", 1), ("128", 2)):
+    for force, code in (("256", 0), ("224", 1), ("128", 2), ("pingpong", 4)):
         monkeypatch.setenv("DG_GEMM_TILE", force)
         assert dg.tn_config(2048, 2048, 2048) == code
         assert dg.tn_config(4096, 4096, 128, 64) == 3   # skinny-K is never forced

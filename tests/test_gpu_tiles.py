@@ -25,7 +25,7 @@ SHAPES16 = [(1, 1, 136), (3, 5, 136), (31, 33, 264), (129, 131, 136), (257, 255,
             (300, 290, 200), (513, 260, 1000), (64, 700, 3976), (700, 64, 392)]
 SHAPES8 = [(1, 1, 272), (3, 5, 272), (31, 33, 528), (129, 131, 272), (257, 255, 1040),
            (513, 260, 400), (300, 290, 3856)]
-FORCED = [("256", 0), ("224", 1), ("128", 2)]
+FORCED = [("256", 0), ("224", 1), ("128", 2), ("pingpong", 4)]
 
 
 @pytest.fixture
@@ -60,7 +60,7 @@ def test_forced_tile_padding_and_odd_ldc(force, tile, code, kind):
     assert_exact(kind, got, reference(kind, x, M, N, K))
 
 
-@pytest.mark.parametrize("tile", ["256", "128"])
+@pytest.mark.parametrize("tile", ["256", "128", "pingpong"])
 def test_forced_tile_normal_data(force, tile):
     force(tile)
     M, N, K = 520, 390, 1544
