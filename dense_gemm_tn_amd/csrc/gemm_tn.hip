@@ -673,7 +673,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   constexpr int kWin = kWin0 < kAfter + kBarQ ? kWin0 : kAfter + kBarQ;
   static_assert(kWin >= kCopies && kWin - kAfter <= kBarQ, "copy window");
   auto first_copy = [](int x) { return (x * kCopies + kWin - 1) / kWin; };
-  constexpr int kPost = (kAfter * kCopies + kWin - 1) / kWin;  // first_copy(kAfter)
+  // Copies of step t + 1 already issued in step t - 1's window: all of them
+  // when that window ends inside step t - 1 (fp8), else first_copy(kAfter).
+  constexpr int kPost0 = (kAfter * kCopies + kWin - 1) / kWin;
+  constexpr int kPost = kPost0 < kCopies ? kPost0 : kCopies;
   frag_t fa[8], fx, fb[2][NTN];
   if (nk2 > 0) {
     // Copies of all of step 0 and the first kPost of step 1; wait for step 0
