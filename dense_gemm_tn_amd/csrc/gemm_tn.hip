@@ -5,8 +5,8 @@
 // RDNA 3 and RDNA 4", section "What we compute", and the dot-product equation of
 // "hello-gpu, chapter 11 (GEMM-like)", section 11.1.
 //
-// Kernel design.  Two kernel families, each with fp16 and fp8 instantiations
-// and an optional head index:
+// Kernel design.  Four kernels, each with fp16 and fp8 instantiations and an
+// optional head index; a host selector picks one per problem:
 //
 // gemm_tn_kernel (K * es > 256 bytes):
 //   * 256 x 256 output tile per workgroup, 4 waves (one per SIMD), each wave owns
@@ -46,7 +46,12 @@
 //   of 128 x 128 tiles with B's strip resident, bound by writing C.
 //
 // gemm_tn_mid_kernel: 128 x 128 tiles, two blocks per CU, for grids the
-//   256-wide tiles cannot fill; a host selector picks the configuration.
+//   256-wide tiles cannot fill.
+//
+// gemm_tn_pp_kernel: the 256 x 256 tile computed by 8 waves in two groups that
+//   alternate between fragment reads and products (the "ping-pong" design the
+//   MI355X FP8 GEMM page weighs against its 4-wave one); measured slower here,
+//   so only used when forced.
 //
 // Other op-code layouts (fp16, gemm_f16): the 256 x 256 and 128 x 128 kernels
 //   take template flags AMN / BMN for an M- or N-contiguous operand, staged in
