@@ -17,8 +17,8 @@ Prints ONE JSON line.  The headline `value` is the FP16 TN 4096^3 workload; the
 FP8 8192^3 workload, the fused attention forward over 64 heads x 4096 queries x
 4096 keys x head dim 128 (4*M*N*D flops per head: two products), FP16 2048^3
 (a grid the 256-wide tiles cannot fill, served by the 128 x 128 kernel), FP16
-4096^3 in the NN, TT and NT op codes (operands read as they lie, no transpose
-pass), the 8-wave ping-pong kernel forced on the FP16 4096^3 and FP8 8192^3
+4096^3 and FP8 8192^3 in the NN, TT and NT op codes (operands read as they lie,
+no transpose pass), the 8-wave ping-pong kernel forced on the FP16 4096^3 and FP8 8192^3
 problems (a measured counter-design), and any other requested workload are
 reported under "workloads" in the same line.  `roofline` is for the FP16 kernel; `traffic`
 comes from a stored rocprofv3 counter summary and is null when the kernel
@@ -55,9 +55,10 @@ def kernel_name(w):
     if layout != "TN":
         amn = "true" if layout[0] == "N" else "false"
         bmn = "true" if layout[1] == "T" else "false"
-        if dg.f16_config(layout[0], layout[1], w.M, w.N, w.K) == 2:
-            return "gemm_tn_mid_kernel<0, %s, %s>" % (amn, bmn)
-        return "gemm_tn_kernel<0, 8, %s, %s>" % (amn, bmn)
+        cfg_of = dg.f8_config if w.kind == "f8" else dg.f16_config
+        if cfg_of(layout[0], layout[1], w.M, w.N, w.K) == 2:
+            return "gemm_tn_mid_kernel<%d, %s, %s>" % (kind, amn, bmn)
+        return "gemm_tn_kernel<%d, 8, %s, %s>" % (kind, amn, bmn)
     cfg = dg.tn_config(w.M, w.N, w.K, w.batch, fp8=(w.kind == "f8"))
     return {0: "gemm_tn_kernel<%d, 8, false, false>" % kind,
             1: "gemm_tn_kernel<%d, 7, false, false>" % kind,
@@ -150,6 +151,9 @@ def make_launcher(w, dev):
                         w.M)
         elif w.kind == "f16":
             dg.gemm_f16_tn(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M)
+        elif w.kind == "f8" and layout != "TN":
+            dg.gemm_f8(layout[0], layout[1], a, b, c, w.M, w.N, w.K, a.stride(0), b.stride(0),
+                       w.M, x["scale_a"], x["scale_b"])
         elif w.kind == "f8":
             dg.gemm_f8_tn(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M, x["scale_a"], x["scale_b"])
         else:
@@ -261,8 +265,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", action="append", default=None,
                     help="workload names (default: f16_4096, f8_8192, "
-                         "attn_64x4096x4096x128, f16_2048, the NN/TT/NT 4096^3 layouts and the "
-                         "ping-pong kernel on f16_4096 and f8_8192)")
+                         "attn_64x4096x4096x128, f16_2048, the NN/TT/NT layouts of f16_4096 "
+                         "and f8_8192, and the ping-pong kernel on both)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (a known-size kernel for "
@@ -293,6 +297,7 @@ def main():
     dev = torch.device("cuda:0")
     names = args.workload or ["f16_4096", "f8_8192", "attn_64x4096x4096x128", "f16_2048",
                               "f16_nn_4096", "f16_tt_4096", "f16_nt_4096",
+                              "f8_nn_8192", "f8_tt_8192", "f8_nt_8192",
                               "f16_4096_pingpong", "f8_8192_pingpong"]
     head = "f16_4096" if "f16_4096" in names else names[0]
     results = {}

@@ -34,6 +34,8 @@ EXPORTS = (
     "gemm_block_tile",
     "gemm_tn_config",
     "gemm_f16_config",
+    "gemm_f8",
+    "gemm_f8_config",
 )
 
 _lib = None
@@ -67,8 +69,12 @@ def lib() -> ctypes.CDLL:
         L.gemm_block_tile.argtypes = []
         L.gemm_tn_config.argtypes = [ctypes.c_int, i64, i64, i64, i64]
         L.gemm_f16_config.argtypes = [ctypes.c_char, ctypes.c_char, i64, i64, i64]
+        L.gemm_f8.argtypes = [ctypes.c_char, ctypes.c_char, vp, vp, vp, i64, i64, i64, i64, i64,
+                              i64, f32, f32, vp]
+        L.gemm_f8_config.argtypes = [ctypes.c_char, ctypes.c_char, i64, i64, i64]
         for f in (L.gemm_f16_tn, L.gemm_f16, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
-                  L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config, L.gemm_f16_config):
+                  L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config, L.gemm_f16_config,
+                  L.gemm_f8, L.gemm_f8_config):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -117,6 +123,17 @@ def gemm_f16(transa: str, transb: str, A, B, C, M: int, N: int, K: int, lda: int
         raise ValueError("op codes are 'T' or 'N'")
     _check("gemm_f16", lib().gemm_f16(transa.encode(), transb.encode(), _ptr(A), _ptr(B), _ptr(C),
                                       M, N, K, lda, ldb, ldc, _stream(stream)))
+
+
+def gemm_f8(transa: str, transb: str, A, B, C, M: int, N: int, K: int, lda: int, ldb: int,
+            ldc: int, scale_a: float, scale_b: float, stream=None) -> None:
+    """bf16 C = fp32(scale_a*scale_b) * op(A) op(B) with E4M3FN A, B in any op-code layout
+    (the index conventions of gemm_f16)."""
+    if transa not in "TtNn" or transb not in "TtNn" or len(transa) != 1 or len(transb) != 1:
+        raise ValueError("op codes are 'T' or 'N'")
+    _check("gemm_f8", lib().gemm_f8(transa.encode(), transb.encode(), _ptr(A), _ptr(B), _ptr(C),
+                                    M, N, K, lda, ldb, ldc, float(scale_a), float(scale_b),
+                                    _stream(stream)))
 
 
 def gemm_f8_tn(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
@@ -170,6 +187,11 @@ def tn_config(M: int, N: int, K: int, batch: int = 1, fp8: bool = False) -> int:
 def f16_config(transa: str, transb: str, M: int, N: int, K: int) -> int:
     """Kernel configuration gemm_f16 chooses for a layout (see gemm_f16_config)."""
     return lib().gemm_f16_config(transa.encode(), transb.encode(), M, N, K)
+
+
+def f8_config(transa: str, transb: str, M: int, N: int, K: int) -> int:
+    """Kernel configuration gemm_f8 chooses for a layout (see gemm_f8_config)."""
+    return lib().gemm_f8_config(transa.encode(), transb.encode(), M, N, K)
 
 
 # ----------------------------------------------------------- tensor helpers

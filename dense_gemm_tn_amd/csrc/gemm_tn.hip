@@ -247,61 +247,80 @@ __device__ __forceinline__ void dma16(const v4u32 &r, uint32_t voff, uint32_t ld
                :: "v"(voff), "s"(r), "{m0}"(lds) : "memory");
 }
 
-// M/N-contiguous fp16 operands of the 256 x 256 kernel (A of an 'N' op, B of
-// a 'T' op) are staged as they lie: a stage strip is 64 K-rows of 256
-// elements (512 B), the 16-byte chunk c of K-row k in slot c ^ mn_key(k).
-// Load q of wave w fills K-rows mn_wave_row(w) + mn_load_row(q) + {0, 1}
-// (lanes 0..31 the first, 32..63 the second): w supplies row bits 1 and 3, q
-// bits 2, 4 and 5, so a lane's key is the same for all eight of its loads.
-__host__ __device__ constexpr int mn_key(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
-__host__ __device__ constexpr int mn_wave_row(int w) { return 2 * (w & 1) + 8 * (w >> 1); }
-__host__ __device__ constexpr int mn_load_row(int q) {
-  return 4 * (q & 1) + 16 * ((q >> 1) & 1) + 32 * (q >> 2);
-}
-constexpr int kMnRowBytes = 512;
+// M/N-contiguous operands of the 256 x 256 kernel (A of an 'N' op, B of a 'T'
+// op) are staged as they lie: a stage strip is T::kstep K-rows of the block's
+// 256 columns (fp16: 64 K-rows of 512 B; fp8: 128 K-rows of 256 B), the
+// 16-byte chunk c of K-row k in slot c ^ Mn::key(k).  Each 1 KiB load fills
+// Mn::rows_per_load consecutive K-rows (lane l: row l / (64 / rows_per_load),
+// slot l % (64 / rows_per_load)); load q of wave w starts at K-row
+// Mn::wave_row(w) + Mn::load_row(q).  The wave supplies the row bits the key
+// uses beyond the lane's own, so a lane's key is the same for all its loads.
+// The key spreads the K-rows one transposing read phase touches (32 lanes)
+// over distinct 16-byte bank groups.
+template <int KIND> struct Mn;
+template <> struct Mn<kF16> {
+  static constexpr int row_bytes = 512;
+  static constexpr int rows_per_load = 2;
+  __host__ __device__ static constexpr int key(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+  __host__ __device__ static constexpr int wave_row(int w) { return 2 * (w & 1) + 8 * (w >> 1); }
+  __host__ __device__ static constexpr int load_row(int q) {
+    return 4 * (q & 1) + 16 * ((q >> 1) & 1) + 32 * (q >> 2);
+  }
+};
+template <> struct Mn<kF8> {
+  static constexpr int row_bytes = 256;
+  static constexpr int rows_per_load = 4;
+  __host__ __device__ static constexpr int key(int k) { return (k & 7) + 8 * ((k >> 4) & 1); }
+  __host__ __device__ static constexpr int wave_row(int w) { return 4 * (w & 1) + 16 * (w >> 1); }
+  __host__ __device__ static constexpr int load_row(int q) { return 8 * (q & 1) + 32 * (q >> 1); }
+};
+constexpr int kMnRowBytes = Mn<kF16>::row_bytes;
 
 // Issue copy d of a step: d < 8 is load q = d of A, else load q = d - 8 of B.
 // K-contiguous operands: load q is 32 rows further (q_stride = 32 rows).
-// M/N-contiguous ones: load q starts mn_load_row(q) K-rows further
+// M/N-contiguous ones: load q starts Mn::load_row(q) K-rows further
 // (q_stride = one K-row).
-template <bool AMN, bool BMN>
+template <bool AMN, bool BMN, int KIND = kF16>
 __device__ __forceinline__ void copy_one(const StepCopy &c, int d, uint32_t qs_a, uint32_t qs_b) {
+  typedef Mn<KIND> G;
   if (d < 8) {
-    const int lds_off = AMN ? mn_load_row(d) * kMnRowBytes : d * 4096;
-    const uint32_t step = (uint32_t)(AMN ? mn_load_row(d) : d) * qs_a;
+    const int lds_off = AMN ? G::load_row(d) * G::row_bytes : d * 4096;
+    const uint32_t step = (uint32_t)(AMN ? G::load_row(d) : d) * qs_a;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, (lds_void_t *)(c.la + lds_off), 16,
                                              c.va + step, 0, 0, 0);
   } else {
     const int q = d - 8;
-    const int lds_off = BMN ? mn_load_row(q) * kMnRowBytes : q * 4096;
-    const uint32_t step = (uint32_t)(BMN ? mn_load_row(q) : q) * qs_b;
+    const int lds_off = BMN ? G::load_row(q) * G::row_bytes : q * 4096;
+    const uint32_t step = (uint32_t)(BMN ? G::load_row(q) : q) * qs_b;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, (lds_void_t *)(c.lb + lds_off), 16,
                                              c.vb + step, 0, 0, 0);
   }
 }
 
-template <bool AMN, bool BMN>
+template <bool AMN, bool BMN, int KIND = kF16>
 __device__ __forceinline__ void copy_one(const StepCopyAsm &c, int d, uint32_t qs_a,
                                          uint32_t qs_b) {
+  typedef Mn<KIND> G;
   if (d < 8) {
-    const int lds_off = AMN ? mn_load_row(d) * kMnRowBytes : d * 4096;
-    dma16(c.ra, c.va + (uint32_t)(AMN ? mn_load_row(d) : d) * qs_a, c.la + lds_off);
+    const int lds_off = AMN ? G::load_row(d) * G::row_bytes : d * 4096;
+    dma16(c.ra, c.va + (uint32_t)(AMN ? G::load_row(d) : d) * qs_a, c.la + lds_off);
   } else {
     const int q = d - 8;
-    const int lds_off = BMN ? mn_load_row(q) * kMnRowBytes : q * 4096;
-    dma16(c.rb, c.vb + (uint32_t)(BMN ? mn_load_row(q) : q) * qs_b, c.lb + lds_off);
+    const int lds_off = BMN ? G::load_row(q) * G::row_bytes : q * 4096;
+    dma16(c.rb, c.vb + (uint32_t)(BMN ? G::load_row(q) : q) * qs_b, c.lb + lds_off);
   }
 }
 
 // Descriptor bytes of an M/N-contiguous operand's K-step starting at K-row k0
-// (rows of ld_b bytes, `cols` elements of the block inside the matrix): all
-// 64 rows while the step is not the last, else up to the block's last element
-// of K-row K - 1, so rows at or past K and columns past the matrix in that
-// row read zero.  Other out-of-matrix columns only feed outputs that are never
-// stored.
+// (rows of ld_b bytes, `cols` elements of es bytes of the block inside the
+// matrix): all `kstep` rows while the step is not the last, else up to the
+// block's last element of K-row K - 1, so rows at or past K and columns past
+// the matrix in that row read zero.  Other out-of-matrix columns only feed
+// outputs that are never stored.
 __device__ __forceinline__ uint32_t mn_records(int64_t K, int64_t k0, int64_t ld_b,
-                                               int64_t cols) {
-  return K - k0 > 64 ? (uint32_t)(64 * ld_b) : (uint32_t)((K - k0 - 1) * ld_b + cols * 2);
+                                               int64_t cols, int kstep, int es) {
+  return K - k0 > kstep ? (uint32_t)(kstep * ld_b)
+                        : (uint32_t)((K - k0 - 1) * ld_b + cols * es);
 }
 
 // An fp16 MFMA operand fragment of an M/N-contiguous strip: lanes 16g .. 16g+15
@@ -315,6 +334,27 @@ __device__ __forceinline__ half8_t mn_frag(lds_cptr strip, uint32_t off, int s) 
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)at);
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(at + 4 * kMnRowBytes));
   return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// An fp8 MFMA operand fragment (32 bytes of K per lane) of an M/N-contiguous
+// strip with rows of `row_bytes`, from four ds_read_b64_tr_b8.  Within each
+// 16-lane group that read gives lane 8a + b byte e from element b of the 8
+// bytes that lane 2e + a addresses (measured), so lanes 2e + a pointing at
+// K-row k0 + e, columns 8a .. 8a+7 of a 16-wide tile leave lane j holding
+// K-rows k0 .. k0+7 of column j.  Lanes 16g .. 16g+15 take K-rows
+// 16g + {0..7, 8..15, 64..71, 72..79}, the K order of the K-contiguous fp8
+// fragment (chunks g and g + 4 of a 128-byte row).  `off` is the lane's
+// swizzled byte offset of its first read.
+template <int ROW_BYTES>
+__device__ __forceinline__ int8_t_v mn_frag8(lds_cptr strip, uint32_t off) {
+  typedef int v2i32 __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+  lds_cptr at = strip + off;
+  const v2i32 r0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)at);
+  const v2i32 r1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(at + 8 * ROW_BYTES));
+  const v2i32 r2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(at + 64 * ROW_BYTES));
+  const v2i32 r3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32 *)(at + 72 * ROW_BYTES));
+  return int8_t_v{r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
 }
 
 // One MFMA operand fragment: 32 rows x (16 fp16 or 64 fp8) of K.  Lane l reads
@@ -480,7 +520,7 @@ static_assert(extra_slot<8>(8) == 25 && extra_slot<7>(0) == 8 && extra_slot<7>(3
 template <int KIND, int NTN, bool AMN, bool BMN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   typedef Traits<KIND> T;
-  static_assert(KIND == kF16 || (!AMN && !BMN), "M/N-contiguous operands are fp16 only");
+  typedef Mn<KIND> G;                    // M/N-contiguous staging geometry
   constexpr int kTileN = 2 * 16 * NTN;   // block tile width (columns of B / C)
   // Two stages of [A strip | B strip], 64 KiB each.
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * 2 * kStageBytes];
@@ -495,8 +535,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
 
   // Block bases: K-contiguous operands at their first row, M/N-contiguous ones
   // at their first column (element m0 / n0 of K-row 0).
-  const uint8_t *Ab = p.A + head * p.stride_a_b + (AMN ? m0 * 2 : m0 * p.lda_b);
-  const uint8_t *Bb = p.B + head * p.stride_b_b + (BMN ? n0 * 2 : n0 * p.ldb_b);
+  const uint8_t *Ab = p.A + head * p.stride_a_b + (AMN ? m0 * T::es : m0 * p.lda_b);
+  const uint8_t *Bb = p.B + head * p.stride_b_b + (BMN ? n0 * T::es : n0 * p.ldb_b);
   uint8_t *Cb = p.C + head * p.stride_c_b;
   const int64_t rows_a = (p.M - m0) < kTile ? (p.M - m0) : kTile;
   const int64_t rows_b = (p.N - n0) < kTileN ? (p.N - n0) : kTileN;
@@ -509,12 +549,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   // the MI355X FP8 GEMM page: a ds_read_b128 phase (16 lanes, 16 consecutive
   // rows, one chunk) covers all 16 slots of the 256-byte bank period.
   // Copy geometry of this lane (same for A and B, see copy_one).
-  // M/N-contiguous copies: K-row mn_wave_row(w) + (l >> 5) (+ mn_load_row(q)),
-  // slot l & 31, fetching the chunk the swizzle keeps there.
+  // M/N-contiguous copies: K-row G::wave_row(w) + l / (64 / rows_per_load)
+  // (+ G::load_row(q)), slot l % (64 / rows_per_load), fetching the chunk the
+  // swizzle keeps there.
   const int crow = 8 * wave + (lane >> 3);            // row within a 32-row band
   const int gchunk = (lane & 7) ^ ((crow >> 1) & 7);  // global 16-B chunk of that row
-  const int mrow = mn_wave_row(wave) + (lane >> 5);
-  const uint32_t mchunk16 = (uint32_t)(((lane & 31) ^ mn_key(mrow)) * 16);
+  constexpr int kLanesPerRow = 64 / G::rows_per_load;
+  const int mrow = G::wave_row(wave) + lane / kLanesPerRow;
+  const uint32_t mchunk16 = (uint32_t)(((lane % kLanesPerRow) ^ G::key(mrow)) * 16);
   const uint32_t voff_a = AMN ? (uint32_t)(mrow * p.lda_b) + mchunk16
                               : (uint32_t)(crow * p.lda_b) + gchunk * 16;
   const uint32_t voff_b = BMN ? (uint32_t)(mrow * p.ldb_b) + mchunk16
@@ -542,26 +584,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     a_off[x] = lo + wm * kWaveTile * kRowBytes;
     b_off[x] = lo + kStageBytes + wn * S::WN * kRowBytes;
   }
-  // M/N-contiguous fragments: lane (rl, grp) reads K-row 8 grp + rl / 4 at
-  // elements 4 (rl % 4) .. +3 of the 16-wide tile whose first chunk is c0, i.e.
-  // slot (c0 + (rl % 4) / 2) ^ key, byte 8 (rl % 2).  c0 is even and the key
-  // only has bits 1..3, so the address is mn_lane ^ (16 c0): one XOR per read.
-  const int mk = 8 * grp + (rl >> 2);
-  const uint32_t mn_lane = (uint32_t)(mk * kMnRowBytes + 16 * mn_key(mk) +
-                                      16 * ((rl & 3) >> 1) + 8 * (rl & 1));
+  // M/N-contiguous fragments.  fp16: lane (rl, grp) reads K-row 8 grp + rl / 4
+  // at elements 4 (rl % 4) .. +3 of the 16-wide tile whose first chunk is c0,
+  // i.e. slot (c0 + (rl % 4) / 2) ^ key, byte 8 (rl % 2); c0 is even and the
+  // key has bits 1..3 only.  fp8: K-row 16 grp + rl / 2 at bytes 8 (rl % 2) ..
+  // +7 of the tile's single chunk c0 (16 columns), slot c0 ^ key.  Either way
+  // the address is mn_lane ^ (16 c0): one XOR per read.
+  const int mk = (KIND == kF16) ? 8 * grp + (rl >> 2) : 16 * grp + (rl >> 1);
+  const uint32_t mn_lane =
+      (KIND == kF16) ? (uint32_t)(mk * G::row_bytes + 16 * G::key(mk) + 16 * ((rl & 3) >> 1) +
+                                  8 * (rl & 1))
+                     : (uint32_t)(mk * G::row_bytes + 16 * G::key(mk) + 8 * (rl & 1));
+  // First chunk of a tile (16 columns) within the strip: 2 chunks per fp16
+  // tile, 1 per fp8 tile.
+  constexpr int kTileChunks = 16 * T::es / 16;
   typedef typename T::frag_t frag_t;
   constexpr int kTileBytes = MT * kRowBytes;      // LDS bytes between MFMA tiles
   // Fragment g of A (16 rows at wave row 16 g) and j of B, sub-step s, from the
   // stage at `st`.
+  auto mn_read = [&](lds_cptr strip, int c0, int s) -> frag_t {
+    const uint32_t off = mn_lane ^ (uint32_t)(16 * c0);
+    if constexpr (KIND == kF16)
+      return mn_frag(strip, off, s);
+    else
+      return mn_frag8<Mn<kF8>::row_bytes>(strip, off);
+  };
   auto frag_a = [&](lds_cptr st, int g, int s) -> frag_t {
     if constexpr (AMN)
-      return mn_frag(st, mn_lane ^ (uint32_t)(16 * (kWaveTile / 8 * wm + 2 * g)), s);
+      return mn_read(st, kTileChunks * (kWaveTile / 16 * wm + g), s);
     else
       return read_frag<KIND>(st + g * kTileBytes, a_off, s);
   };
   auto frag_b = [&](lds_cptr st, int j, int s) -> frag_t {
     if constexpr (BMN)
-      return mn_frag(st + kStageBytes, mn_lane ^ (uint32_t)(16 * (S::WN / 8 * wn + 2 * j)), s);
+      return mn_read(st + kStageBytes, kTileChunks * (S::WN / 16 * wn + j), s);
     else
       return read_frag<KIND>(st + j * kTileBytes, b_off, s);
   };
@@ -609,17 +665,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
       // matrix gets an empty descriptor (every load reads zero).
       if constexpr (AMN)
         c.ra = u.k0 < 0 ? rsrc_words(Ab, 0u)
-                        : rsrc_words(Ab + u.k0 * p.lda_b, mn_records(p.K, u.k0, p.lda_b, rows_a));
+                        : rsrc_words(Ab + u.k0 * p.lda_b,
+                                     mn_records(p.K, u.k0, p.lda_b, rows_a, T::kstep, T::es));
       else
         c.ra = rsrc_words(Ab + u.kb, rec_a - u.kb);
       if constexpr (BMN)
         c.rb = u.k0 < 0 ? rsrc_words(Bb, 0u)
-                        : rsrc_words(Bb + u.k0 * p.ldb_b, mn_records(p.K, u.k0, p.ldb_b, rows_b));
+                        : rsrc_words(Bb + u.k0 * p.ldb_b,
+                                     mn_records(p.K, u.k0, p.ldb_b, rows_b, T::kstep, T::es));
       else
         c.rb = rsrc_words(Bb + u.kb, rec_b - u.kb);
       const uint32_t st = (uint32_t)(uintptr_t)((lds_u8 *)smem + u.stage * 2 * kStageBytes);
-      c.la = st + (AMN ? mn_wave_row(wave) * kMnRowBytes : wave * 1024);
-      c.lb = st + kStageBytes + (BMN ? mn_wave_row(wave) * kMnRowBytes : wave * 1024);
+      c.la = st + (AMN ? G::wave_row(wave) * G::row_bytes : wave * 1024);
+      c.lb = st + kStageBytes + (BMN ? G::wave_row(wave) * G::row_bytes : wave * 1024);
     } else {
       c.ra = make_rsrc(Ab + u.kb, rec_a - u.kb);
       c.rb = make_rsrc(Bb + u.kb, rec_b - u.kb);
@@ -688,10 +746,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     // only (loads complete in order) and publish it.
     const Copy c0 = step_copy(0);
 #pragma unroll
-    for (int d = 0; d < kCopies; ++d) copy_one<AMN, BMN>(c0, d, qs_a, qs_b);
+    for (int d = 0; d < kCopies; ++d) copy_one<AMN, BMN, KIND>(c0, d, qs_a, qs_b);
     const Copy c1 = step_copy(1);
 #pragma unroll
-    for (int d = 0; d < kPost; ++d) copy_one<AMN, BMN>(c1, d, qs_a, qs_b);
+    for (int d = 0; d < kPost; ++d) copy_one<AMN, BMN, KIND>(c1, d, qs_a, qs_b);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPost));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -739,10 +797,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
             if (slot == kPlan + 2) step_lanes(un, cnn);
             if (slot < kWin - kAfter) {
               const int x = slot + kAfter;     // at most one copy per slot
-              if (first_copy(x) < first_copy(x + 1)) copy_one<AMN, BMN>(cn, first_copy(x), qs_a, qs_b);
+              if (first_copy(x) < first_copy(x + 1)) copy_one<AMN, BMN, KIND>(cn, first_copy(x), qs_a, qs_b);
             } else if (slot >= kBarSlot && slot - kBarSlot < kWin) {
               const int x = slot - kBarSlot;
-              if (first_copy(x) < first_copy(x + 1)) copy_one<AMN, BMN>(cnn, first_copy(x), qs_a, qs_b);
+              if (first_copy(x) < first_copy(x + 1)) copy_one<AMN, BMN, KIND>(cnn, first_copy(x), qs_a, qs_b);
             }
             if (g == 7 && par == 1) acc[g][j] = mma(fx, fb[par][j], acc[g][j]);
             else acc[g][j] = mma(fa[g], fb[par][j], acc[g][j]);
@@ -1089,7 +1147,11 @@ struct MidOperand {
   uint32_t frag[4];    // fragment read offsets (see read)
 };
 
+// Swizzle key of K-row k in the 128 x 128 kernel's M/N-contiguous strips
+// (fp16: 256-byte K-rows, fp8: 128-byte K-rows): distinct 16-byte bank groups
+// for the K-rows one transposing read phase touches.
 __device__ __forceinline__ int mn_swz(int k) { return 2 * (k & 3) + 8 * ((k >> 3) & 1); }
+__device__ __forceinline__ int mn_swz8(int k) { return ((k >> 1) & 3) + 4 * ((k >> 4) & 1); }
 
 // Copies of one operand of the 128 x 128 kernel for K-step t into this
 // wave's KiB `st` of each 4 KiB quarter of the operand's LDS strip.
@@ -1106,7 +1168,7 @@ __device__ __forceinline__ void mid_copy(const uint8_t *base, int64_t ld_b, int6
   uint32_t rbytes;
   if constexpr (MN) {
     // Rebased on the step's first K-row; rows at or past K and chunks past
-    // M / N read zero.  The descriptor covers the step's 64 K-rows.
+    // M / N read zero.  The descriptor covers the step's K-rows.
     rbase = base + k0 * ld_b;
     rbytes = (uint32_t)(T::kstep * ld_b);
 #pragma unroll
@@ -1140,7 +1202,6 @@ __device__ __forceinline__ void mid_copy(const uint8_t *base, int64_t ld_b, int6
 template <int KIND, bool AMN, bool BMN>
 __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   typedef Traits<KIND> T;
-  static_assert(KIND == kF16 || (!AMN && !BMN), "M/N-major operands are fp16 only");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * kMidStrip];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1150,8 +1211,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   const int64_t m0 = (int64_t)tm * kMidTile, n0 = (int64_t)tn * kMidTile;
   // Block bases: K-major operands at their first row, M/N-major ones at their
   // first column (element m0 / n0 of K-row 0).
-  const uint8_t *Ab = p.A + head * p.stride_a_b + (AMN ? m0 * 2 : m0 * p.lda_b);
-  const uint8_t *Bb = p.B + head * p.stride_b_b + (BMN ? n0 * 2 : n0 * p.ldb_b);
+  const uint8_t *Ab = p.A + head * p.stride_a_b + (AMN ? m0 * T::es : m0 * p.lda_b);
+  const uint8_t *Bb = p.B + head * p.stride_b_b + (BMN ? n0 * T::es : n0 * p.ldb_b);
   uint8_t *Cb = p.C + head * p.stride_c_b;
   const int64_t rows_a = (p.M - m0) < kMidTile ? (p.M - m0) : kMidTile;
   const int64_t rows_b = (p.N - n0) < kMidTile ? (p.N - n0) : kMidTile;
@@ -1164,17 +1225,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   const int crow = 8 * wave + (lane >> 3);
   const int gchunk = (lane & 7) ^ ((crow >> 1) & 7);
   const int kchunk = gchunk * (16 / T::es);
-  // M/N-major copies: load q fills K-rows 16q + 4w .. +3 (1 KiB); lane l
-  // lands in K-row 16q + 4w + (l >> 4), slot l & 15.
+  // M/N-major copies (load q of wave w: 1 KiB at strip byte 4096 q + 1024 w).
+  // fp16 (256-byte K-rows): lane l lands in K-row 16q + 4w + (l >> 4), slot
+  // l & 15.  fp8 (128-byte K-rows): K-row 32q + 16 (w >> 1) + 8 (w & 1) +
+  // (l >> 3), slot l & 7.  Each fetches the chunk its slot holds under the
+  // swizzle; chunks past M (N) and K-rows past K read zero.
   auto mn_operand = [&](int64_t ld_b, int64_t rows) {
     MidOperand<true> o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int k = 16 * q + 4 * wave + (lane >> 4);
-      const int c = (lane & 15) ^ mn_swz(k);
+      const int k = (KIND == kF16) ? 16 * q + 4 * wave + (lane >> 4)
+                                   : 32 * q + 16 * (wave >> 1) + 8 * (wave & 1) + (lane >> 3);
+      const int c = (KIND == kF16) ? (lane & 15) ^ mn_swz(k) : (lane & 7) ^ mn_swz8(k);
       o.krow[q] = k;
       o.off[q] = (uint32_t)(k * ld_b) + c * 16;
-      o.cvalid[q] = 8 * c < rows;
+      o.cvalid[q] = (16 / T::es) * c < rows;
     }
     return o;
   };
@@ -1215,17 +1280,25 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   // K-row 8g + (rl >> 2) (+ 32s + 4h), slot of the tile's first chunk
   // (8 w + 2i) ^ swz with swz = 2 (rl >> 2) + 8 (g & 1), plus chunk half and
   // 8-byte half from rl & 3.
-  const int mn_k = 8 * grp + (rl >> 2);
-  const int mn_swz_l = mn_swz(mn_k);
-  auto mn_frag = [&](lds_cptr strip, int w8, int i, int s) -> half8_t {
-    typedef short v4i16 __attribute__((ext_vector_type(4)));
-    const int slot = ((w8 + 2 * i) ^ mn_swz_l) + ((rl & 3) >> 1);
-    const uint32_t off = (uint32_t)((32 * s + mn_k) * 256 + slot * 16 + (rl & 1) * 8);
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(strip + off));
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16 *)(strip + off + 4 * 256));
-    return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  // fp8: lane (rl, grp) reads K-row 16 grp + rl / 2 (+ 8, 64, 72) at bytes
+  // 8 (rl % 2) .. +7 of the tile's single 16-byte chunk 4 w + i, in slot
+  // (4 w + i) ^ swz8 with swz8 = (rl >> 2) + 4 (grp & 1).
+  const int mn_k = (KIND == kF16) ? 8 * grp + (rl >> 2) : 16 * grp + (rl >> 1);
+  const int mn_swz_l = (KIND == kF16) ? mn_swz(mn_k) : mn_swz8(mn_k);
+  auto mn_frag = [&](lds_cptr strip, int w, int i, int s) -> typename T::frag_t {
+    if constexpr (KIND == kF16) {
+      typedef short v4i16 __attribute__((ext_vector_type(4)));
+      const int slot = ((8 * w + 2 * i) ^ mn_swz_l) + ((rl & 3) >> 1);
+      const uint32_t off = (uint32_t)((32 * s + mn_k) * 256 + slot * 16 + (rl & 1) * 8);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16 *)(strip + off));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16 *)(strip + off + 4 * 256));
+      return __builtin_bit_cast(half8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      const int slot = (4 * w + i) ^ mn_swz_l;
+      return mn_frag8<128>(strip, (uint32_t)(mn_k * 128 + slot * 16 + (rl & 1) * 8));
+    }
   };
 
   float4_t_v acc[4][4];
@@ -1248,11 +1321,11 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (AMN)
-          fa[i] = mn_frag(st, 8 * wm, i, s);
+          fa[i] = mn_frag(st, wm, i, s);
         else
           fa[i] = read_frag<KIND>(st + i * 16 * kRowBytes, a_off, s);
         if constexpr (BMN)
-          fb[i] = mn_frag(st + kMidStrip, 8 * wn, i, s);
+          fb[i] = mn_frag(st + kMidStrip, wn, i, s);
         else
           fb[i] = read_frag<KIND>(st + i * 16 * kRowBytes, b_off, s);
       }
@@ -1645,46 +1718,51 @@ static int launch(const Problem &pr, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
-// fp16 products in any of the four op-code layouts.  TN goes through
-// launch<> and its configurations; for the others each M- or N-contiguous
-// operand (A of an 'N' op, B of a 'T' op) is staged as it lies in memory and
-// turned by the fragment reads -- no transpose pass -- in the 256-row kernel
-// or the 128 x 128 one, picked by the same selector (the skinny-K kernel is
-// TN-only; its problems take the 128 x 128 tiles).
-static int launch_f16_layout(char ta, char tb, const Problem &pr, hipStream_t stream) {
+// Products in any of the four op-code layouts (fp16 in and out, or fp8 E4M3FN
+// in and bf16 out with per-tensor scales).  TN goes through launch<> and its
+// configurations; for the others each M- or N-contiguous operand (A of an 'N'
+// op, B of a 'T' op) is staged as it lies in memory and turned by the
+// fragment reads -- no transpose pass -- in the 256-row kernel or the
+// 128 x 128 one, picked by the same selector (the skinny-K kernel is TN-only;
+// its problems take the 128 x 128 tiles).
+template <int KIND>
+static int launch_layout(char ta, char tb, const Problem &pr, hipStream_t stream) {
+  typedef Traits<KIND> T;
+  const int es = T::es;
+  const int64_t vec = 16 / es;  // elements per 16-byte chunk
   const bool a_t = ta == 'T' || ta == 't', a_n = ta == 'N' || ta == 'n';
   const bool b_t = tb == 'T' || tb == 't', b_n = tb == 'N' || tb == 'n';
   if (!(a_t || a_n) || !(b_t || b_n)) return DG_ERR_INVALID_ARGUMENT;
-  if (a_t && b_n) return launch<kF16>(pr, stream);
+  if (a_t && b_n) return launch<KIND>(pr, stream);
   const bool amn = a_n, bmn = b_t;
   if (pr.M < 0 || pr.N < 0 || pr.K < 0) return DG_ERR_INVALID_ARGUMENT;
   if (pr.lda < (amn ? pr.M : pr.K) || pr.ldb < (bmn ? pr.N : pr.K) || pr.ldc < pr.M)
     return DG_ERR_INVALID_ARGUMENT;
   if (pr.M == 0 || pr.N == 0) return DG_OK;
   if (!pr.A || !pr.B || !pr.C) return DG_ERR_INVALID_ARGUMENT;
-  const uint64_t a_all = amn ? span_bytes(pr.K, pr.M, pr.lda, 2) : span_bytes(pr.M, pr.K, pr.lda, 2);
-  const uint64_t b_all = bmn ? span_bytes(pr.K, pr.N, pr.ldb, 2) : span_bytes(pr.N, pr.K, pr.ldb, 2);
+  const uint64_t a_all = amn ? span_bytes(pr.K, pr.M, pr.lda, es) : span_bytes(pr.M, pr.K, pr.lda, es);
+  const uint64_t b_all = bmn ? span_bytes(pr.K, pr.N, pr.ldb, es) : span_bytes(pr.N, pr.K, pr.ldb, es);
   const uint64_t c_all = span_bytes(pr.N, pr.M, pr.ldc, 2);
   if (overlaps(pr.C, c_all, pr.A, a_all) || overlaps(pr.C, c_all, pr.B, b_all))
     return DG_ERR_INVALID_ARGUMENT;
 
   // 16-byte chunks along each operand's contiguous dimension; K only has to be
-  // a multiple of 8 when an operand is K-contiguous.
-  if (pr.lda % 8 || pr.ldb % 8) return DG_ERR_UNSUPPORTED;
-  if ((!amn || !bmn) && pr.K % 8) return DG_ERR_UNSUPPORTED;
-  if ((amn && pr.M % 8) || (bmn && pr.N % 8)) return DG_ERR_UNSUPPORTED;
+  // a multiple of the chunk when an operand is K-contiguous.
+  if (pr.lda % vec || pr.ldb % vec) return DG_ERR_UNSUPPORTED;
+  if ((!amn || !bmn) && pr.K % vec) return DG_ERR_UNSUPPORTED;
+  if ((amn && pr.M % vec) || (bmn && pr.N % vec)) return DG_ERR_UNSUPPORTED;
   if (!aligned16(pr.A) || !aligned16(pr.B) || !aligned16(pr.C)) return DG_ERR_UNSUPPORTED;
   // Offsets inside one block's descriptors stay below kOob: 256 rows of a
-  // K-contiguous operand (and its strip), 64 K-rows (one step, 512 bytes of
-  // columns) of an M/N-contiguous one.
+  // K-contiguous operand (and its strip), one K-step of an M/N-contiguous one
+  // (plus a 256-column row).
   auto fits = [&](bool mn, int64_t ld, int64_t rows) {
-    if (mn) return 64 * ld * 2 + 2 * kMnRowBytes < (int64_t)kOob;
-    const int64_t strip = (int64_t)span_bytes(rows < kTile ? rows : kTile, pr.K, ld, 2);
-    return kTile * ld * 2 + kRowBytes < (int64_t)kOob && strip < (int64_t)kOob;
+    if (mn) return T::kstep * ld * es + 2 * Mn<KIND>::row_bytes < (int64_t)kOob;
+    const int64_t strip = (int64_t)span_bytes(rows < kTile ? rows : kTile, pr.K, ld, es);
+    return kTile * ld * es + kRowBytes < (int64_t)kOob && strip < (int64_t)kOob;
   };
   if (!fits(amn, pr.lda, pr.M) || !fits(bmn, pr.ldb, pr.N)) return DG_ERR_UNSUPPORTED;
 
-  const bool mid = choose_config(2, pr.M, pr.N, pr.K, 1, false).kind == kCfgMid;
+  const bool mid = choose_config(es, pr.M, pr.N, pr.K, 1, false).kind == kCfgMid;
   const int64_t tile_m = mid ? kMidTile : kTile;
   const int64_t tile_n = mid ? kMidTile : kTile;
   const int64_t tiles_m = (pr.M + tile_m - 1) / tile_m;
@@ -1697,22 +1775,22 @@ static int launch_f16_layout(char ta, char tb, const Problem &pr, hipStream_t st
   p.B = (const uint8_t *)pr.B;
   p.C = (uint8_t *)pr.C;
   p.M = pr.M; p.N = pr.N; p.K = pr.K;
-  p.lda_b = pr.lda * 2; p.ldb_b = pr.ldb * 2; p.ldc = pr.ldc;
+  p.lda_b = pr.lda * es; p.ldb_b = pr.ldb * es; p.ldc = pr.ldc;
   p.stride_a_b = 0; p.stride_b_b = 0; p.stride_c_b = 0;
   p.tiles_m = (int32_t)tiles_m; p.tiles_n = (int32_t)tiles_n;
-  p.scale = 1.0f;
+  p.scale = pr.scale;
   p.c_vec_ok = (pr.ldc % 4 == 0) ? 1 : 0;
   p.c_vec16_ok = (pr.ldc % 8 == 0) ? 1 : 0;
   p.sk_walk = 1;
   const dim3 grid((unsigned)blocks), block(kThreads);
   // One kernel per (layout, configuration).
   typedef void (*kernel_t)(Params);
-  static const kernel_t mids[3] = {gemm_tn_mid_kernel<kF16, true, false>,
-                                   gemm_tn_mid_kernel<kF16, false, true>,
-                                   gemm_tn_mid_kernel<kF16, true, true>};
-  static const kernel_t bigs[3] = {gemm_tn_kernel<kF16, 8, true, false>,
-                                   gemm_tn_kernel<kF16, 8, false, true>,
-                                   gemm_tn_kernel<kF16, 8, true, true>};
+  static const kernel_t mids[3] = {gemm_tn_mid_kernel<KIND, true, false>,
+                                   gemm_tn_mid_kernel<KIND, false, true>,
+                                   gemm_tn_mid_kernel<KIND, true, true>};
+  static const kernel_t bigs[3] = {gemm_tn_kernel<KIND, 8, true, false>,
+                                   gemm_tn_kernel<KIND, 8, false, true>,
+                                   gemm_tn_kernel<KIND, 8, true, true>};
   const int li = amn && bmn ? 2 : amn ? 0 : 1;
   const kernel_t k = mid ? mids[li] : bigs[li];
   hipLaunchKernelGGL(k, grid, block, 0, stream, p);
@@ -1726,7 +1804,14 @@ extern "C" {
 int gemm_f16(char transa, char transb, const void *A, const void *B, void *C, int64_t M,
              int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, void *stream) {
   dg::Problem pr{A, B, C, 1, M, N, K, lda, ldb, ldc, 0, 0, 0, 1.0f};
-  return dg::launch_f16_layout(transa, transb, pr, (hipStream_t)stream);
+  return dg::launch_layout<dg::kF16>(transa, transb, pr, (hipStream_t)stream);
+}
+
+int gemm_f8(char transa, char transb, const void *A, const void *B, void *C, int64_t M,
+            int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, float scale_a,
+            float scale_b, void *stream) {
+  dg::Problem pr{A, B, C, 1, M, N, K, lda, ldb, ldc, 0, 0, 0, scale_a * scale_b};
+  return dg::launch_layout<dg::kF8>(transa, transb, pr, (hipStream_t)stream);
 }
 
 int gemm_f16_tn(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
@@ -1776,11 +1861,19 @@ int gemm_tile_order(int64_t tiles_m, int64_t tiles_n, int64_t batch, int64_t *ou
 
 int gemm_block_tile(void) { return dg::kTile; }
 
-int gemm_f16_config(char transa, char transb, int64_t M, int64_t N, int64_t K) {
+static int layout_config(int es, char transa, char transb, int64_t M, int64_t N, int64_t K) {
   const bool a_t = transa == 'T' || transa == 't', a_n = transa == 'N' || transa == 'n';
   const bool b_t = transb == 'T' || transb == 't', b_n = transb == 'N' || transb == 'n';
   if (!(a_t || a_n) || !(b_t || b_n) || M < 0 || N < 0 || K < 0) return -1;
-  return dg::choose_config(2, M, N, K, 1, a_t && b_n).kind;
+  return dg::choose_config(es, M, N, K, 1, a_t && b_n).kind;
+}
+
+int gemm_f16_config(char transa, char transb, int64_t M, int64_t N, int64_t K) {
+  return layout_config(2, transa, transb, M, N, K);
+}
+
+int gemm_f8_config(char transa, char transb, int64_t M, int64_t N, int64_t K) {
+  return layout_config(1, transa, transb, M, N, K);
 }
 
 int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch) {

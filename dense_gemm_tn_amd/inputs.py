@@ -57,12 +57,19 @@ WORKLOADS = {
         Workload("f16_1920x13900x4096_pm1", "f16", 1920, 13900, 4096, "pm1", seed=1),
         Workload("f8_8192", "f8", 8192, 8192, 8192, "normal", seed=0),
         # The other op-code layouts (A 'T' = K-contiguous rows, 'N' = M-contiguous;
-        # B 'N' = K-contiguous, 'T' = N-contiguous), same values as f16_4096.
+        # B 'N' = K-contiguous, 'T' = N-contiguous), same values as f16_4096 and
+        # f8_8192.
         Workload("f16_nn_4096", "f16", 4096, 4096, 4096, "normal", seed=0,
                  extra={"layout": "NN"}),
         Workload("f16_tt_4096", "f16", 4096, 4096, 4096, "normal", seed=0,
                  extra={"layout": "TT"}),
         Workload("f16_nt_4096", "f16", 4096, 4096, 4096, "normal", seed=0,
+                 extra={"layout": "NT"}),
+        Workload("f8_nn_8192", "f8", 8192, 8192, 8192, "normal", seed=0,
+                 extra={"layout": "NN"}),
+        Workload("f8_tt_8192", "f8", 8192, 8192, 8192, "normal", seed=0,
+                 extra={"layout": "TT"}),
+        Workload("f8_nt_8192", "f8", 8192, 8192, 8192, "normal", seed=0,
                  extra={"layout": "NT"}),
         # The 8-wave ping-pong form of the 256 x 256 tile, forced (a measured
         # counter-design; the library never picks it by itself).

@@ -113,6 +113,24 @@ int gemm_f8_tn(const void *A, const void *B, void *C,
                void *stream);
 
 /*
+ * FP8 GEMM in any of the four BLAS op-code layouts, without a transpose pass:
+ * E4M3FN A and B with per-tensor fp32 scales, bf16 C, exactly as gemm_f8_tn
+ * (C = bf16_rne(fp32(scale_a * scale_b) * op(A) op(B)), fp32 accumulation),
+ * with op(A), op(B) and C laid out as for gemm_f16 (elements are one byte).
+ * ('T', 'N') is gemm_f8_tn.  The chunk granularity is 16 elements: lda, ldb,
+ * K (when an operand is K-contiguous), M (transa 'N') and N (transb 'T') must
+ * be multiples of 16, else DG_ERR_UNSUPPORTED; other errors as for gemm_f16.
+ * Source: the FP8 GEMM of "AMD ROCm 4-wave interleave FP8 GEMM for Instinct
+ * MI355X (CDNA 4)" and, for the layouts, "FP16 GEMM optimisation on AMD RDNA 3
+ * and RDNA 4", section "What we compute".
+ */
+int gemm_f8(char transa, char transb, const void *A, const void *B, void *C,
+            int64_t M, int64_t N, int64_t K,
+            int64_t lda, int64_t ldb, int64_t ldc,
+            float scale_a, float scale_b,
+            void *stream);
+
+/*
  * Strided-batched Q K^T (fp16 in, fp16 out, fp32 accumulate): for each head
  * h < batch,
  *   S[h*stride_s + j*lds + i] = sum_d Q[h*stride_q + i*ldq + d] * Kmat[h*stride_k + j*ldk + d]
@@ -220,6 +238,9 @@ int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch);
  * and 128 configuration 2 for the other layouts (K > 128).
  */
 int gemm_f16_config(char transa, char transb, int64_t M, int64_t N, int64_t K);
+
+/* The same for gemm_f8 (TN: gemm_tn_config with fp8 != 0). */
+int gemm_f8_config(char transa, char transb, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
 }

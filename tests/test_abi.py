@@ -145,6 +145,35 @@ def test_f16_layout_selector(monkeypatch):
     assert dg.f16_config("T", "N", 4096, 4096, 4096) == 4
 
 
+@pytest.mark.parametrize("codes,args,status", [
+    ((b"X", b"N"), (A_ADDR, B_ADDR, C_ADDR, 16, 16, 16, 16, 16, 16), dg.DG_ERR_INVALID_ARGUMENT),
+    ((b"N", b"N"), (A_ADDR, B_ADDR, C_ADDR, 32, 16, 16, 16, 16, 32), dg.DG_ERR_INVALID_ARGUMENT),
+    ((b"N", b"N"), (A_ADDR, B_ADDR, C_ADDR, 24, 16, 16, 32, 16, 24), dg.DG_ERR_UNSUPPORTED),  # M % 16
+    ((b"T", b"T"), (A_ADDR, B_ADDR, C_ADDR, 16, 24, 16, 16, 32, 16), dg.DG_ERR_UNSUPPORTED),  # N % 16
+    ((b"N", b"N"), (A_ADDR, B_ADDR, C_ADDR, 16, 16, 24, 16, 32, 16), dg.DG_ERR_UNSUPPORTED),  # K % 16
+    ((b"N", b"T"), (A_ADDR, B_ADDR, C_ADDR, 16, 16, 16, 24, 16, 16), dg.DG_ERR_UNSUPPORTED),  # lda % 16
+    ((b"N", b"T"), (A_ADDR, B_ADDR, C_ADDR, 16, 16, 8, 8, 16, 16), dg.DG_ERR_INVALID_ARGUMENT),
+    ((b"T", b"N"), (A_ADDR, B_ADDR, C_ADDR, 16, 16, 8, 16, 16, 16), dg.DG_ERR_UNSUPPORTED),   # TN rules
+    ((b"N", b"T"), (None, None, None, 0, 16, 16, 16, 16, 16), dg.DG_OK),
+])
+def test_f8_any_layout_validation(codes, args, status):
+    assert dg.lib().gemm_f8(*codes, *args, 1.0, 1.0, None) == status
+
+
+def test_f8_layout_selector(monkeypatch):
+    monkeypatch.delenv("DG_GEMM_TILE", raising=False)
+    for M, N, K in [(8192, 8192, 8192), (2048, 2048, 2048), (1024, 1024, 256)]:
+        tn = dg.lib().gemm_tn_config(1, M, N, K, 1)
+        assert dg.f8_config("T", "N", M, N, K) == tn
+        for ta, tb in [("N", "N"), ("T", "T"), ("N", "T")]:
+            c = dg.f8_config(ta, tb, M, N, K)
+            assert c in (0, 2)
+            if K <= 256:
+                assert c == 2
+    assert dg.f8_config("N", "N", 8192, 8192, 8192) == 0
+    assert dg.lib().gemm_f8_config(b"Q", b"N", 16, 16, 16) == -1
+
+
 def test_f16_binding_rejects_bad_codes():
     with pytest.raises(ValueError):
         dg.gemm_f16("X", "N", A_ADDR, B_ADDR, C_ADDR, 8, 8, 8, 8, 8, 8)
