@@ -119,6 +119,21 @@ def test_f8_layout_padding_and_odd_ldc(tile, ta, tb):
     exact(got, oracle.gemm(As, Bs, oracle.FMT_E4M3FN, M, N, K, ta, tb, lda, ldb))
 
 
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_f8_layout_k_zero_writes_zeros(ta, tb):
+    """K = 0: the empty sum, +0 in bf16 at every logical element and nothing else
+    written, whatever the scales."""
+    M, N = 144, 80
+    print("f8 layout K=0 %s%s" % (ta, tb), flush=True)
+    lda = 16 if ta == "T" else M
+    ldb = 16 if tb == "N" else N
+    As = np.zeros((M if ta == "T" else 1, lda), np.uint8)
+    Bs = np.zeros((N if tb == "N" else 1, ldb), np.uint8)
+    got, canary = run_layout(ta, tb, As, Bs, M, N, 0, lda, ldb, 3.0, 0.5)
+    assert canary
+    assert np.all(got == 0)
+
+
 @pytest.mark.parametrize("force", ["128", "256"])
 def test_f8_layouts_scaled_normal_agree(monkeypatch, force):
     """Per-tensor-scaled N(0,1) data: every layout within the bf16 tolerance of the
