@@ -53,11 +53,11 @@
 //   MI355X FP8 GEMM page weighs against its 4-wave one); measured slower here,
 //   so only used when forced.
 //
-// Other op-code layouts (fp16, gemm_f16): the 256 x 256 and 128 x 128 kernels
-//   take template flags AMN / BMN for an M- or N-contiguous operand, staged in
-//   LDS as it lies (K-rows of the tile's columns) and turned into MFMA operand
-//   fragments by gfx950's transposing LDS read, so data in those layouts needs
-//   no transpose pass ("FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4",
+// Other op-code layouts (gemm_f16, gemm_f8): the 256 x 256 and 128 x 128
+//   kernels take template flags AMN / BMN for an M- or N-contiguous operand,
+//   staged in LDS as it lies (K-rows of the tile's columns) and turned into
+//   MFMA operand fragments by gfx950's transposing LDS reads (16-bit elements
+//   for fp16, bytes for fp8), so data in those layouts needs no transpose pass ("FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4",
 //   section "What we compute", notes real data may otherwise need one).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -1139,6 +1139,8 @@ __device__ __forceinline__ float4_t_v mma_c(const int8_t_v &a, const int8_t_v &b
 // of a 16-wide tile leave lane j holding K-rows k0 .. k0 + 3 of column j --
 // the MFMA operand layout.  The swizzle spreads the sixteen K-rows one such
 // read touches (two 16-lane groups per LDS pass) over distinct slots.
+// M/N-major fp8 operands: 128 K-rows of 128 bytes, chunk c of K-row k in slot
+// c ^ mn_swz8(k), fragments from ds_read_b64_tr_b8 (see mn_frag8).
 template <bool MN>
 struct MidOperand {
   uint32_t off[4];     // copy offsets of loads q = 0..3 (lane constant)
