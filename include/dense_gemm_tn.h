@@ -90,8 +90,8 @@ int gemm_f16_tn(const void *A, const void *B, void *C,
  * lda or ldb below the contiguous extent listed above.  DG_ERR_UNSUPPORTED
  * for lda or ldb not a multiple of 8; K not a multiple of 8 when an operand is
  * K-contiguous; M (transa 'N') or N (transb 'T') not a multiple of 8; A, B or
- * C not 16-byte aligned; 64 rows of an M/N-contiguous operand or 128 rows of
- * a K-contiguous one spanning 2^31 bytes or more.
+ * C not 16-byte aligned; one K-step of rows of an M/N-contiguous operand (64
+ * K-rows) or 256 rows of a K-contiguous one spanning 2^31 bytes or more.
  */
 int gemm_f16(char transa, char transb, const void *A, const void *B, void *C,
              int64_t M, int64_t N, int64_t K,
@@ -119,7 +119,8 @@ int gemm_f8_tn(const void *A, const void *B, void *C,
  * with op(A), op(B) and C laid out as for gemm_f16 (elements are one byte).
  * ('T', 'N') is gemm_f8_tn.  The chunk granularity is 16 elements: lda, ldb,
  * K (when an operand is K-contiguous), M (transa 'N') and N (transb 'T') must
- * be multiples of 16, else DG_ERR_UNSUPPORTED; other errors as for gemm_f16.
+ * be multiples of 16, else DG_ERR_UNSUPPORTED; a K-step of an M/N-contiguous
+ * operand is 128 K-rows here; other errors as for gemm_f16.
  * Source: the FP8 GEMM of "AMD ROCm 4-wave interleave FP8 GEMM for Instinct
  * MI355X (CDNA 4)" and, for the layouts, "FP16 GEMM optimisation on AMD RDNA 3
  * and RDNA 4", section "What we compute".
