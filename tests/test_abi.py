@@ -154,6 +154,10 @@ def test_f16_layout_selector(monkeypatch):
     ((b"N", b"T"), (A_ADDR, B_ADDR, C_ADDR, 16, 16, 16, 24, 16, 16), dg.DG_ERR_UNSUPPORTED),  # lda % 16
     ((b"N", b"T"), (A_ADDR, B_ADDR, C_ADDR, 16, 16, 8, 8, 16, 16), dg.DG_ERR_INVALID_ARGUMENT),
     ((b"T", b"N"), (A_ADDR, B_ADDR, C_ADDR, 16, 16, 8, 16, 16, 16), dg.DG_ERR_UNSUPPORTED),   # TN rules
+    ((b"N", b"N"), (1 << 44, 2 << 44, 3 << 44, 16, 16, 16, 16 << 20, 16, 16),
+     dg.DG_ERR_UNSUPPORTED),                                                  # 128 K-rows >= 2 GiB
+    ((b"T", b"T"), (1 << 44, 2 << 44, 3 << 44, 16, 16, 16, 16, 16 << 20, 16),
+     dg.DG_ERR_UNSUPPORTED),                                                  # the same for B
     ((b"N", b"T"), (None, None, None, 0, 16, 16, 16, 16, 16), dg.DG_OK),
 ])
 def test_f8_any_layout_validation(codes, args, status):
