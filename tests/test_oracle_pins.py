@@ -295,3 +295,42 @@ def test_four_layouts_against_integer_matmul(trans_a, trans_b):
     e = oracle.gemm_entries(Astore, Bstore, oracle.FMT_F16, K, ms, ns, M, N, trans_a=trans_a,
                             trans_b=trans_b, lda=Astore.shape[1], ldb=Bstore.shape[1])
     np.testing.assert_array_equal(e, want[ms, ns].astype(np.float64))
+
+
+# E4M3FN codes of small dyadic values, from the format's definition
+# (sign bit 7, 4 exponent bits with bias 7, 3 mantissa bits: 2^(e-7) * (1 + m/8)).
+E4M3_TABLE = {0x38: 1.0, 0xB8: -1.0, 0x40: 2.0, 0xC0: -2.0, 0x30: 0.5, 0xB0: -0.5,
+              0x3C: 1.5, 0xBC: -1.5}
+
+
+@pytest.mark.parametrize("trans_a", ["T", "N"])
+@pytest.mark.parametrize("trans_b", ["T", "N"])
+def test_four_layouts_fp8_against_exact_matmul(trans_a, trans_b):
+    """The FP8 path of the strided oracle in each op-code layout: E4M3FN codes of
+    dyadic values (every product and partial sum exact in binary64), padding holding
+    the E4M3FN NaN code, a power-of-two scale; numpy's float64 matmul of the values
+    the codes stand for is exact here."""
+    rng = np.random.default_rng(29)
+    M, N, K = 21, 17, 45
+    codes = np.array(sorted(E4M3_TABLE), dtype=np.uint8)
+    ca = rng.choice(codes, size=(M, K))
+    cb = rng.choice(codes, size=(K, N))
+    va = np.vectorize(E4M3_TABLE.get)(ca).astype(np.float64)
+    vb = np.vectorize(E4M3_TABLE.get)(cb).astype(np.float64)
+    want = (va @ vb) * 0.25                          # [M, N]
+    pad = 3
+    sa = ca if trans_a == "T" else ca.T
+    Astore = np.full((sa.shape[0], sa.shape[1] + pad), 0x7F, np.uint8)
+    Astore[:, :sa.shape[1]] = sa
+    sb = cb.T if trans_b == "N" else cb
+    Bstore = np.full((sb.shape[0], sb.shape[1] + pad), 0x7F, np.uint8)
+    Bstore[:, :sb.shape[1]] = sb
+    C = oracle.gemm(Astore, Bstore, oracle.FMT_E4M3FN, M, N, K, trans_a=trans_a,
+                    trans_b=trans_b, lda=Astore.shape[1], ldb=Bstore.shape[1], scale=0.25)
+    np.testing.assert_array_equal(C.T, want)
+    ms = rng.integers(0, M, 30)
+    ns = rng.integers(0, N, 30)
+    e = oracle.gemm_entries(Astore, Bstore, oracle.FMT_E4M3FN, K, ms, ns, M, N,
+                            trans_a=trans_a, trans_b=trans_b, lda=Astore.shape[1],
+                            ldb=Bstore.shape[1], scale=0.25)
+    np.testing.assert_array_equal(e, want[ms, ns])
