@@ -72,7 +72,6 @@
 namespace dg {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float16_t_v __attribute__((ext_vector_type(16)));
 typedef float float4_t_v __attribute__((ext_vector_type(4)));
 typedef int int8_t_v __attribute__((ext_vector_type(8)));
 typedef int int4_t_v __attribute__((ext_vector_type(4)));
@@ -84,7 +83,6 @@ constexpr int kRowBytes = 128;    // bytes of K per row per K-step (full 128-byt
 constexpr int kStages = 2;        // LDS stages (double buffer)
 constexpr int kThreads = 256;     // 4 waves of 64
 constexpr int kWaveTile = 128;    // each wave owns kWaveTile x kWaveTile of C
-constexpr int kMma = 32;          // MFMA output tile edge of the skinny-K kernels
 constexpr int kXcds = 8;          // chiplets the dispatcher deals blocks over
 constexpr int kGroupM = 8;        // tile rows per group in the grouped order
 constexpr int kStageBytes = kTile * kRowBytes;   // 32 KiB per operand per stage
@@ -117,10 +115,6 @@ template <> struct Traits<kF8> {
   typedef float4_t_v acc_t;
 };
 
-__device__ __forceinline__ float16_t_v mma(const half8_t &a, const half8_t &b, float16_t_v c) {
-  // v_mfma_f32_32x32x16_f16: fp16 products, fp32 accumulate.
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ float4_t_v mma(const half8_t &a, const half8_t &b, float4_t_v c) {
   // v_mfma_f32_16x16x32_f16: fp16 products, fp32 accumulate.  Written as
   // inline assembly with the accumulator tied in place in AGPRs: with the
@@ -143,10 +137,16 @@ __device__ __forceinline__ float4_t_v mma(const int8_t_v &a, const int8_t_v &b, 
 __device__ __forceinline__ void mfma_drain() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
-__device__ __forceinline__ float16_t_v mma(const int8_t_v &a, const int8_t_v &b, float16_t_v c) {
-  // v_mfma_f32_32x32x64_f8f6f4 with both operand formats = 0 (FP8 E4M3) and
-  // no block scales; the per-tensor scales are applied in the epilogue.
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+// The same products with the accumulators left to the compiler (the 128 x 128
+// and skinny-K kernels, whose few accumulators need no pinning).
+__device__ __forceinline__ float4_t_v mma_c(const half8_t &a, const half8_t &b,
+                                            const float4_t_v &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4_t_v mma_c(const int8_t_v &a, const int8_t_v &b,
+                                            const float4_t_v &c) {
+  // v_mfma_f32_16x16x128_f8f6f4, FP8 E4M3 operands, no block scales.
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 // Kernel arguments (one struct, passed by value).
@@ -841,15 +841,17 @@ template __global__ void gemm_tn_kernel<kF8, 7, false, false>(Params);
 // ----------------------------------------------------------------- skinny K
 // Kernels for K * es <= 256 bytes (the QK^T shape: K = head dim 128): the whole
 // K extent of a 128 x 128 tile's A and B strips fits in LDS at once (2 x 32
-// KiB), so there is no K pipeline; each wave owns 64 x 64 of C (2 x 2 MFMA
-// 32x32 tiles, 64 accumulators).  Writing C bounds these shapes; one tile per
+// KiB), so there is no K pipeline; each wave owns 64 x 64 of C (4 x 4 MFMA
+// tiles of 16 x 16, 64 accumulators; the 16x16 shapes draw less power than
+// the 32x32 ones, which this power-limited kernel turns into clock, measured
+// 2-3 % faster on the QK^T shape).  Writing C bounds these shapes; one tile per
 // block and two blocks per CU let one block's stores drain while the other
 // block copies and computes.
 constexpr int kSkTile = 128;       // rows of A / columns of B per block
 constexpr int kSkRow = 256;        // LDS bytes per row (all of K, zero-filled)
 constexpr int kSkStrip = kSkTile * kSkRow;  // 32 KiB per operand
 constexpr int kSkWave = 64;        // each wave owns 64 x 64 of C
-constexpr int kSkSub = 2;          // MFMA tiles per wave edge
+constexpr int kSkSub = 4;          // MFMA tiles of 16 x 16 per wave edge
 constexpr int kSkWalkMax = 32;     // most M tiles one block walks
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -901,26 +903,30 @@ __device__ __forceinline__ void sk_copy_b(const Params &p, lds_u8 *strip, int he
                       lane);
 }
 
-// The wave's 64 x 64 block of A x B from a stage (substeps of 32 B of K: one
-// 16-byte chunk per lane half for fp16, two for fp8; fragments double-buffered).
+// The wave's 64 x 64 block of A x B from a stage as 4 x 4 MFMA tiles of
+// 16 x 16: lane l reads row l % 16 of a 16-row tile and K group g = l / 16 of
+// each sub-step (fp16 16x16x32: chunk 4s + g; fp8 16x16x128: chunks 8s + g and
+// 8s + g + 4, the K order of the 256 x 256 kernel); fragments double-buffered.
+// A 16-lane read phase covers 16 consecutive rows of one chunk: 16 distinct
+// slots of the bank period.
 template <int KIND>
-__device__ __forceinline__ void sk_compute(float16_t_v (&acc)[kSkSub][kSkSub], lds_cptr stage,
+__device__ __forceinline__ void sk_compute(float4_t_v (&acc)[kSkSub][kSkSub], lds_cptr stage,
                                            int wm, int wn, int lane) {
   typedef Traits<KIND> T;
-  constexpr int kSubs = (T::reads == 1) ? 8 : 4;
-  lds_cptr la = stage + (wm * kSkWave + (lane & 31)) * kSkRow;
-  lds_cptr lb = stage + kSkStrip + (wn * kSkWave + (lane & 31)) * kSkRow;
-  const int sw = lane & 15;
+  constexpr int kSubs = (KIND == kF16) ? 4 : 2;   // sub-steps over 256 bytes of K
+  const int g = lane >> 4, sw = lane & 15;
+  lds_cptr la = stage + (wm * kSkWave + sw) * kSkRow;
+  lds_cptr lb = stage + kSkStrip + (wn * kSkWave + sw) * kSkRow;
   auto frag = [&](lds_cptr row0, int i, int s) -> typename T::frag_t {
-    lds_cptr r = row0 + i * kMma * kSkRow;
-    if constexpr (T::reads == 1) {
-      const int c = 2 * s + (lane >> 5);
+    lds_cptr r = row0 + i * 16 * kSkRow;
+    if constexpr (KIND == kF16) {
+      const int c = 4 * s + g;
       return *(const __attribute__((address_space(3))) half8_t *)(r + ((c ^ sw) * 16));
     } else {
-      const int c = 4 * s + 2 * (lane >> 5);
+      const int c = 8 * s + g;
       const int4_t_v lo = *(const __attribute__((address_space(3))) int4_t_v *)(r + ((c ^ sw) * 16));
       const int4_t_v hi =
-          *(const __attribute__((address_space(3))) int4_t_v *)(r + (((c + 1) ^ sw) * 16));
+          *(const __attribute__((address_space(3))) int4_t_v *)(r + (((c + 4) ^ sw) * 16));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
@@ -929,7 +935,7 @@ __device__ __forceinline__ void sk_compute(float16_t_v (&acc)[kSkSub][kSkSub], l
 #pragma unroll
     for (int j = 0; j < kSkSub; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
   typename T::frag_t fa[2][kSkSub], fb[2][kSkSub];
 #pragma unroll
   for (int i = 0; i < kSkSub; ++i) {
@@ -949,41 +955,31 @@ __device__ __forceinline__ void sk_compute(float16_t_v (&acc)[kSkSub][kSkSub], l
 #pragma unroll
     for (int i = 0; i < kSkSub; ++i)
 #pragma unroll
-      for (int j = 0; j < kSkSub; ++j) acc[i][j] = mma(fa[u][i], fb[u][j], acc[i][j]);
+      for (int j = 0; j < kSkSub; ++j) acc[i][j] = mma_c(fa[u][i], fb[u][j], acc[i][j]);
   }
 }
 
 // Converted accumulators of wave (wm, wn) into the tile's 32 KiB transpose
 // buffer: column n (0..127) at n * 256 B, its 16-byte chunk c (rows 8c ..
-// 8c+7) in slot c ^ (n & 15).  A 16-lane read phase covers one whole column
-// (all 16 slots of a bank period); the 32 columns of a write phase meet each
-// slot at most twice.
+// 8c+7) in slot c ^ (n & 15).  Lane (rl, grp) of tile (i, j) holds rows
+// 16i + 4 grp .. +3 of column 16j + rl: one 8-byte write per tile.  A 16-lane
+// read phase covers one whole column (all 16 slots of a bank period).
 template <int KIND>
-__device__ __forceinline__ void sk_to_lds(const Params &p, const float16_t_v (&acc)[kSkSub][kSkSub],
+__device__ __forceinline__ void sk_to_lds(const Params &p, const float4_t_v (&acc)[kSkSub][kSkSub],
                                           lds_u8 *buf, int wm, int wn, int lane) {
 #pragma unroll
   for (int j = 0; j < kSkSub; ++j) {
-    const int n = kSkWave * wn + kMma * j + (lane & 31);
+    const int n = kSkWave * wn + 16 * j + (lane & 15);
 #pragma unroll
     for (int i = 0; i < kSkSub; ++i) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int m = kSkWave * wm + kMma * i + 8 * b + 4 * (lane >> 5);
-        uint16_t h[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (KIND == kF16) {
-            h[e] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][4 * b + e]);
-          } else {
-            h[e] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][4 * b + e] * p.scale));
-          }
-        }
-        u32x2 w;
-        w.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
-        w.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
-        *(__attribute__((address_space(3))) u32x2 *)(buf + n * 256 + (((m >> 3) ^ (n & 15)) * 16) +
-                                                   (m & 7) * 2) = w;
-      }
+      const int m = kSkWave * wm + 16 * i + 4 * (lane >> 4);
+      uint32_t w0, w1;
+      pack_run<KIND>(p, acc[i][j], 0, w0, w1);
+      u32x2 w;
+      w.x = w0;
+      w.y = w1;
+      *(__attribute__((address_space(3))) u32x2 *)(buf + n * 256 + (((m >> 3) ^ (n & 15)) * 16) +
+                                                 (m & 7) * 2) = w;
     }
   }
 }
@@ -1020,7 +1016,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_skinny_kernel(Params p) {
     // also covers the previous tile's stores.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();
-    float16_t_v acc[kSkSub][kSkSub];
+    float4_t_v acc[kSkSub][kSkSub];
     sk_compute<KIND>(acc, (lds_cptr)smem, wm, wn, lane);
     __syncthreads();  // every wave is done reading A's strip
     sk_to_lds<KIND>(p, acc, a_st, wm, wn, lane);
@@ -1116,16 +1112,6 @@ constexpr int kMidStrip = kMidTile * kRowBytes;  // 16 KiB per operand per stage
 // Relative cost per output element of the 128 x 128 kernel, in 64ths of the
 // 256-row kernel's (measured; see the host selector in launch<>).
 constexpr int kMidCost = 83;
-
-__device__ __forceinline__ float4_t_v mma_c(const half8_t &a, const half8_t &b,
-                                            const float4_t_v &c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float4_t_v mma_c(const int8_t_v &a, const int8_t_v &b,
-                                            const float4_t_v &c) {
-  // v_mfma_f32_16x16x128_f8f6f4, FP8 E4M3 operands, no block scales.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
-}
 
 // An operand of the 128 x 128 kernel in LDS.  K-major operands (K
 // contiguous: A of a 'T' op, B of an 'N' op) use the 128 x 128-byte strip of
