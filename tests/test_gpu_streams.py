@@ -1,0 +1,122 @@
+"""Stream ordering and graph capture of the C-ABI calls.
+
+Every entry point enqueues its kernel on the stream it is given and touches
+no other stream, allocates nothing and issues no memset, so its launches can be
+ordered on a side stream and captured into a HIP graph.  The tests below check
+both with +-1 inputs, whose products are small integers and must match the
+oracle exactly: a GEMM on a side stream that also produces its inputs, and a
+captured graph of four different calls (fp16 TN, fp8 TN, fp16 NN, batched
+QK^T) replayed several times.  Between replays, eager copies on the current
+stream put new inputs in place, and every replay is checked against the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dense_gemm_tn_amd as dg
+import oracle
+from dense_gemm_tn_amd import inputs
+from test_gpu_parity import DEV
+
+pytestmark = pytest.mark.gpu
+
+
+def exact(got_codes, ref, fmt):
+    want = oracle.decode(oracle.encode(ref, fmt), fmt)
+    got = oracle.decode(got_codes, fmt)
+    assert np.array_equal(got, want), "%d mismatches" % int((got != want).sum())
+
+
+def test_side_stream_orders_producer_and_gemm():
+    """Inputs written by kernels on a side stream, the GEMM queued behind them on
+    that stream, the result read after synchronising only that stream."""
+    M, N, K = 520, 392, 264
+    x = inputs.make_shape("f16", M, N, K, dist="pm1", seed=41)
+    a_host = torch.from_numpy(x["A"]).pin_memory()
+    b_host = torch.from_numpy(x["B"]).pin_memory()
+    side = torch.cuda.Stream(device=DEV)
+    with torch.cuda.stream(side):
+        a = torch.empty((M, K), dtype=torch.float16, device=DEV)
+        b = torch.empty((N, K), dtype=torch.float16, device=DEV)
+        c = torch.full((N, M), 7.0, dtype=torch.float16, device=DEV)
+        a.copy_(a_host, non_blocking=True)
+        b.copy_(b_host, non_blocking=True)
+        a.mul_(-1.0).mul_(-1.0)           # more producer kernels on the same stream
+        dg.gemm_f16_tn(a, b, c, M, N, K, K, K, M, stream=side)
+    side.synchronize()
+    print("side stream %dx%dx%d" % (M, N, K), flush=True)
+    exact(c.cpu().numpy().view(np.uint16), oracle.gemm_tn(x["A"], x["B"], oracle.FMT_F16, M, N, K),
+          oracle.FMT_F16)
+
+
+def test_graph_capture_replays_match_oracle():
+    shapes = {"f16": (264, 136, 200), "f8": (272, 144, 256), "nn": (136, 264, 200),
+              "qkt": (3, 200, 300, 128)}
+    M1, N1, K1 = shapes["f16"]
+    M2, N2, K2 = shapes["f8"]
+    M3, N3, K3 = shapes["nn"]
+    H, M4, N4, D4 = shapes["qkt"]
+    # Static device buffers the graph reads and writes.
+    a1 = torch.empty((M1, K1), dtype=torch.float16, device=DEV)
+    b1 = torch.empty((N1, K1), dtype=torch.float16, device=DEV)
+    c1 = torch.empty((N1, M1), dtype=torch.float16, device=DEV)
+    a2 = torch.empty((M2, K2), dtype=torch.uint8, device=DEV)
+    b2 = torch.empty((N2, K2), dtype=torch.uint8, device=DEV)
+    c2 = torch.empty((N2, M2), dtype=torch.int16, device=DEV)
+    a3 = torch.empty((K3, M3), dtype=torch.float16, device=DEV)    # 'N': A[m + k*lda]
+    b3 = torch.empty((N3, K3), dtype=torch.float16, device=DEV)    # 'N': B[k + n*ldb]
+    c3 = torch.empty((N3, M3), dtype=torch.float16, device=DEV)
+    q4 = torch.empty((H, M4, D4), dtype=torch.float16, device=DEV)
+    k4 = torch.empty((H, N4, D4), dtype=torch.float16, device=DEV)
+    s4 = torch.empty((H, N4, M4), dtype=torch.float16, device=DEV)
+
+    def calls():
+        dg.gemm_f16_tn(a1, b1, c1, M1, N1, K1, K1, K1, M1)
+        dg.gemm_f8_tn(a2, b2, c2, M2, N2, K2, K2, K2, M2, 1.0, 1.0)
+        dg.gemm_f16("N", "N", a3, b3, c3, M3, N3, K3, M3, K3, M3)
+        dg.gemm_batched_qkt(q4, k4, s4, H, M4, N4, D4, D4, D4, M4, M4 * D4, N4 * D4, N4 * M4)
+
+    def load(seed):
+        x1 = inputs.make_shape("f16", M1, N1, K1, dist="pm1", seed=seed)
+        x2 = inputs.make_shape("f8", M2, N2, K2, dist="pm1", seed=seed + 1)
+        x3 = inputs.make_shape("f16", M3, N3, K3, dist="pm1", seed=seed + 2)
+        x4 = inputs.make_shape("qkt", M4, N4, D4, dist="pm1", seed=seed + 3, batch=H)
+        a1.copy_(torch.from_numpy(x1["A"]))
+        b1.copy_(torch.from_numpy(x1["B"]))
+        a2.copy_(torch.from_numpy(x2["A"]))
+        b2.copy_(torch.from_numpy(x2["B"]))
+        a3.copy_(torch.from_numpy(np.ascontiguousarray(x3["A"].T)))
+        b3.copy_(torch.from_numpy(x3["B"]))
+        q4.copy_(torch.from_numpy(x4["Q"]))
+        k4.copy_(torch.from_numpy(x4["K"]))
+        for t in (c1, c2, c3, s4):
+            t.fill_(0)
+        torch.cuda.synchronize()
+        return x1, x2, x3, x4
+
+    def check(x1, x2, x3, x4):
+        exact(c1.cpu().numpy().view(np.uint16),
+              oracle.gemm_tn(x1["A"], x1["B"], oracle.FMT_F16, M1, N1, K1), oracle.FMT_F16)
+        exact(c2.cpu().numpy().view(np.uint16),
+              oracle.gemm_tn(x2["A"], x2["B"], oracle.FMT_E4M3FN, M2, N2, K2), oracle.FMT_BF16)
+        exact(c3.cpu().numpy().view(np.uint16),
+              oracle.gemm_tn(x3["A"], x3["B"], oracle.FMT_F16, M3, N3, K3), oracle.FMT_F16)
+        exact(s4.cpu().numpy().view(np.uint16),
+              oracle.batched_qkt(x4["Q"], x4["K"], H, M4, N4, D4), oracle.FMT_F16)
+
+    # Eager run first (also settles the library's one-time device queries).
+    xs = load(100)
+    calls()
+    torch.cuda.synchronize()
+    check(*xs)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):      # captures on its own (default-priority) stream
+        calls()
+    torch.cuda.synchronize()
+    for r in range(4):
+        print("graph replay %d" % r, flush=True)
+        xs = load(200 + 10 * r)
+        g.replay()
+        torch.cuda.synchronize()
+        check(*xs)
