@@ -5,9 +5,11 @@ no other stream, allocates nothing and issues no memset, so its launches can be
 ordered on a side stream and captured into a HIP graph.  The tests below check
 both with +-1 inputs, whose products are small integers and must match the
 oracle exactly: a GEMM on a side stream that also produces its inputs, and a
-captured graph of four different calls (fp16 TN, fp8 TN, fp16 NN, batched
-QK^T) replayed several times.  Between replays, eager copies on the current
-stream put new inputs in place, and every replay is checked against the oracle.
+captured graph of five different calls (fp16 TN, fp8 TN, fp16 NN, batched
+QK^T, fused attention) replayed several times.  Between replays, eager copies
+on the current stream put new inputs in place, and every replay is checked
+against the oracle (the attention output within its tolerance of
+test_gpu_attention).
 """
 import numpy as np
 import pytest
@@ -16,6 +18,7 @@ import torch
 import dense_gemm_tn_amd as dg
 import oracle
 from dense_gemm_tn_amd import inputs
+from test_gpu_attention import tol
 from test_gpu_parity import DEV
 
 pytestmark = pytest.mark.gpu
@@ -69,18 +72,27 @@ def test_graph_capture_replays_match_oracle():
     q4 = torch.empty((H, M4, D4), dtype=torch.float16, device=DEV)
     k4 = torch.empty((H, N4, D4), dtype=torch.float16, device=DEV)
     s4 = torch.empty((H, N4, M4), dtype=torch.float16, device=DEV)
+    H5, M5, N5, D5 = 2, 200, 328, 128
+    q5 = torch.empty((H5, M5, D5), dtype=torch.float16, device=DEV)
+    k5 = torch.empty((H5, N5, D5), dtype=torch.float16, device=DEV)
+    vt5 = torch.empty((H5, D5, N5), dtype=torch.float16, device=DEV)
+    o5 = torch.empty((H5, M5, D5), dtype=torch.float16, device=DEV)
+    scale5 = 1.0 / D5 ** 0.5
 
     def calls():
         dg.gemm_f16_tn(a1, b1, c1, M1, N1, K1, K1, K1, M1)
         dg.gemm_f8_tn(a2, b2, c2, M2, N2, K2, K2, K2, M2, 1.0, 1.0)
         dg.gemm_f16("N", "N", a3, b3, c3, M3, N3, K3, M3, K3, M3)
         dg.gemm_batched_qkt(q4, k4, s4, H, M4, N4, D4, D4, D4, M4, M4 * D4, N4 * D4, N4 * M4)
+        dg.attention_fwd_f16(q5, k5, vt5, o5, H5, M5, N5, D5, D5, D5, N5, D5, M5 * D5, N5 * D5,
+                             D5 * N5, M5 * D5, scale5)
 
     def load(seed):
         x1 = inputs.make_shape("f16", M1, N1, K1, dist="pm1", seed=seed)
         x2 = inputs.make_shape("f8", M2, N2, K2, dist="pm1", seed=seed + 1)
         x3 = inputs.make_shape("f16", M3, N3, K3, dist="pm1", seed=seed + 2)
         x4 = inputs.make_shape("qkt", M4, N4, D4, dist="pm1", seed=seed + 3, batch=H)
+        x5 = inputs.make_shape("attn", M5, N5, D5, seed=seed + 4, batch=H5)
         a1.copy_(torch.from_numpy(x1["A"]))
         b1.copy_(torch.from_numpy(x1["B"]))
         a2.copy_(torch.from_numpy(x2["A"]))
@@ -89,12 +101,15 @@ def test_graph_capture_replays_match_oracle():
         b3.copy_(torch.from_numpy(x3["B"]))
         q4.copy_(torch.from_numpy(x4["Q"]))
         k4.copy_(torch.from_numpy(x4["K"]))
-        for t in (c1, c2, c3, s4):
+        q5.copy_(torch.from_numpy(x5["Q"]))
+        k5.copy_(torch.from_numpy(x5["K"]))
+        vt5.copy_(torch.from_numpy(x5["Vt"]))
+        for t in (c1, c2, c3, s4, o5):
             t.fill_(0)
         torch.cuda.synchronize()
-        return x1, x2, x3, x4
+        return x1, x2, x3, x4, x5
 
-    def check(x1, x2, x3, x4):
+    def check(x1, x2, x3, x4, x5):
         exact(c1.cpu().numpy().view(np.uint16),
               oracle.gemm_tn(x1["A"], x1["B"], oracle.FMT_F16, M1, N1, K1), oracle.FMT_F16)
         exact(c2.cpu().numpy().view(np.uint16),
@@ -103,6 +118,11 @@ def test_graph_capture_replays_match_oracle():
               oracle.gemm_tn(x3["A"], x3["B"], oracle.FMT_F16, M3, N3, K3), oracle.FMT_F16)
         exact(s4.cpu().numpy().view(np.uint16),
               oracle.batched_qkt(x4["Q"], x4["K"], H, M4, N4, D4), oracle.FMT_F16)
+        o = o5.cpu().numpy().astype(np.float64)
+        rows = np.arange(M5)
+        for h in range(H5):
+            want = oracle.attention_rows(x5["Q"][h], x5["K"][h], x5["Vt"][h], N5, D5, rows, scale5)
+            assert np.all(np.abs(o[h] - want) <= tol(want, x5["Vt"][h])), h
 
     # Eager run first (also settles the library's one-time device queries).
     xs = load(100)
