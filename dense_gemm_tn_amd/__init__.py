@@ -36,6 +36,10 @@ EXPORTS = (
     "gemm_f16_config",
     "gemm_f8",
     "gemm_f8_config",
+    "gemm_f16_tn_splitk",
+    "gemm_f8_tn_splitk",
+    "gemm_splitk_workspace_bytes",
+    "gemm_splitk_choose",
 )
 
 _lib = None
@@ -72,9 +76,15 @@ def lib() -> ctypes.CDLL:
         L.gemm_f8.argtypes = [ctypes.c_char, ctypes.c_char, vp, vp, vp, i64, i64, i64, i64, i64,
                               i64, f32, f32, vp]
         L.gemm_f8_config.argtypes = [ctypes.c_char, ctypes.c_char, i64, i64, i64]
+        L.gemm_f16_tn_splitk.argtypes = [vp, vp, vp] + [i64] * 7 + [vp, i64, vp]
+        L.gemm_f8_tn_splitk.argtypes = [vp, vp, vp] + [i64] * 6 + [f32, f32, i64, vp, i64, vp]
+        L.gemm_splitk_workspace_bytes.argtypes = [i64, i64, i64]
+        L.gemm_splitk_workspace_bytes.restype = i64
+        L.gemm_splitk_choose.argtypes = [ctypes.c_int, i64, i64, i64]
+        L.gemm_splitk_choose.restype = i64
         for f in (L.gemm_f16_tn, L.gemm_f16, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
                   L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config, L.gemm_f16_config,
-                  L.gemm_f8, L.gemm_f8_config):
+                  L.gemm_f8, L.gemm_f8_config, L.gemm_f16_tn_splitk, L.gemm_f8_tn_splitk):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -141,6 +151,34 @@ def gemm_f8_tn(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
     """C = bf16(fp32(scale_a*scale_b) * A x B) with E4M3FN A, B and fp32 accumulation."""
     _check("gemm_f8_tn", lib().gemm_f8_tn(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                                           float(scale_a), float(scale_b), _stream(stream)))
+
+
+def splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
+    """Bytes of workspace the split-K calls need (-1 for invalid arguments)."""
+    return int(lib().gemm_splitk_workspace_bytes(M, N, splits))
+
+
+def splitk_choose(M: int, N: int, K: int, fp8: bool = False) -> int:
+    """The library's suggested split count for an M x N x K TN product."""
+    return int(lib().gemm_splitk_choose(1 if fp8 else 0, M, N, K))
+
+
+def gemm_f16_tn_splitk(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
+                       splits: int, workspace, workspace_bytes: int, stream=None) -> None:
+    """gemm_f16_tn with K cut into up to `splits` ranges summed through an fp32 workspace."""
+    _check("gemm_f16_tn_splitk",
+           lib().gemm_f16_tn_splitk(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc, splits,
+                                    _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def gemm_f8_tn_splitk(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
+                      scale_a: float, scale_b: float, splits: int, workspace,
+                      workspace_bytes: int, stream=None) -> None:
+    """gemm_f8_tn with K cut into up to `splits` ranges summed through an fp32 workspace."""
+    _check("gemm_f8_tn_splitk",
+           lib().gemm_f8_tn_splitk(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                                   float(scale_a), float(scale_b), splits, _ptr(workspace),
+                                   workspace_bytes, _stream(stream)))
 
 
 def gemm_batched_qkt(Q, Kmat, S, batch: int, M: int, N: int, D: int, ldq: int, ldk: int,

@@ -163,6 +163,12 @@ struct Params {
   int32_t c_vec_ok;      // 8-byte C stores are aligned (ldc % 4 == 0)
   int32_t c_vec16_ok;    // 16-byte C stores are aligned (ldc % 8 == 0)
   int32_t sk_walk;       // skinny-K kernel: consecutive M tiles per block
+  // Split-K partial products (128 x 128 kernel): split h covers K elements
+  // [h * k_slice, min((h + 1) * k_slice, K)) and writes fp32 partial sums to
+  // W + h * N * ldw, column-major with leading dimension ldw.
+  int64_t k_slice;
+  float *W;
+  int64_t ldw;
 };
 
 // Logical tile -> (head, tile_m, tile_n): the grouped order inside a head,
@@ -1187,9 +1193,10 @@ __device__ __forceinline__ void mid_copy(const uint8_t *base, int64_t ld_b, int6
   }
 }
 
-template <int KIND, bool AMN, bool BMN>
+template <int KIND, bool AMN, bool BMN, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   typedef Traits<KIND> T;
+  static_assert(!SPLIT || (!AMN && !BMN), "split-K partials are TN only");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * 2 * kMidStrip];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1197,14 +1204,20 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   int head, tm, tn;
   tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
   const int64_t m0 = (int64_t)tm * kMidTile, n0 = (int64_t)tn * kMidTile;
+  // Split-K: the "head" index is the split; this block's K range starts at
+  // k_begin (a whole number of K-steps) and the operands are read from there.
+  const int64_t k_begin = SPLIT ? head * p.k_slice : 0;
+  const int64_t Kx = SPLIT ? ((p.K - k_begin) < p.k_slice ? (p.K - k_begin) : p.k_slice) : p.K;
   // Block bases: K-major operands at their first row, M/N-major ones at their
   // first column (element m0 / n0 of K-row 0).
-  const uint8_t *Ab = p.A + head * p.stride_a_b + (AMN ? m0 * T::es : m0 * p.lda_b);
-  const uint8_t *Bb = p.B + head * p.stride_b_b + (BMN ? n0 * T::es : n0 * p.ldb_b);
+  const uint8_t *Ab = SPLIT ? p.A + m0 * p.lda_b + k_begin * T::es
+                            : p.A + head * p.stride_a_b + (AMN ? m0 * T::es : m0 * p.lda_b);
+  const uint8_t *Bb = SPLIT ? p.B + n0 * p.ldb_b + k_begin * T::es
+                            : p.B + head * p.stride_b_b + (BMN ? n0 * T::es : n0 * p.ldb_b);
   uint8_t *Cb = p.C + head * p.stride_c_b;
   const int64_t rows_a = (p.M - m0) < kMidTile ? (p.M - m0) : kMidTile;
   const int64_t rows_b = (p.N - n0) < kMidTile ? (p.N - n0) : kMidTile;
-  const uint32_t kbytes = (uint32_t)(p.K * T::es);
+  const uint32_t kbytes = (uint32_t)(Kx * T::es);
 
   // K-major copies: load q (0..3) of wave w fills strip rows 32q + 8w .. +7;
   // lane l lands in row 32q + 8w + (l >> 3), slot l & 7, and fetches the chunk
@@ -1240,12 +1253,12 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   const uint32_t qs_a = (uint32_t)(32 * p.lda_b), qs_b = (uint32_t)(32 * p.ldb_b);
   const uint32_t rec_a = AMN ? 0u : (uint32_t)((rows_a - 1) * p.lda_b) + kbytes;
   const uint32_t rec_b = BMN ? 0u : (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes;
-  const int64_t nk = (p.K + T::kstep - 1) / T::kstep;
+  const int64_t nk = (Kx + T::kstep - 1) / T::kstep;
 
   auto copy_step = [&](int64_t t) {
     lds_u8 *st = (lds_u8 *)smem + (t & 1) * 2 * kMidStrip + wave * 1024;
-    mid_copy<KIND, AMN, AMN || BMN>(Ab, p.lda_b, p.K, rec_a, voff_a, qs_a, kchunk, opa, t, st);
-    mid_copy<KIND, BMN, AMN || BMN>(Bb, p.ldb_b, p.K, rec_b, voff_b, qs_b, kchunk, opb, t,
+    mid_copy<KIND, AMN, AMN || BMN>(Ab, p.lda_b, Kx, rec_a, voff_a, qs_a, kchunk, opa, t, st);
+    mid_copy<KIND, BMN, AMN || BMN>(Bb, p.ldb_b, Kx, rec_b, voff_b, qs_b, kchunk, opb, t,
                                     st + kMidStrip);
   };
 
@@ -1327,6 +1340,28 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   // Lane (rl, grp) of tile (i, j) holds C rows 16i + 4 grp .. +3 of column
   // 16j + rl of the wave's 64 x 64 block.
   const int64_t mb = m0 + wm * 64 + 4 * grp, nb = n0 + wn * 64 + rl;
+  if constexpr (SPLIT) {
+    // fp32 partial sums, 16 bytes per lane (ldw % 4 == 0, so aligned).
+    float *Wh = p.W + head * p.N * p.ldw;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = nb + 16 * j;
+      if (n >= p.N) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = mb + 16 * i;
+        float *dst = Wh + n * p.ldw + m;
+        if (m + 3 < p.M) {
+          *(float4_t_v *)dst = acc[i][j];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (m + e < p.M) dst[e] = acc[i][j][e];
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t n = nb + 16 * j;
@@ -1347,6 +1382,35 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
           if (m + e < p.M) dst[e] = h[e];
       }
     }
+  }
+}
+
+// Split-K reduction: C(m, n) = convert(sum over splits h = 0, 1, ... of
+// W[h][n][m]) in that fixed order (deterministic), the conversion of the
+// epilogue (fp16, or bf16 of the fp32 sum times the scale product).  One
+// thread per four consecutive rows of a column: 16-byte partial loads.
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void gemm_splitk_reduce_kernel(Params p, int32_t splits) {
+  const int64_t quads = (p.M + 3) / 4;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= quads * p.N) return;
+  const int64_t n = idx / quads, m = 4 * (idx - n * quads);
+  const float *src = p.W + n * p.ldw + m;
+  float4_t_v sum = *(const float4_t_v *)src;
+  for (int32_t h = 1; h < splits; ++h) {
+    const float4_t_v v = __builtin_nontemporal_load((const float4_t_v *)(src + h * p.N * p.ldw));
+    sum += v;
+  }
+  uint32_t w0, w1;
+  pack_run<KIND>(p, sum, 0, w0, w1);
+  uint16_t *dst = (uint16_t *)p.C + (n * p.ldc + m);
+  if (p.c_vec_ok && m + 3 < p.M) {
+    *(uint2 *)dst = uint2{w0, w1};
+  } else {
+    const uint16_t h4[4] = {(uint16_t)w0, (uint16_t)(w0 >> 16), (uint16_t)w1, (uint16_t)(w1 >> 16)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (m + e < p.M) dst[e] = h4[e];
   }
 }
 
@@ -1620,13 +1684,12 @@ static Config choose_config(int es, int64_t M, int64_t N, int64_t K, int64_t bat
   return Config{ntn == 7 ? kCfg224 : kCfg256};
 }
 
-template <int KIND>
-static int launch(const Problem &pr, hipStream_t stream) {
-  typedef Traits<KIND> T;
-  const int es = T::es;
+// Host-side validation of a TN call (the rules the header states); -1 for a
+// valid call with nothing to do (M, N or batch 0).
+static int check_tn(const Problem &pr, int es) {
   if (pr.batch < 0 || pr.M < 0 || pr.N < 0 || pr.K < 0) return DG_ERR_INVALID_ARGUMENT;
   if (pr.lda < pr.K || pr.ldb < pr.K || pr.ldc < pr.M) return DG_ERR_INVALID_ARGUMENT;
-  if (pr.batch == 0 || pr.M == 0 || pr.N == 0) return DG_OK;
+  if (pr.batch == 0 || pr.M == 0 || pr.N == 0) return -1;  // a valid no-op
   if (!pr.A || !pr.B || !pr.C) return DG_ERR_INVALID_ARGUMENT;
   if (pr.batch > 1 && (pr.stride_a < 0 || pr.stride_b < 0 || pr.stride_c < 0))
     return DG_ERR_INVALID_ARGUMENT;
@@ -1654,6 +1717,16 @@ static int launch(const Problem &pr, hipStream_t stream) {
   if (strip_a >= (int64_t)kOob || strip_b >= (int64_t)kOob || reach_a >= (int64_t)kOob ||
       reach_b >= (int64_t)kOob)
     return DG_ERR_UNSUPPORTED;
+  return DG_OK;
+}
+
+template <int KIND>
+static int launch(const Problem &pr, hipStream_t stream) {
+  typedef Traits<KIND> T;
+  const int es = T::es;
+  const int chk = check_tn(pr, es);
+  if (chk < 0) return DG_OK;
+  if (chk != DG_OK) return chk;
 
   const Config cfg = choose_config(es, pr.M, pr.N, pr.K, pr.batch);
   const bool skinny = cfg.kind == kCfgSkinny, mid = cfg.kind == kCfgMid;
@@ -1675,7 +1748,7 @@ static int launch(const Problem &pr, hipStream_t stream) {
   const int64_t blocks = ((tiles_m + walk - 1) / walk) * tiles_n * pr.batch;
   if (blocks > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;
 
-  Params p;
+  Params p = {};
   p.A = (const uint8_t *)pr.A;
   p.B = (const uint8_t *)pr.B;
   p.C = (uint8_t *)pr.C;
@@ -1758,7 +1831,7 @@ static int launch_layout(char ta, char tb, const Problem &pr, hipStream_t stream
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;
 
-  Params p;
+  Params p = {};
   p.A = (const uint8_t *)pr.A;
   p.B = (const uint8_t *)pr.B;
   p.C = (uint8_t *)pr.C;
@@ -1783,6 +1856,85 @@ static int launch_layout(char ta, char tb, const Problem &pr, hipStream_t stream
   const kernel_t k = mid ? mids[li] : bigs[li];
   hipLaunchKernelGGL(k, grid, block, 0, stream, p);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
+}
+
+// Split-K for grids of few output tiles with a long K (128 x 128 tiles): split
+// h of S multiplies the K range [h * k_slice, (h + 1) * k_slice) of every tile
+// into an fp32 partial in the caller's workspace, and one reduction kernel sums
+// the S partials in split order and converts.  k_slice is a whole number of
+// K-steps, so every split starts on a step boundary; S = ceil(K-steps /
+// steps per split) <= the requested count.
+constexpr int64_t kSplitMax = 64;
+
+static int64_t splitk_ldw(int64_t M) { return (M + 3) / 4 * 4; }
+
+template <int KIND>
+static int launch_splitk(const Problem &pr, int64_t splits, void *ws, int64_t ws_bytes,
+                         hipStream_t stream) {
+  typedef Traits<KIND> T;
+  const int es = T::es;
+  if (splits < 1 || splits > kSplitMax || ws_bytes < 0) return DG_ERR_INVALID_ARGUMENT;
+  const int chk = check_tn(pr, es);
+  if (chk < 0) return DG_OK;
+  if (chk != DG_OK) return chk;
+  const int64_t nk = (pr.K + T::kstep - 1) / T::kstep;
+  const int64_t per = nk > 0 ? (nk + splits - 1) / splits : 0;   // K-steps per split
+  const int64_t S = per > 0 ? (nk + per - 1) / per : 0;
+  if (S <= 1) return launch<KIND>(pr, stream);
+  const int64_t ldw = splitk_ldw(pr.M);
+  const uint64_t need = (uint64_t)splits * (uint64_t)pr.N * (uint64_t)ldw * 4u;
+  if (!ws || (uint64_t)ws_bytes < need) return DG_ERR_INVALID_ARGUMENT;
+  const uint64_t used = (uint64_t)S * (uint64_t)pr.N * (uint64_t)ldw * 4u;
+  if (overlaps(ws, used, pr.A, span_bytes(pr.M, pr.K, pr.lda, es)) ||
+      overlaps(ws, used, pr.B, span_bytes(pr.N, pr.K, pr.ldb, es)) ||
+      overlaps(ws, used, pr.C, span_bytes(pr.N, pr.M, pr.ldc, 2)))
+    return DG_ERR_INVALID_ARGUMENT;
+  if (!aligned16(ws)) return DG_ERR_UNSUPPORTED;
+  const int64_t tiles_m = (pr.M + kMidTile - 1) / kMidTile;
+  const int64_t tiles_n = (pr.N + kMidTile - 1) / kMidTile;
+  const int64_t blocks = tiles_m * tiles_n * S;
+  const int64_t quads = ldw / 4 * pr.N;
+  const int64_t rblocks = (quads + kThreads - 1) / kThreads;
+  if (blocks > 0x7fffffffLL || rblocks > 0x7fffffffLL) return DG_ERR_UNSUPPORTED;
+
+  Params p = {};
+  p.A = (const uint8_t *)pr.A;
+  p.B = (const uint8_t *)pr.B;
+  p.C = (uint8_t *)pr.C;
+  p.M = pr.M; p.N = pr.N; p.K = pr.K;
+  p.lda_b = pr.lda * es; p.ldb_b = pr.ldb * es; p.ldc = pr.ldc;
+  p.tiles_m = (int32_t)tiles_m; p.tiles_n = (int32_t)tiles_n;
+  p.scale = pr.scale;
+  p.c_vec_ok = (pr.ldc % 4 == 0) ? 1 : 0;
+  p.c_vec16_ok = (pr.ldc % 8 == 0) ? 1 : 0;
+  p.sk_walk = 1;
+  p.k_slice = per * T::kstep;
+  p.W = (float *)ws;
+  p.ldw = ldw;
+  hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false, true>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return DG_ERR_HIP;
+  hipLaunchKernelGGL(gemm_splitk_reduce_kernel<KIND>, dim3((unsigned)rblocks), dim3(kThreads), 0,
+                     stream, p, (int32_t)S);
+  return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
+}
+
+// Suggested split count: enough 128 x 128 tile splits to give every CU a
+// block, each split keeping at least kSplitMinSteps K-steps; 1 when the tiles
+// alone fill half the CUs or K is short.
+constexpr int64_t kSplitMinSteps = 16;
+static int64_t choose_splits(int es, int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 1;
+  const int64_t kstep = 128 / es;
+  const int64_t nk = (K + kstep - 1) / kstep;
+  const int64_t tiles = ((M + kMidTile - 1) / kMidTile) * ((N + kMidTile - 1) / kMidTile);
+  const int64_t cus = cu_count();
+  if (2 * tiles >= cus) return 1;
+  int64_t s = (cus + tiles - 1) / tiles;
+  const int64_t by_k = nk / kSplitMinSteps;
+  if (s > by_k) s = by_k;
+  if (s > kSplitMax) s = kSplitMax;
+  return s < 1 ? 1 : s;
 }
 
 }  // namespace dg
@@ -1867,6 +2019,31 @@ int gemm_f8_config(char transa, char transb, int64_t M, int64_t N, int64_t K) {
 int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch) {
   if (M < 0 || N < 0 || K < 0 || batch < 0) return -1;
   return dg::choose_config(fp8 ? 1 : 2, M, N, K, batch).kind;
+}
+
+int64_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) {
+  if (M < 0 || N < 0 || splits < 1 || splits > dg::kSplitMax) return -1;
+  return splits * N * dg::splitk_ldw(M) * 4;
+}
+
+int64_t gemm_splitk_choose(int fp8, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+  return dg::choose_splits(fp8 ? 1 : 2, M, N, K);
+}
+
+int gemm_f16_tn_splitk(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc, int64_t splits, void *workspace,
+                       int64_t workspace_bytes, void *stream) {
+  dg::Problem pr{A, B, C, 1, M, N, K, lda, ldb, ldc, 0, 0, 0, 1.0f};
+  return dg::launch_splitk<dg::kF16>(pr, splits, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int gemm_f8_tn_splitk(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldc, float scale_a, float scale_b,
+                      int64_t splits, void *workspace, int64_t workspace_bytes, void *stream) {
+  const float s = scale_a * scale_b;
+  dg::Problem pr{A, B, C, 1, M, N, K, lda, ldb, ldc, 0, 0, 0, s};
+  return dg::launch_splitk<dg::kF8>(pr, splits, workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 }  // extern "C"

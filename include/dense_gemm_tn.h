@@ -243,6 +243,53 @@ int gemm_f16_config(char transa, char transb, int64_t M, int64_t N, int64_t K);
 /* The same for gemm_f8 (TN: gemm_tn_config with fp8 != 0). */
 int gemm_f8_config(char transa, char transb, int64_t M, int64_t N, int64_t K);
 
+/*
+ * Split-K TN GEMM for grids of few output tiles with a long K (small M x N,
+ * large K), where one block per tile would leave most compute units idle.
+ * Same product, rounding, validation and ownership as gemm_f16_tn /
+ * gemm_f8_tn; in addition K is cut into at most `splits` ranges of whole
+ * K-steps (64 fp16 or 128 fp8 elements), each multiplied into an fp32 partial
+ * in the caller's `workspace`, and a second kernel on the same stream sums
+ * the partials in range order (deterministic) and rounds once into C.  The
+ * result differs from the unsplit call only by fp32 summation order.
+ *   splits     1 .. 64; 1 (or a K too short to split) is exactly gemm_*_tn
+ *              and does not touch the workspace.  gemm_splitk_choose suggests
+ *              a count.
+ *   workspace  device memory, 16-byte aligned, at least
+ *              gemm_splitk_workspace_bytes(M, N, splits) bytes, overlapping
+ *              none of A, B and C; owned by the caller, contents undefined
+ *              afterwards, and it must not be used by other work on another
+ *              stream until this call's kernels have run.
+ * Errors: as for gemm_f16_tn / gemm_f8_tn, plus DG_ERR_INVALID_ARGUMENT for
+ * splits outside 1 .. 64, a null or too-small workspace (when the call does
+ * split) or one overlapping an operand, and DG_ERR_UNSUPPORTED for a
+ * misaligned one.
+ * Source: "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", sections "Final
+ * results" and "Further tuning" (one tile configuration is wrong for small or
+ * skinny products; a library needs a set of configurations and a selector).
+ */
+int gemm_f16_tn_splitk(const void *A, const void *B, void *C,
+                       int64_t M, int64_t N, int64_t K,
+                       int64_t lda, int64_t ldb, int64_t ldc,
+                       int64_t splits, void *workspace, int64_t workspace_bytes,
+                       void *stream);
+int gemm_f8_tn_splitk(const void *A, const void *B, void *C,
+                      int64_t M, int64_t N, int64_t K,
+                      int64_t lda, int64_t ldb, int64_t ldc,
+                      float scale_a, float scale_b,
+                      int64_t splits, void *workspace, int64_t workspace_bytes,
+                      void *stream);
+
+/* Workspace bytes the split-K calls need for M x N and `splits`:
+ * splits * N * (M rounded up to 4) * 4; -1 for invalid arguments. */
+int64_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
+
+/* Suggested split count for an M x N x K TN product (fp8 != 0: FP8): enough
+ * splits of the 128 x 128 tiles to give every compute unit a block, each
+ * keeping at least 16 K-steps; 1 when the tiles alone fill half the compute
+ * units.  -1 for negative sizes. */
+int64_t gemm_splitk_choose(int fp8, int64_t M, int64_t N, int64_t K);
+
 #ifdef __cplusplus
 }
 #endif

@@ -311,3 +311,53 @@ def torch_device_count():
         return torch.cuda.device_count()
     except Exception:
         return 0
+
+
+def splitk(*args):
+    return dg.lib().gemm_f16_tn_splitk(*args, None)
+
+
+# 128 x 128 x 8192: 128 K-steps, so any split count >= 2 really splits and the
+# workspace checks run (with these fake addresses nothing may be launched).
+SK = (A_ADDR, B_ADDR, C_ADDR, 128, 128, 8192, 8192, 8192, 128)
+SK_NEED = 4 * 128 * 128 * 4
+
+
+@pytest.mark.parametrize("tail,status", [
+    ((0, 0x20000000, SK_NEED), dg.DG_ERR_INVALID_ARGUMENT),               # splits < 1
+    ((65, 0x20000000, 65 * 128 * 128 * 4), dg.DG_ERR_INVALID_ARGUMENT),   # splits > 64
+    ((4, None, SK_NEED), dg.DG_ERR_INVALID_ARGUMENT),                     # no workspace
+    ((4, 0x20000000, SK_NEED - 4), dg.DG_ERR_INVALID_ARGUMENT),           # too small
+    ((4, 0x20000000, -1), dg.DG_ERR_INVALID_ARGUMENT),                    # negative size
+    ((4, A_ADDR + 4096, SK_NEED), dg.DG_ERR_INVALID_ARGUMENT),            # overlaps A
+    ((4, C_ADDR, SK_NEED), dg.DG_ERR_INVALID_ARGUMENT),                   # overlaps C
+    ((4, 0x20000008, SK_NEED), dg.DG_ERR_UNSUPPORTED),                    # misaligned
+])
+def test_splitk_validation(tail, status):
+    assert splitk(*SK, *tail) == status
+
+
+def test_splitk_validation_keeps_tn_rules():
+    # K % 8 and a null A fail as for gemm_f16_tn, before the workspace is looked at.
+    assert splitk(A_ADDR, B_ADDR, C_ADDR, 128, 128, 8188, 8192, 8192, 128, 4, None, 0) == \
+        dg.DG_ERR_UNSUPPORTED
+    assert splitk(None, B_ADDR, C_ADDR, 128, 128, 8192, 8192, 8192, 128, 4, None, 0) == \
+        dg.DG_ERR_INVALID_ARGUMENT
+    assert splitk(None, None, None, 0, 128, 8192, 8192, 8192, 128, 4, None, 0) == dg.DG_OK
+    assert dg.lib().gemm_f8_tn_splitk(A_ADDR, B_ADDR, C_ADDR, 128, 128, 8192, 8192, 8192, 128,
+                                      1.0, 1.0, 4, None, 0, None) == dg.DG_ERR_INVALID_ARGUMENT
+
+
+def test_splitk_workspace_and_choice():
+    assert dg.splitk_workspace_bytes(130, 7, 3) == 3 * 7 * 132 * 4
+    assert dg.splitk_workspace_bytes(1, 1, 64) == 64 * 4 * 4
+    assert dg.splitk_workspace_bytes(8, 8, 0) == -1
+    assert dg.splitk_workspace_bytes(8, 8, 65) == -1
+    assert dg.splitk_workspace_bytes(-1, 8, 2) == -1
+    # Few tiles and a long K split; a full grid or a short K does not.
+    assert dg.splitk_choose(512, 512, 32768) > 1
+    assert dg.splitk_choose(256, 256, 1 << 20) == 64
+    assert dg.splitk_choose(4096, 4096, 4096) == 1
+    assert dg.splitk_choose(512, 512, 1024) == 1
+    assert dg.splitk_choose(512, 512, 0) == 1
+    assert dg.splitk_choose(-1, 512, 4096) == -1
