@@ -18,7 +18,8 @@ FP8 8192^3 workload, the fused attention forward over 64 heads x 4096 queries x
 4096 keys x head dim 128 (4*M*N*D flops per head: two products), FP16 2048^3
 (a grid the 256-wide tiles cannot fill, served by the 128 x 128 kernel), FP16
 4096^3 and FP8 8192^3 in the NN, TT and NT op codes (operands read as they lie,
-no transpose pass), the 8-wave ping-pong kernel forced on the FP16 4096^3 and FP8 8192^3
+no transpose pass), FP16 512 x 512 x 32768 (16 output tiles, long K) without and
+with split-K, the 8-wave ping-pong kernel forced on the FP16 4096^3 and FP8 8192^3
 problems (a measured counter-design), and any other requested workload are
 reported under "workloads" in the same line.  `roofline` is for the FP16 kernel; `traffic`
 comes from a stored rocprofv3 counter summary and is null when the kernel
@@ -59,6 +60,8 @@ def kernel_name(w):
         if cfg_of(layout[0], layout[1], w.M, w.N, w.K) == 2:
             return "gemm_tn_mid_kernel<%d, %s, %s>" % (kind, amn, bmn)
         return "gemm_tn_kernel<%d, 8, %s, %s>" % (kind, amn, bmn)
+    if w.extra.get("splitk") and dg.splitk_choose(w.M, w.N, w.K, fp8=(w.kind == "f8")) > 1:
+        return "gemm_tn_mid_kernel<%d, false, false, true>" % kind
     cfg = dg.tn_config(w.M, w.N, w.K, w.batch, fp8=(w.kind == "f8"))
     return {0: "gemm_tn_kernel<%d, 8, false, false>" % kind,
             1: "gemm_tn_kernel<%d, 7, false, false>" % kind,
@@ -138,6 +141,12 @@ def make_launcher(w, dev):
             sets.append((a, b, c))
 
     scale = 1.0 / w.K ** 0.5
+    splits, ws, ws_bytes = 1, None, 0
+    if w.extra.get("splitk"):
+        # One workspace serves every set: the launches are ordered on one stream.
+        splits = dg.splitk_choose(w.M, w.N, w.K, fp8=(w.kind == "f8"))
+        ws_bytes = dg.splitk_workspace_bytes(w.M, w.N, splits)
+        ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev)
 
     def launch(i):
         if w.kind == "attn":
@@ -149,6 +158,8 @@ def make_launcher(w, dev):
         if w.kind == "f16" and layout != "TN":
             dg.gemm_f16(layout[0], layout[1], a, b, c, w.M, w.N, w.K, a.stride(0), b.stride(0),
                         w.M)
+        elif w.kind == "f16" and splits > 1:
+            dg.gemm_f16_tn_splitk(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M, splits, ws, ws_bytes)
         elif w.kind == "f16":
             dg.gemm_f16_tn(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M)
         elif w.kind == "f8" and layout != "TN":
@@ -266,7 +277,8 @@ def main():
     ap.add_argument("--workload", action="append", default=None,
                     help="workload names (default: f16_4096, f8_8192, "
                          "attn_64x4096x4096x128, f16_2048, the NN/TT/NT layouts of f16_4096 "
-                         "and f8_8192, and the ping-pong kernel on both)")
+                         "and f8_8192, 512 x 512 x 32768 without and with split-K, and the "
+                         "ping-pong kernel on f16_4096 and f8_8192)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (a known-size kernel for "
@@ -298,6 +310,7 @@ def main():
     names = args.workload or ["f16_4096", "f8_8192", "attn_64x4096x4096x128", "f16_2048",
                               "f16_nn_4096", "f16_tt_4096", "f16_nt_4096",
                               "f8_nn_8192", "f8_tt_8192", "f8_nt_8192",
+                              "f16_512x512x32768", "f16_512x512x32768_splitk",
                               "f16_4096_pingpong", "f8_8192_pingpong"]
     head = "f16_4096" if "f16_4096" in names else names[0]
     results = {}

@@ -1396,11 +1396,21 @@ __global__ __launch_bounds__(kThreads) void gemm_splitk_reduce_kernel(Params p, 
   if (idx >= quads * p.N) return;
   const int64_t n = idx / quads, m = 4 * (idx - n * quads);
   const float *src = p.W + n * p.ldw + m;
+  const int64_t hs = p.N * p.ldw;   // floats between consecutive splits
   float4_t_v sum = *(const float4_t_v *)src;
-  for (int32_t h = 1; h < splits; ++h) {
-    const float4_t_v v = __builtin_nontemporal_load((const float4_t_v *)(src + h * p.N * p.ldw));
-    sum += v;
+  int32_t h = 1;
+  // Four loads in flight before their (in-order) additions.
+  for (; h + 3 < splits; h += 4) {
+    const float4_t_v v0 = __builtin_nontemporal_load((const float4_t_v *)(src + h * hs));
+    const float4_t_v v1 = __builtin_nontemporal_load((const float4_t_v *)(src + (h + 1) * hs));
+    const float4_t_v v2 = __builtin_nontemporal_load((const float4_t_v *)(src + (h + 2) * hs));
+    const float4_t_v v3 = __builtin_nontemporal_load((const float4_t_v *)(src + (h + 3) * hs));
+    sum += v0;
+    sum += v1;
+    sum += v2;
+    sum += v3;
   }
+  for (; h < splits; ++h) sum += __builtin_nontemporal_load((const float4_t_v *)(src + h * hs));
   uint32_t w0, w1;
   pack_run<KIND>(p, sum, 0, w0, w1);
   uint16_t *dst = (uint16_t *)p.C + (n * p.ldc + m);

@@ -71,6 +71,11 @@ WORKLOADS = {
                  extra={"layout": "TT"}),
         Workload("f8_nt_8192", "f8", 8192, 8192, 8192, "normal", seed=0,
                  extra={"layout": "NT"}),
+        # Few output tiles, long K: 16 tiles of 128 x 128 over K = 32768, one
+        # block per tile, and the same product split along K over a workspace.
+        Workload("f16_512x512x32768", "f16", 512, 512, 32768, "normal", seed=0),
+        Workload("f16_512x512x32768_splitk", "f16", 512, 512, 32768, "normal", seed=0,
+                 extra={"splitk": True}),
         # The 8-wave ping-pong form of the 256 x 256 tile, forced (a measured
         # counter-design; the library never picks it by itself).
         Workload("f16_4096_pingpong", "f16", 4096, 4096, 4096, "normal", seed=0,
