@@ -5,8 +5,9 @@ no other stream, allocates nothing and issues no memset, so its launches can be
 ordered on a side stream and captured into a HIP graph.  The tests below check
 both with +-1 inputs, whose products are small integers and must match the
 oracle exactly: a GEMM on a side stream that also produces its inputs, and a
-captured graph of five different calls (fp16 TN, fp8 TN, fp16 NN, batched
-QK^T, fused attention) replayed several times.  Between replays, eager copies
+captured graph of six different calls (fp16 TN, fp8 TN, fp16 NN, batched
+QK^T, fused attention, split-K fp16 TN with its workspace) replayed several
+times.  Between replays, eager copies
 on the current stream put new inputs in place, and every replay is checked
 against the oracle (the attention output within its tolerance of
 test_gpu_attention).
@@ -78,6 +79,12 @@ def test_graph_capture_replays_match_oracle():
     vt5 = torch.empty((H5, D5, N5), dtype=torch.float16, device=DEV)
     o5 = torch.empty((H5, M5, D5), dtype=torch.float16, device=DEV)
     scale5 = 1.0 / D5 ** 0.5
+    M6, N6, K6, S6 = 136, 200, 4096, 4
+    a6 = torch.empty((M6, K6), dtype=torch.float16, device=DEV)
+    b6 = torch.empty((N6, K6), dtype=torch.float16, device=DEV)
+    c6 = torch.empty((N6, M6), dtype=torch.float16, device=DEV)
+    ws6_bytes = dg.splitk_workspace_bytes(M6, N6, S6)
+    ws6 = torch.empty(ws6_bytes // 4, dtype=torch.float32, device=DEV)
 
     def calls():
         dg.gemm_f16_tn(a1, b1, c1, M1, N1, K1, K1, K1, M1)
@@ -86,6 +93,7 @@ def test_graph_capture_replays_match_oracle():
         dg.gemm_batched_qkt(q4, k4, s4, H, M4, N4, D4, D4, D4, M4, M4 * D4, N4 * D4, N4 * M4)
         dg.attention_fwd_f16(q5, k5, vt5, o5, H5, M5, N5, D5, D5, D5, N5, D5, M5 * D5, N5 * D5,
                              D5 * N5, M5 * D5, scale5)
+        dg.gemm_f16_tn_splitk(a6, b6, c6, M6, N6, K6, K6, K6, M6, S6, ws6, ws6_bytes)
 
     def load(seed):
         x1 = inputs.make_shape("f16", M1, N1, K1, dist="pm1", seed=seed)
@@ -93,6 +101,7 @@ def test_graph_capture_replays_match_oracle():
         x3 = inputs.make_shape("f16", M3, N3, K3, dist="pm1", seed=seed + 2)
         x4 = inputs.make_shape("qkt", M4, N4, D4, dist="pm1", seed=seed + 3, batch=H)
         x5 = inputs.make_shape("attn", M5, N5, D5, seed=seed + 4, batch=H5)
+        x6 = inputs.make_shape("f16", M6, N6, K6, dist="pm1", seed=seed + 5)
         a1.copy_(torch.from_numpy(x1["A"]))
         b1.copy_(torch.from_numpy(x1["B"]))
         a2.copy_(torch.from_numpy(x2["A"]))
@@ -104,12 +113,14 @@ def test_graph_capture_replays_match_oracle():
         q5.copy_(torch.from_numpy(x5["Q"]))
         k5.copy_(torch.from_numpy(x5["K"]))
         vt5.copy_(torch.from_numpy(x5["Vt"]))
-        for t in (c1, c2, c3, s4, o5):
+        a6.copy_(torch.from_numpy(x6["A"]))
+        b6.copy_(torch.from_numpy(x6["B"]))
+        for t in (c1, c2, c3, s4, o5, c6, ws6):
             t.fill_(0)
         torch.cuda.synchronize()
-        return x1, x2, x3, x4, x5
+        return x1, x2, x3, x4, x5, x6
 
-    def check(x1, x2, x3, x4, x5):
+    def check(x1, x2, x3, x4, x5, x6):
         exact(c1.cpu().numpy().view(np.uint16),
               oracle.gemm_tn(x1["A"], x1["B"], oracle.FMT_F16, M1, N1, K1), oracle.FMT_F16)
         exact(c2.cpu().numpy().view(np.uint16),
@@ -123,6 +134,8 @@ def test_graph_capture_replays_match_oracle():
         for h in range(H5):
             want = oracle.attention_rows(x5["Q"][h], x5["K"][h], x5["Vt"][h], N5, D5, rows, scale5)
             assert np.all(np.abs(o[h] - want) <= tol(want, x5["Vt"][h])), h
+        exact(c6.cpu().numpy().view(np.uint16),
+              oracle.gemm_tn(x6["A"], x6["B"], oracle.FMT_F16, M6, N6, K6), oracle.FMT_F16)
 
     # Eager run first (also settles the library's one-time device queries).
     xs = load(100)
