@@ -48,6 +48,11 @@
 // gemm_tn_mid_kernel: 128 x 128 tiles, two blocks per CU, for grids the
 //   256-wide tiles cannot fill.
 //
+// Split-K (gemm_f16_tn_splitk, gemm_f8_tn_splitk): for few output tiles and a
+//   long K, the 128 x 128 kernel with SPLIT multiplies one K range per block
+//   into an fp32 partial in the caller's workspace, and
+//   gemm_splitk_reduce_kernel sums the partials in range order and converts.
+//
 // gemm_tn_pp_kernel: the 256 x 256 tile computed by 8 waves in two groups that
 //   alternate between fragment reads and products (the "ping-pong" design the
 //   MI355X FP8 GEMM page weighs against its 4-wave one); measured slower here,
