@@ -62,11 +62,14 @@ def fmt_in(kind):
 
 
 # (M, N, K, splits): even and uneven ranges, K tails, the 64-split maximum,
-# more splits than 16-step ranges allow, tiny M / N.
+# more splits than 16-step ranges allow, tiny M / N, M not a multiple of 4
+# (partial rows stored one by one, padded workspace columns).
 CASES = {
     "f16": [(256, 256, 8192, 8), (200, 136, 4000, 7), (128, 128, 64 * 33, 4), (1, 8, 2048, 16),
-            (512, 384, 16384, 64), (300, 260, 1024, 64), (136, 72, 65536, 32)],
-    "f8": [(256, 256, 16384, 8), (208, 144, 8000, 7), (16, 32, 4096, 16), (272, 160, 2048, 64)],
+            (512, 384, 16384, 64), (300, 260, 1024, 64), (136, 72, 65536, 32),
+            (133, 45, 3000, 6)],
+    "f8": [(256, 256, 16384, 8), (208, 144, 8000, 7), (16, 32, 4096, 16), (272, 160, 2048, 64),
+           (131, 77, 4096, 8)],
 }
 
 
