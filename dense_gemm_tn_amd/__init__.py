@@ -234,8 +234,11 @@ def f8_config(transa: str, transb: str, M: int, N: int, K: int) -> int:
 
 # ----------------------------------------------------------- tensor helpers
 
-def matmul_tn_f16(a, b, out=None, stream=None):
-    """a: [M, K] fp16 (row-major A), b: [N, K] fp16 (column-major B) -> C as [N, M] fp16."""
+def matmul_tn_f16(a, b, out=None, stream=None, splits=1):
+    """a: [M, K] fp16 (row-major A), b: [N, K] fp16 (column-major B) -> C as [N, M] fp16.
+
+    splits > 1, or "auto" (the library's suggestion), runs the split-K call with
+    a workspace allocated here on the launch stream."""
     import torch
 
     M, K = a.shape
@@ -244,7 +247,21 @@ def matmul_tn_f16(a, b, out=None, stream=None):
         raise ValueError("matmul_tn_f16 expects fp16 [M, K] and [N, K]")
     if out is None:
         out = torch.empty((N, M), dtype=torch.float16, device=a.device)
-    gemm_f16_tn(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), stream)
+    if splits == "auto":
+        splits = splitk_choose(M, N, K)
+    if splits == 1:
+        gemm_f16_tn(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), stream)
+        return out
+    if stream is not None and not isinstance(stream, torch.cuda.Stream):
+        raise ValueError("split-K through this helper needs a torch.cuda.Stream (or None)")
+    nbytes = splitk_workspace_bytes(M, N, int(splits))
+    if nbytes < 0:
+        raise ValueError("splits must be 1 .. 64 or 'auto'")
+    ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=a.device)
+    gemm_f16_tn_splitk(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), int(splits),
+                       ws, nbytes, stream)
+    if stream is not None:
+        ws.record_stream(stream)   # freed only after the launch stream has used it
     return out
 
 

@@ -135,3 +135,19 @@ def test_choose_gives_every_cu_a_block():
     assert 1 < s <= 64 and 16 * s >= cus
     assert dg.splitk_choose(4096, 4096, 4096) == 1
     assert dg.splitk_choose(512, 512, 1024) == 1
+
+
+@pytest.mark.parametrize("splits", ["auto", 5])
+def test_matmul_helper_splitk(splits):
+    """The tensor helper allocates the workspace itself (auto: the chooser's count)."""
+    M, N, K = 256, 192, 16384
+    x = inputs.make_shape("f16", M, N, K, dist="pm1", seed=17)
+    a = torch.from_numpy(x["A"]).to(DEV)
+    b = torch.from_numpy(x["B"]).to(DEV)
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    c = dg.matmul_tn_f16(a, b, stream=side, splits=splits)
+    side.synchronize()
+    ref = oracle.gemm_tn(x["A"], x["B"], oracle.FMT_F16, M, N, K)
+    want = oracle.decode(oracle.encode(ref, oracle.FMT_F16), oracle.FMT_F16)
+    assert np.array_equal(oracle.decode(c.cpu().numpy(), oracle.FMT_F16), want)
