@@ -1935,10 +1935,12 @@ static int launch_splitk(const Problem &pr, int64_t splits, void *ws, int64_t ws
 }
 
 // Suggested split count: as many splits of the 128 x 128 tiles as fit one
-// block per CU (never a second round), each split keeping at least
-// kSplitMinSteps K-steps; 1 when the tiles alone fill half the CUs or K is
-// short.  (Measured on 512^2 x 32768, 256^2 x 65536, 1024 x 512 x 16384 and
-// 768^2 x 8192: within 3 % of the best count, 1024^2 x 16384 within 12 %.)
+// block per CU (never a second round), doubled to two blocks per CU when each
+// range would still be 4 * kSplitMinSteps K-steps or longer (the second block
+// hides the first one's waits), each split keeping at least kSplitMinSteps
+// K-steps; 1 when the tiles alone fill half the CUs or K is short.  (Measured
+// on 512^2 x 32768, 256^2 x 65536, 1024^2 x 16384, 1024 x 512 x 16384 and
+// 768^2 x 8192: within 3 % of the best count of a sweep.)
 constexpr int64_t kSplitMinSteps = 16;
 static int64_t choose_splits(int es, int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 1;
@@ -1948,6 +1950,7 @@ static int64_t choose_splits(int es, int64_t M, int64_t N, int64_t K) {
   const int64_t cus = cu_count();
   if (2 * tiles >= cus) return 1;
   int64_t s = cus / tiles;
+  if (s >= 1 && nk / s >= 4 * kSplitMinSteps) s *= 2;
   const int64_t by_k = nk / kSplitMinSteps;
   if (s > by_k) s = by_k;
   if (s > kSplitMax) s = kSplitMax;

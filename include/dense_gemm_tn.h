@@ -285,9 +285,10 @@ int gemm_f8_tn_splitk(const void *A, const void *B, void *C,
 int64_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
 
 /* Suggested split count for an M x N x K TN product (fp8 != 0: FP8): as many
- * splits of the 128 x 128 tiles as fit one block per compute unit, each
- * keeping at least 16 K-steps; 1 when the tiles alone fill half the compute
- * units.  -1 for negative sizes. */
+ * splits of the 128 x 128 tiles as fit one block per compute unit (two per
+ * compute unit when each range would still be 64 K-steps or longer), each
+ * keeping at least 16 K-steps and at most 64 splits; 1 when the tiles alone
+ * fill half the compute units.  -1 for negative sizes. */
 int64_t gemm_splitk_choose(int fp8, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus
