@@ -7,24 +7,39 @@ A step is one launch of the GEMM over one set of inputs (A, B -> C).  Inputs
 are generated on the host with fixed seeds, copied to HBM before timing, and
 rotated over R buffer sets so the working set exceeds the 256 MB last-level
 cache (the method of the MI355X FP8 GEMM page: warm-up runs, timed runs,
-normally distributed data, rotating buffers).  W untimed steps, then exactly K
-timed steps bracketed by torch.cuda.synchronize(); HIP events recorded on the
-launch stream give the average kernel duration.  Throughput = 2*M*N*K per
-step / time (section 11.1 of the hello-gpu chapter counts a multiply-add as
-two flops).
+normally distributed data, rotating buffers).  Per workload:
+  1. every set is launched once and set 0's output is checked against the CPU
+     oracle on sampled entries (parity before timing; exact on +-1 data);
+  2. W untimed steps, then exactly K timed steps bracketed by
+     torch.cuda.synchronize(); HIP events recorded on the launch stream give
+     the average kernel duration (`ms_per_step`), from which
+     throughput = 2*M*N*K per step / time (section 11.1 of the hello-gpu
+     chapter counts a multiply-add as two flops);
+  3. a second pass of K launches with an event pair around each gives the
+     per-launch median / min / max (the hello-gpu chapter, section 11.5, reports
+     medians with their range);
+  4. set 0 is launched again and its output must equal, bit for bit, the one
+     checked in step 1 (parity after timing);
+  5. the launches of step 3 also write per-block clock records (the kernels'
+     shader-clock and 100 MHz counters at each block's start and end, and the
+     XCD it ran on): the clock the kernel actually ran at, overall and per
+     XCD, which explains run-to-run and box-to-box spread of a power-limited
+     part.
+Before the warm-up steps, each workload runs back to back for --settle-ms
+(0.25 s) so timing starts at the clock the load sustains rather than on the
+ramp up from idle.
 
-Prints ONE JSON line.  The headline `value` is the FP16 TN 4096^3 workload; the
-FP8 8192^3 workload, the fused attention forward over 64 heads x 4096 queries x
-4096 keys x head dim 128 (4*M*N*D flops per head: two products), FP16 2048^3
-(a grid the 256-wide tiles cannot fill, served by the 128 x 128 kernel), FP16
-4096^3 and FP8 8192^3 in the NN, TT and NT op codes (operands read as they lie,
-no transpose pass), FP16 512 x 512 x 32768 (16 output tiles, long K) without and
-with split-K, the 8-wave ping-pong kernel forced on the FP16 4096^3 and FP8 8192^3
-problems (a measured counter-design), and any other requested workload are
-reported under "workloads" in the same line.  `roofline` is for the FP16 kernel; `traffic`
-comes from a stored rocprofv3 counter summary and is null when the kernel
-source changed after the counters were taken.  `cpu_baseline` times the CPU
-oracle on a bounded column sample of the same workload.
+Prints ONE JSON line.  The headline `value` is the FP16 TN 4096^3 workload;
+every other workload of the default list (the five configurations of the
+hot path -- FP16 256^3 +-1, FP16 4096^3, FP16 1920 x 13900 x 4096, FP8 8192^3,
+batched QK^T 64 x 4096 x 4096 x 128 -- then the fused attention forward, FP16
+2048^3 on the 128 x 128 kernel, the NN/TT/NT op codes, 512 x 512 x 32768
+without and with split-K, and the 8-wave ping-pong kernel) is reported under
+"workloads".  `roofline` is for the FP16 kernel (the QK^T workload carries an
+HBM roofline of its own); `traffic` comes from a stored rocprofv3 counter
+summary and is null when the kernel source changed after the counters were
+taken.  `cpu_baseline` times the CPU oracle on a bounded column sample of the
+headline workload.
 """
 from __future__ import annotations
 
@@ -69,6 +84,16 @@ def kernel_name(w):
             3: "gemm_tn_skinny_kernel<%d>" % kind,
             4: "gemm_tn_pp_kernel<%d>" % kind}[cfg]
 
+
+# The five configurations of the hot path first (the headline FP16 4096^3, FP8
+# 8192^3, FP16 256^3 +-1, the wide ragged FP16 shape, batched QK^T), then the
+# adjacent parts.
+DEFAULT_WORKLOADS = (
+    "f16_4096", "f8_8192", "f16_256_pm1", "f16_1920x13900x4096", "qkt_64x4096x4096x128",
+    "attn_64x4096x4096x128", "f16_2048",
+    "f16_nn_4096", "f16_tt_4096", "f16_nt_4096", "f8_nn_8192", "f8_tt_8192", "f8_nt_8192",
+    "f16_512x512x32768", "f16_512x512x32768_splitk", "f16_4096_pingpong", "f8_8192_pingpong",
+)
 
 CSRC = os.path.join(ROOT, "dense_gemm_tn_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
@@ -174,10 +199,131 @@ def make_launcher(w, dev):
     return x, sets, launch, R
 
 
-def time_workload(w, steps, warmup, dev):
+CLOCK_WORDS = 10   # uint64 words per block record (see gemm_clock_record)
+
+
+def clock_summary(rec) -> dict | None:
+    """Per-block clock records (see gemm_clock_record: shader-clock ticks and
+    100 MHz real-time ticks at the block's start, K-loop start, K-loop end and
+    end, and its XCD) -> the clock the blocks ran at: time-weighted MHz overall
+    and per XCD, the median and range of per-block MHz, the median block
+    duration and, for kernels with a pipelined K loop, the median prologue,
+    loop and epilogue durations (microseconds) and the loop's own clock."""
+    import numpy as np
+
+    rec = np.asarray(rec, dtype=np.uint64).reshape(-1, CLOCK_WORDS)
+    t = (rec[:, 6] - rec[:, 0]).astype(np.float64)
+    r = (rec[:, 7] - rec[:, 1]).astype(np.float64)
+    ok = (rec[:, 6] > rec[:, 0]) & (rec[:, 7] > rec[:, 1]) & (rec[:, 0] > 0)
+    if not ok.any():
+        return None
+    rec, t, r = rec[ok], t[ok], r[ok]
+    xcd = rec[:, 8].astype(np.int64)
+    mhz = t / r * 100.0                       # real-time counter: 100 MHz
+    per_xcd = {int(x): float(t[xcd == x].sum() / r[xcd == x].sum() * 100.0)
+               for x in np.unique(xcd)}
+    out = {
+        "blocks": int(ok.sum()),
+        "sclk_mhz": float(t.sum() / r.sum() * 100.0),
+        "sclk_mhz_block_median": float(np.median(mhz)),
+        "sclk_mhz_block_min": float(mhz.min()),
+        "sclk_mhz_block_max": float(mhz.max()),
+        "sclk_mhz_per_xcd": per_xcd,
+        "block_us_median": float(np.median(r) / 100.0),
+    }
+    looped = (rec[:, 2] >= rec[:, 0]) & (rec[:, 4] >= rec[:, 2]) & (rec[:, 6] >= rec[:, 4]) & \
+        (rec[:, 3] > 0) & (rec[:, 5] > 0)
+    if looped.all():
+        rr = rec[:, 1::2].astype(np.float64)       # real-time ticks at the four points
+        tt = rec[:, 0::2][:, :4].astype(np.float64)
+        out["prologue_us_median"] = float(np.median(rr[:, 1] - rr[:, 0]) / 100.0)
+        out["loop_us_median"] = float(np.median(rr[:, 2] - rr[:, 1]) / 100.0)
+        out["epilogue_us_median"] = float(np.median(rr[:, 3] - rr[:, 2]) / 100.0)
+        out["loop_sclk_mhz"] = float((tt[:, 2] - tt[:, 1]).sum() / (rr[:, 2] - rr[:, 1]).sum()
+                                     * 100.0)
+    return out
+
+
+def sample_check(w, x, out):
+    """The GPU output of set 0 against the oracle on sampled entries: corners,
+    tile edges and seeded random entries (attention: sampled query rows of the
+    first and last head).  Returns {"entries", "max_rel_err" or "inexact",
+    "ok"} -- +-1 data must be exact, other data within the output format's bar
+    relative to the largest sampled reference value."""
+    import numpy as np
     import torch
 
+    import oracle
+
+    rng = np.random.default_rng(7)
+    if w.kind == "attn":
+        D, scale = w.K, 1.0 / w.K ** 0.5
+        worst, n = 0.0, 0
+        for h in sorted({0, w.batch - 1}):
+            rows = np.unique(np.concatenate([[0, w.M - 1], rng.integers(0, w.M, 6)]))
+            ref = oracle.attention_rows(x["Q"][h], x["K"][h], x["Vt"][h], w.N, D, rows, scale)
+            got = out[h][torch.from_numpy(rows).to(out.device)].float().cpu().numpy()
+            bound = 1e-3 * np.abs(x["Vt"][h].astype(np.float64)).max() + 2e-3 * np.abs(ref) + 1e-5
+            worst = max(worst, float(np.max(np.abs(got - ref) / bound)))
+            n += ref.size
+        return {"entries": n, "max_err_over_bound": worst, "ok": worst <= 1.0}
+    edges_m = sorted({0, 1, 15, 16, 127, 128, 255, 256, w.M // 2, w.M - 1} & set(range(w.M)))
+    edges_n = sorted({0, 1, 15, 16, 127, 128, 255, 256, w.N // 2, w.N - 1} & set(range(w.N)))
+    ms = np.array([m for m in edges_m for _ in edges_n] + list(rng.integers(0, w.M, 256)))
+    ns = np.array([n for _ in edges_m for n in edges_n] + list(rng.integers(0, w.N, 256)))
+    if w.kind == "qkt":
+        pairs = [(x["Q"][h], x["K"][h], out[h]) for h in sorted({0, w.batch - 1})]
+        fmt_in, fmt_out, scale = oracle.FMT_F16, oracle.FMT_F16, 1.0
+    else:
+        pairs = [(x["A"], x["B"], out)]
+        fmt_in = oracle.FMT_E4M3FN if w.kind == "f8" else oracle.FMT_F16
+        fmt_out = oracle.FMT_BF16 if w.kind == "f8" else oracle.FMT_F16
+        scale = float(x["scale_a"]) * float(x["scale_b"]) if w.kind == "f8" else 1.0
+    err, top, inexact, n = 0.0, 0.0, 0, 0
+    idx_n = torch.from_numpy(ns).to(out.device)
+    idx_m = torch.from_numpy(ms).to(out.device)
+    for A, B, c in pairs:
+        ref = oracle.gemm_tn_entries(A, B, fmt_in, w.K, ms, ns, scale=scale)
+        codes = c.view(torch.int16)[idx_n, idx_m].cpu().numpy().view(np.uint16)
+        got = oracle.decode(codes, fmt_out)
+        err = max(err, float(np.max(np.abs(got - ref))))
+        top = max(top, float(np.max(np.abs(ref))))
+        want = oracle.decode(oracle.encode(ref, fmt_out), fmt_out)
+        inexact += int(np.sum(got != want))
+        n += ref.size
+    if w.dist == "pm1":
+        return {"entries": n, "inexact": inexact, "ok": inexact == 0}
+    rel = err / top if top > 0 else err
+    bar = 1e-2 if w.kind == "f8" else 4e-3
+    return {"entries": n, "max_rel_err": rel, "ok": rel <= bar}
+
+
+def time_workload(w, steps, warmup, dev, check=True, settle_s=0.25):
+    import statistics as st
+
+    import torch
+
+    import dense_gemm_tn_amd as dg
+
     x, sets, launch, R = make_launcher(w, dev)
+    # Parity before timing: every set is launched once (its buffers are then
+    # in use before the timed region), set 0's output is checked and kept.
+    for i in range(R):
+        launch(i)
+    torch.cuda.synchronize()
+    out0 = sets[0][-1]
+    before = sample_check(w, x, out0) if check else None
+    ref_bits = out0.clone()
+    # Settle: back-to-back launches for a fixed time before the warm-up steps,
+    # so the timed steps start at the clock the load sustains, not on the ramp
+    # up from idle (the MI355X FP8 GEMM page warms up with 1000 launches).
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle < settle_s:
+        for _ in range(4):
+            launch(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
@@ -190,17 +336,50 @@ def time_workload(w, steps, warmup, dev):
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # Second pass: an event pair around every launch, and the per-block clock
+    # records of these launches (one launch first, to learn its block count).
+    probe = torch.zeros(CLOCK_WORDS, dtype=torch.int64, device=dev)
+    dg.clock_record(probe, 1)
+    launch(0)
+    torch.cuda.synchronize()
+    blocks = dg.clock_records_used()
+    n_rec = min(steps, max(1, (256 << 20) // (8 * CLOCK_WORDS * blocks)))
+    recs = torch.zeros((n_rec * blocks, CLOCK_WORDS), dtype=torch.int64, device=dev)
+    dg.clock_record(recs, n_rec * blocks)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        launch(i)
+        e1.record()
+    torch.cuda.synchronize()
+    dg.clock_record(None, 0)
+    clock = clock_summary(recs.cpu().numpy().view("uint64"))
+    if clock is not None:
+        clock["launches_recorded"] = n_rec
+    del recs, probe
+    per = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)   # microseconds
+    # Parity after timing: set 0 again, bit for bit the output checked before.
+    launch(0)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(out0, ref_bits))
+    del ref_bits
     ev_ms = start.elapsed_time(stop)
     kernel_s = ev_ms / 1e3 / steps
     tflops = w.flops / kernel_s / 1e12
     res = {
         "M": w.M, "N": w.N, "K": w.K, "batch": w.batch, "kind": w.kind, "seed": w.seed,
         "dist": w.dist, "rotating_sets": R,
+        "settle_launches": n_settle,
         "ms_per_step": ev_ms / steps,
         "wall_ms_per_step": wall * 1e3 / steps,
+        "per_launch_us": {"median": st.median(per), "min": per[0], "max": per[-1],
+                          "launches": len(per)},
         "tflops": tflops,
         "frac_of_peak": tflops / PEAK_TFLOPS[w.kind],
         "hbm_gbs_algorithmic": algorithmic_bytes(w) / kernel_s / 1e9,
+        "clock": clock,
+        "parity": {"before": before, "after_bitwise_equal": same},
     }
     return res, x, sets
 
@@ -275,11 +454,16 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", action="append", default=None,
-                    help="workload names (default: f16_4096, f8_8192, "
-                         "attn_64x4096x4096x128, f16_2048, the NN/TT/NT layouts of f16_4096 "
-                         "and f8_8192, 512 x 512 x 32768 without and with split-K, and the "
-                         "ping-pong kernel on f16_4096 and f8_8192)")
+                    help="workload names (default: DEFAULT_WORKLOADS: the five configurations "
+                         "f16_4096, f8_8192, f16_256_pm1, f16_1920x13900x4096, "
+                         "qkt_64x4096x4096x128, then attn_64x4096x4096x128, f16_2048, the "
+                         "NN/TT/NT layouts of f16_4096 and f8_8192, 512 x 512 x 32768 without "
+                         "and with split-K, and the ping-pong kernel on f16_4096 and f8_8192)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-check", action="store_true",
+                    help="skip the sampled oracle checks before timing (profiling runs)")
+    ap.add_argument("--settle-ms", type=float, default=250.0,
+                    help="back-to-back launches for this long before the warm-up steps")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (a known-size kernel for "
                          "scaling HBM byte counters), then exit")
@@ -307,11 +491,7 @@ def main():
     from dense_gemm_tn_amd import inputs
 
     dev = torch.device("cuda:0")
-    names = args.workload or ["f16_4096", "f8_8192", "attn_64x4096x4096x128", "f16_2048",
-                              "f16_nn_4096", "f16_tt_4096", "f16_nt_4096",
-                              "f8_nn_8192", "f8_tt_8192", "f8_nt_8192",
-                              "f16_512x512x32768", "f16_512x512x32768_splitk",
-                              "f16_4096_pingpong", "f8_8192_pingpong"]
+    names = args.workload or list(DEFAULT_WORKLOADS)
     head = "f16_4096" if "f16_4096" in names else names[0]
     results = {}
     keep = {}
@@ -324,13 +504,17 @@ def main():
             os.environ["DG_GEMM_TILE"] = w.extra["tile"]
         elif saved is not None:
             os.environ["DG_GEMM_TILE"] = saved
-        res, x, sets = time_workload(w, args.steps, args.warmup, dev)
+        print("bench: %s" % name, file=sys.stderr, flush=True)
+        res, x, sets = time_workload(w, args.steps, args.warmup, dev, check=not args.no_check,
+                                     settle_s=args.settle_ms / 1e3)
         kname = kernel_name(w)
         os.environ.pop("DG_GEMM_TILE", None)
         if saved is not None:
             os.environ["DG_GEMM_TILE"] = saved
         kernel_s = res["ms_per_step"] / 1e3
         tb = traffic_for(name, w, kernel_s)
+        if w.kind == "qkt":
+            res["hbm_frac_of_peak"] = res["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
         res["roofline"] = {
             "bound": "hbm" if w.kind == "qkt" else "mfma",
             "achieved": res["hbm_gbs_algorithmic"] if w.kind == "qkt" else res["tflops"],
@@ -373,6 +557,9 @@ def main():
         "roofline": {k: hr["roofline"][k] for k in
                      ("bound", "achieved", "peak", "unit", "frac", "traffic")},
         "cpu_baseline": cpu,
+        "clock": hr.get("clock"),
+        "parity_ok": all((r["parity"]["before"] or {}).get("ok", True)
+                         and r["parity"]["after_bitwise_equal"] for r in results.values()),
         "workloads": results,
         "kernel_source_sha256_16": {k: source_hash(k) for k in ("f16", "attn")},
     }

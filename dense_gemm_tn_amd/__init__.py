@@ -40,6 +40,8 @@ EXPORTS = (
     "gemm_f8_tn_splitk",
     "gemm_splitk_workspace_bytes",
     "gemm_splitk_choose",
+    "gemm_clock_record",
+    "gemm_clock_records_used",
 )
 
 _lib = None
@@ -82,6 +84,10 @@ def lib() -> ctypes.CDLL:
         L.gemm_splitk_workspace_bytes.restype = i64
         L.gemm_splitk_choose.argtypes = [ctypes.c_int, i64, i64, i64]
         L.gemm_splitk_choose.restype = i64
+        L.gemm_clock_record.argtypes = [vp, i64]
+        L.gemm_clock_record.restype = ctypes.c_int
+        L.gemm_clock_records_used.argtypes = []
+        L.gemm_clock_records_used.restype = i64
         for f in (L.gemm_f16_tn, L.gemm_f16, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
                   L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config, L.gemm_f16_config,
                   L.gemm_f8, L.gemm_f8_config, L.gemm_f16_tn_splitk, L.gemm_f8_tn_splitk):
@@ -151,6 +157,19 @@ def gemm_f8_tn(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
     """C = bf16(fp32(scale_a*scale_b) * A x B) with E4M3FN A, B and fp32 accumulation."""
     _check("gemm_f8_tn", lib().gemm_f8_tn(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
                                           float(scale_a), float(scale_b), _stream(stream)))
+
+
+CLOCK_RECORD_WORDS = 10  # uint64 words per block record (see gemm_clock_record)
+
+
+def clock_record(buf, records: int) -> None:
+    """Start per-block clock records into a device buffer of `records` records
+    (a 64-bit tensor of 10 * records elements); clock_record(None, 0) stops."""
+    _check("gemm_clock_record", lib().gemm_clock_record(_ptr(buf), records))
+
+
+def clock_records_used() -> int:
+    return int(lib().gemm_clock_records_used())
 
 
 def splitk_workspace_bytes(M: int, N: int, splits: int) -> int:
@@ -233,35 +252,87 @@ def f8_config(transa: str, transb: str, M: int, N: int, K: int) -> int:
 
 
 # ----------------------------------------------------------- tensor helpers
+#
+# The helpers check what the C ABI cannot see from raw pointers -- that every
+# tensor lives on one GPU, that rows are contiguous, and that a caller's `out`
+# has the shape, dtype and strides the product writes -- and raise ValueError
+# before any launch.
+
+def _check_tensors(fn: str, *ts) -> None:
+    """Every tensor is a CUDA (HIP) tensor on one device with a contiguous last dimension."""
+    for t in ts:
+        if t.dim() == 0 or t.stride(-1) != 1:
+            raise ValueError("%s: the last dimension must be contiguous" % fn)
+    dev = None
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("%s: tensors must be on a GPU (got %s)" % (fn, t.device))
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s: tensors on different devices (%s, %s)" % (fn, dev, t.device))
+
+
+def _check_out(fn: str, out, shape, dtypes) -> None:
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError("%s: out must have shape %s, got %s" % (fn, tuple(shape),
+                                                                 tuple(out.shape)))
+    if out.dtype not in dtypes:
+        raise ValueError("%s: out dtype %s is not one of %s" % (fn, out.dtype, dtypes))
+    if out.stride(-1) != 1:
+        raise ValueError("%s: out's last dimension must be contiguous" % fn)
+    for d in range(out.dim() - 1):
+        if out.stride(d) < out.shape[d + 1] * out.stride(d + 1) and out.shape[d] > 1:
+            raise ValueError("%s: out's rows overlap (stride %d)" % (fn, out.stride(d)))
+
+
+def _empty_on(stream, shape, dtype, device):
+    """A new tensor allocated on `stream` (or the current stream): the caching
+    allocator then orders its reuse after the work queued on that stream."""
+    import torch
+
+    if stream is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(shape, dtype=dtype, device=device)
+
 
 def matmul_tn_f16(a, b, out=None, stream=None, splits=1):
     """a: [M, K] fp16 (row-major A), b: [N, K] fp16 (column-major B) -> C as [N, M] fp16.
 
     splits > 1, or "auto" (the library's suggestion), runs the split-K call with
-    a workspace allocated here on the launch stream."""
+    a workspace allocated on the launch stream (so the caching allocator hands
+    it out only after earlier work on that stream).  A new `out` is allocated
+    on the launch stream too; a caller's `out` must be [N, M] fp16 with
+    contiguous rows."""
     import torch
 
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("matmul_tn_f16 expects 2-D tensors")
     M, K = a.shape
     N, Kb = b.shape
     if K != Kb or a.dtype != torch.float16 or b.dtype != torch.float16:
         raise ValueError("matmul_tn_f16 expects fp16 [M, K] and [N, K]")
+    if out is not None:
+        _check_out("matmul_tn_f16", out, (N, M), (torch.float16,))
+    _check_tensors("matmul_tn_f16", a, b, *(() if out is None else (out,)))
+    if stream is not None and not isinstance(stream, torch.cuda.Stream):
+        if splits != 1 or out is None:
+            raise ValueError("matmul_tn_f16: pass a torch.cuda.Stream (or None) when the "
+                             "helper allocates")
     if out is None:
-        out = torch.empty((N, M), dtype=torch.float16, device=a.device)
+        out = _empty_on(stream, (N, M), torch.float16, a.device)
     if splits == "auto":
         splits = splitk_choose(M, N, K)
     if splits == 1:
         gemm_f16_tn(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), stream)
         return out
-    if stream is not None and not isinstance(stream, torch.cuda.Stream):
-        raise ValueError("split-K through this helper needs a torch.cuda.Stream (or None)")
     nbytes = splitk_workspace_bytes(M, N, int(splits))
     if nbytes < 0:
         raise ValueError("splits must be 1 .. 64 or 'auto'")
-    ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=a.device)
+    ws = _empty_on(stream, (max(nbytes, 16) // 4,), torch.float32, a.device)
     gemm_f16_tn_splitk(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), int(splits),
                        ws, nbytes, stream)
-    if stream is not None:
-        ws.record_stream(stream)   # freed only after the launch stream has used it
     return out
 
 
@@ -273,12 +344,18 @@ def matmul_f16(a, b, transa: str = "T", transb: str = "N", out=None, stream=None
 
     if a.dtype != torch.float16 or b.dtype != torch.float16 or a.dim() != 2 or b.dim() != 2:
         raise ValueError("matmul_f16 expects 2-D fp16 tensors")
+    if transa not in ("T", "t", "N", "n") or transb not in ("T", "t", "N", "n"):
+        raise ValueError("op codes are 'T' or 'N'")
     M, K = a.shape if transa in "Tt" else a.shape[::-1]
     N, Kb = b.shape if transb in "Nn" else b.shape[::-1]
-    if K != Kb or a.stride(1) != 1 or b.stride(1) != 1:
-        raise ValueError("matmul_f16: K differs or a last dimension is strided")
+    if K != Kb:
+        raise ValueError("matmul_f16: K differs")
+    if out is not None:
+        _check_out("matmul_f16", out, (N, M), (torch.float16,))
+    _check_tensors("matmul_f16", a, b, *(() if out is None else (out,)))
     if out is None:
-        out = torch.empty((N, M), dtype=torch.float16, device=a.device)
+        out = _empty_on(stream if isinstance(stream, torch.cuda.Stream) else None, (N, M),
+                        torch.float16, a.device)
     gemm_f16(transa, transb, a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), stream)
     return out
 
@@ -287,12 +364,18 @@ def matmul_tn_f8(a, b, scale_a: float, scale_b: float, out=None, stream=None):
     """a: [M, K] uint8 E4M3FN codes, b: [N, K] codes -> C as [N, M] bf16."""
     import torch
 
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("matmul_tn_f8 expects 2-D tensors")
     M, K = a.shape
     N, Kb = b.shape
     if K != Kb or a.element_size() != 1 or b.element_size() != 1:
         raise ValueError("matmul_tn_f8 expects 1-byte [M, K] and [N, K]")
+    if out is not None:
+        _check_out("matmul_tn_f8", out, (N, M), (torch.bfloat16,))
+    _check_tensors("matmul_tn_f8", a, b, *(() if out is None else (out,)))
     if out is None:
-        out = torch.empty((N, M), dtype=torch.bfloat16, device=a.device)
+        out = _empty_on(stream if isinstance(stream, torch.cuda.Stream) else None, (N, M),
+                        torch.bfloat16, a.device)
     gemm_f8_tn(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), scale_a, scale_b,
                stream)
     return out
@@ -302,12 +385,18 @@ def qkt(q, k, out=None, stream=None):
     """q: [H, M, D], k: [H, N, D] fp16 -> S as [H, N, M] fp16 (S_h column-major)."""
     import torch
 
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("qkt expects [H, M, D] and [H, N, D]")
     H, M, D = q.shape
     Hk, N, Dk = k.shape
-    if H != Hk or D != Dk:
-        raise ValueError("qkt expects [H, M, D] and [H, N, D]")
+    if H != Hk or D != Dk or q.dtype != torch.float16 or k.dtype != torch.float16:
+        raise ValueError("qkt expects fp16 [H, M, D] and [H, N, D]")
+    if out is not None:
+        _check_out("qkt", out, (H, N, M), (torch.float16,))
+    _check_tensors("qkt", q, k, *(() if out is None else (out,)))
     if out is None:
-        out = torch.empty((H, N, M), dtype=torch.float16, device=q.device)
+        out = _empty_on(stream if isinstance(stream, torch.cuda.Stream) else None, (H, N, M),
+                        torch.float16, q.device)
     gemm_batched_qkt(q, k, out, H, M, N, D, q.stride(1), k.stride(1), out.stride(1),
                      q.stride(0), k.stride(0), out.stride(0), stream)
     return out
@@ -324,15 +413,21 @@ def attention(q, k, vt, scale: float | None = None, out=None, stream=None):
 
     import torch
 
+    if q.dim() != 3 or k.dim() != 3 or vt.dim() != 3:
+        raise ValueError("attention expects [H, M, D], [H, N, D] and [H, D, N]")
     H, M, D = q.shape
     Hk, N, Dk = k.shape
     Hv, Dv, Nv = vt.shape
     if (H, D) != (Hk, Dk) or (H, D, N) != (Hv, Dv, Nv):
         raise ValueError("attention expects [H, M, D], [H, N, D] and [H, D, N]")
-    if any(t.dtype != torch.float16 or t.stride(2) != 1 for t in (q, k, vt)):
-        raise ValueError("attention expects fp16 tensors with a contiguous last dimension")
+    if any(t.dtype != torch.float16 for t in (q, k, vt)):
+        raise ValueError("attention expects fp16 tensors")
+    if out is not None:
+        _check_out("attention", out, (H, M, D), (torch.float16,))
+    _check_tensors("attention", q, k, vt, *(() if out is None else (out,)))
     if out is None:
-        out = torch.empty((H, M, D), dtype=torch.float16, device=q.device)
+        out = _empty_on(stream if isinstance(stream, torch.cuda.Stream) else None, (H, M, D),
+                        torch.float16, q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     attention_fwd_f16(q, k, vt, out, H, M, N, D, q.stride(1), k.stride(1), vt.stride(1),

@@ -11,13 +11,17 @@
 // along the dimension its product sums over.
 //
 // Kernel design (head dim 128, fp16 in, fp32 accumulate, fp16 out):
-//   * One workgroup = 4 waves = 128 queries of one head; wave w owns 32 queries
-//     (two 16-query MFMA column tiles).  Two workgroups per CU.
-//   * The wave's Q rows live in registers for the whole kernel as B operands of
-//     v_mfma_f32_16x16x32_f16 (the 16x16 shapes of the MI355X FP8 GEMM page).
+//   * One workgroup = 4 waves = 256 queries of one head; wave w owns 64
+//     queries as two halves of 32 (each two 16-query MFMA column tiles), whose
+//     schedules run half a key block apart so one half's softmax arithmetic
+//     issues beside the other half's products.  One workgroup per CU.
+//   * The wave's Q rows live in AGPRs for the whole kernel as B operands of
+//     v_mfma_f32_16x16x32_f16 (the 16x16 shapes of the MI355X FP8 GEMM page),
+//     and so do the output accumulators O^T.
 //   * Keys are processed 64 at a time.  A key block of K (64 x 256 B) and of Vt
 //     (128 x 128 B) is copied global -> LDS by buffer loads that write LDS
-//     directly, double-buffered (2 x 32 KiB), one barrier per key block.
+//     directly into three K slots and two Vt slots (80 KiB), one barrier per
+//     key block.
 //   * S^T = K Q^T is computed tile by tile, so each accumulator lane holds one
 //     query (column) and four keys.  The K rows given to MFMA tile t are chosen
 //     so that the keys a lane ends up holding from tiles 2j and 2j+1 are eight
@@ -85,7 +89,30 @@ struct AttnParams {
   int32_t blocks;                // grid size
   int32_t n_blocks;              // key blocks: ceil(N / 64)
   float c;                       // scale * log2(e)
+  uint64_t *clk;                 // per-block clock records, or null (see clock_mark)
 };
+
+// Per-block clock record (measurement only; the layout of the GEMM kernels'
+// records in gemm_tn.hip): s_memtime and s_memrealtime at the block's start
+// (words 0-1) and after its first wave's last stores have completed (words
+// 6-7), the XCD (word 8) and the block index (word 9); words 2-5 stay zero.
+enum { kClockStart = 0, kClockEnd = 3, kClockWords = 10 };
+__device__ __forceinline__ void clock_mark(uint64_t *clk, int point) {
+  if (clk == nullptr) return;
+  if (point == kClockEnd) __builtin_amdgcn_s_waitcnt(0);
+  const uint64_t t = __builtin_amdgcn_s_memtime();
+  const uint64_t r = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x != 0) return;
+  uint64_t *rec = clk + kClockWords * (uint64_t)blockIdx.x;
+  rec[2 * point] = t;
+  rec[2 * point + 1] = r;
+  if (point == kClockStart) {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    rec[8] = xcc & 15u;
+    rec[9] = blockIdx.x;
+  }
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
@@ -229,6 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
   const int logical = x * q8 + (x < r8 ? x : r8) + b / kXcds;
   const int head = logical / p.tiles_m;
   const int64_t q0 = (int64_t)(logical - head * p.tiles_m) * kBM + kWaveQ * w;
+  clock_mark(p.clk, kClockStart);
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + head * p.sq_b, p.q_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.K + head * p.sk_b, p.k_bytes);
@@ -625,11 +653,16 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
       }
     }
   }
+  clock_mark(p.clk, kClockEnd);
 }
 
 }  // namespace dga
 
 using dga::AttnParams;
+
+namespace dg {
+uint64_t *clock_slot(int64_t blocks);  // gemm_tn.hip: the per-block clock records
+}
 
 namespace {
 
@@ -708,6 +741,7 @@ extern "C" int attention_fwd_f16(const void *Q, const void *K, const void *Vt, v
   p.blocks = (int32_t)(batch * tiles_m);
   p.n_blocks = (int32_t)((N + dga::kBN - 1) / dga::kBN);
   p.c = (float)((double)scale * 1.4426950408889634);  // scale * log2(e)
+  p.clk = dg::clock_slot(p.blocks);
   hipLaunchKernelGGL(dga::attention_fwd_kernel, dim3((unsigned)p.blocks), dim3(dga::kThreads), 0,
                      (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;

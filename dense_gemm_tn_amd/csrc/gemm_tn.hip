@@ -137,6 +137,7 @@ __device__ __forceinline__ float4_t_v mma(const int8_t_v &a, const int8_t_v &b, 
   asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b) : "memory");
   return c;
 }
+
 // Wait states after the last MFMA before its accumulators are read by other
 // instructions (more than the 16x16x32 result latency).
 __device__ __forceinline__ void mfma_drain() {
@@ -165,8 +166,8 @@ struct Params {
   int64_t stride_a_b, stride_b_b, stride_c_b;  // per-head strides in bytes
   int32_t tiles_m, tiles_n;
   float scale;           // fp8 only: fp32(scale_a * scale_b)
-  int32_t c_vec_ok;      // 8-byte C stores are aligned (ldc % 4 == 0)
-  int32_t c_vec16_ok;    // 16-byte C stores are aligned (ldc % 8 == 0)
+  int32_t c_vec_ok;      // 8-byte C stores are aligned (ldc, and stride_c with heads, % 4 == 0)
+  int32_t c_vec16_ok;    // 16-byte C stores are aligned (the same, % 8 == 0)
   int32_t sk_walk;       // skinny-K kernel: consecutive M tiles per block
   // Split-K partial products (128 x 128 kernel): split h covers K elements
   // [h * k_slice, min((h + 1) * k_slice, K)) and writes fp32 partial sums to
@@ -174,7 +175,76 @@ struct Params {
   int64_t k_slice;
   float *W;
   int64_t ldw;
+  int32_t order;         // block -> tile order (kOrderXcd unless measuring)
+  uint64_t *clk;         // per-block clock records, or null (see clock_mark)
 };
+
+// Per-block clock records (a measurement facility, off unless gemm_clock_record
+// has given the library a buffer): kClockWords 64-bit words per block at
+// clk[kClockWords * block] -- for each of four points (block start, K loop
+// start, K loop end, block end after its first wave's last stores completed)
+// the shader-clock counter (s_memtime) and the constant 100 MHz counter
+// (s_memrealtime), then the XCD the block ran on and the block index.
+// Counter ticks over real-time ticks give the clock the block ran at, per
+// XCD; the loop points split prologue, K loop and epilogue (kernels without a
+// pipelined K loop leave them zero).  Written from lane 0 of the first wave
+// with ordinary vector stores; nothing is kept live across the kernel body.
+enum { kClockStart = 0, kClockLoop = 1, kClockLoopEnd = 2, kClockEnd = 3, kClockWords = 10 };
+// This lane's index in its wave, recomputed from the execution mask rather
+// than kept from the kernel's start: an epilogue that takes the lane id from
+// here does not keep the work-item id live across the main loop, which in the
+// 256-register kernels would otherwise be spilled to scratch.  (Volatile, so
+// the compiler cannot reuse an earlier value.)
+__device__ __forceinline__ int lane_id_fresh() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// The record pointer is read from the kernel's argument segment at each mark
+// (a scalar load), so the compiler need not keep it in registers across the
+// K loop, where the 256-register kernels have none to spare.
+template <typename P>
+__device__ __forceinline__ uint64_t *clock_ptr() {
+  typedef uint64_t *const __attribute__((address_space(4))) *karg_t;
+  const __attribute__((address_space(4))) char *ka =
+      (const __attribute__((address_space(4))) char *)__builtin_amdgcn_kernarg_segment_ptr();
+  return *(volatile karg_t)(ka + offsetof(P, clk));
+}
+
+// `wave` is the caller's wave index (a uniform value); the lane index is
+// recomputed, so the work-item id need not stay live for the later marks.
+__device__ __forceinline__ void clock_mark(uint64_t *clk, int point, int wave) {
+  if (clk == nullptr) return;
+  if (point == kClockEnd) __builtin_amdgcn_s_waitcnt(0);
+  const uint64_t t = __builtin_amdgcn_s_memtime();
+  const uint64_t r = __builtin_amdgcn_s_memrealtime();
+  if (wave != 0 || lane_id_fresh() != 0) return;
+  uint64_t *rec = clk + kClockWords * (uint64_t)blockIdx.x;
+  rec[2 * point] = t;
+  rec[2 * point + 1] = r;
+  if (point == kClockStart) {
+    uint32_t xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    rec[8] = xcc & 15u;
+    rec[9] = blockIdx.x;
+  }
+}
+
+// Host side of the records: the buffer, its capacity in records and the next
+// free record.  A launch takes one record per block if they all fit, else
+// none (clk stays null).
+static std::atomic<uint64_t *> g_clk_buf{nullptr};
+static std::atomic<int64_t> g_clk_cap{0};
+static std::atomic<int64_t> g_clk_next{0};
+
+uint64_t *clock_slot(int64_t blocks) {
+  uint64_t *buf = g_clk_buf.load(std::memory_order_acquire);
+  if (buf == nullptr || blocks <= 0) return nullptr;
+  const int64_t base = g_clk_next.fetch_add(blocks, std::memory_order_relaxed);
+  if (base + blocks > g_clk_cap.load(std::memory_order_relaxed)) return nullptr;
+  return buf + kClockWords * base;
+}
 
 // Logical tile -> (head, tile_m, tile_n): the grouped order inside a head,
 // groups of kGroupM tile rows walked column by column (short last group
@@ -202,6 +272,15 @@ __host__ __device__ inline I xcd_first_tile(I x, I T) {
   return x * q + (x < r ? x : r);
 }
 
+// Block -> tile orders.  kOrderXcd is the one the library uses; the other two
+// exist to measure what it buys (DG_TILE_ORDER in the environment selects
+// them, see launch<>):
+//   kOrderXcd      chiplet-aware remap, then the grouped order;
+//   kOrderGrouped  the grouped order on the hardware block id (no remap);
+//   kOrderRow      row order: consecutive blocks walk one row of tiles
+//                  (tile_n fastest), heads one after another.
+enum { kOrderXcd = 0, kOrderGrouped = 1, kOrderRow = 2 };
+
 // Block id -> (head, tile_m, tile_n) for a grid of one block per tile.  The
 // dispatcher deals block b to XCD b % 8 as that XCD's (b / 8)-th block, so XCD
 // x is given the contiguous logical range starting at xcd_first_tile(x, G), a
@@ -210,9 +289,17 @@ __host__ __device__ inline I xcd_first_tile(I x, I T) {
 // and B strips in that XCD's L2.
 template <typename I>
 __host__ __device__ inline void tile_of_block(I b, I G, I tiles_m, I tiles_n, I *head, I *tm,
-                                              I *tn) {
-  const I x = b % kXcds, idx = b / kXcds;
-  tile_coords<I>(xcd_first_tile<I>(x, G) + idx, tiles_m, tiles_n, head, tm, tn);
+                                              I *tn, int order = kOrderXcd) {
+  if (order == kOrderRow) {
+    const I per_head = tiles_m * tiles_n;
+    *head = b / per_head;
+    const I t = b - *head * per_head;
+    *tm = t / tiles_n;
+    *tn = t - *tm * tiles_n;
+    return;
+  }
+  const I logical = order == kOrderGrouped ? b : xcd_first_tile<I>(b % kXcds, G) + b / kXcds;
+  tile_coords<I>(logical, tiles_m, tiles_n, head, tm, tn);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -541,8 +628,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int head, tm, tn;
-  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
+  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn,
+                     p.order);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTileN;
+  clock_mark(clock_ptr<Params>(), kClockStart, wave);
 
   // Block bases: K-contiguous operands at their first row, M/N-contiguous ones
   // at their first column (element m0 / n0 of K-row 0).
@@ -777,6 +866,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   StepScalars un;
   constexpr int kPlan = kBarSlot - 6;
   static_assert(kPlan >= 0 && kPlan >= kWin - kAfter, "plan after the last copy of step t + 1");
+  clock_mark(clock_ptr<Params>(), kClockLoop, wave);
   for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {            // K-step t0 + h lives in stage h
@@ -830,18 +920,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   for (int i = 0; i < NTM; ++i)
 #pragma unroll
     for (int j = 0; j < NTN; ++j) asm volatile("" : "+a"(acc[i][j]));
+  clock_mark(clock_ptr<Params>(), kClockLoopEnd, wave);
 
   // Drain the trailing zero copies; every wave leaves the stages before the
   // epilogue reuses the LDS.
   __builtin_amdgcn_s_waitcnt(0);
+  const int elane = lane_id_fresh();
   if (p.c_vec16_ok) {
     __syncthreads();
     store_c_lds<KIND, NTN>(p, Cb, acc,
                            (__attribute__((address_space(3))) uint8_t *)smem + wave * 32768,
-                           m0 + wm * kWaveTile, n0 + wn * S::WN, lane);
+                           m0 + wm * kWaveTile, n0 + wn * S::WN, elane);
   } else {
-    store_c<KIND, NTN>(p, Cb, acc, m0 + wm * kWaveTile, n0 + wn * S::WN, lane);
+    store_c<KIND, NTN>(p, Cb, acc, m0 + wm * kWaveTile, n0 + wn * S::WN, elane);
   }
+  clock_mark(clock_ptr<Params>(), kClockEnd, wave);
 }
 
 template __global__ void gemm_tn_kernel<kF16, 8, false, false>(Params);
@@ -1011,7 +1104,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_skinny_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int chunks_m = (p.tiles_m + p.sk_walk - 1) / p.sk_walk;
   int head, tmc, tn;
-  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, chunks_m, p.tiles_n, &head, &tmc, &tn);
+  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, chunks_m, p.tiles_n, &head, &tmc, &tn,
+                     p.order);
+  clock_mark(clock_ptr<Params>(), kClockStart, wave);
   const int tm0 = tmc * p.sk_walk;
   const int tm_end = (tm0 + p.sk_walk) < p.tiles_m ? (tm0 + p.sk_walk) : p.tiles_m;
   lds_u8 *const a_st = (lds_u8 *)smem;
@@ -1059,6 +1154,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_skinny_kernel(Params p) {
       }
     }
   }
+  clock_mark(clock_ptr<Params>(), kClockEnd, wave);
 }
 
 template __global__ void gemm_tn_skinny_kernel<kF16>(Params);
@@ -1207,8 +1303,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   int head, tm, tn;
-  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
+  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn,
+                     p.order);
   const int64_t m0 = (int64_t)tm * kMidTile, n0 = (int64_t)tn * kMidTile;
+  clock_mark(clock_ptr<Params>(), kClockStart, wave);
   // Split-K: the "head" index is the split; this block's K range starts at
   // k_begin (a whole number of K-steps) and the operands are read from there.
   const int64_t k_begin = SPLIT ? head * p.k_slice : 0;
@@ -1365,6 +1463,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
         }
       }
     }
+    clock_mark(clock_ptr<Params>(), kClockEnd, wave);
     return;
   }
 #pragma unroll
@@ -1388,6 +1487,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_mid_kernel(Params p) {
       }
     }
   }
+  clock_mark(clock_ptr<Params>(), kClockEnd, wave);
 }
 
 // Split-K reduction: C(m, n) = convert(sum over splits h = 0, 1, ... of
@@ -1513,8 +1613,10 @@ __global__ __launch_bounds__(kPpThreads, 1) void gemm_tn_pp_kernel(Params p) {
   const int grp = wave >> 2, wm = wave & 3;
 
   int head, tm, tn;
-  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn);
+  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn,
+                     p.order);
   const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+  clock_mark(clock_ptr<Params>(), kClockStart, wave);
   const uint8_t *Ab = p.A + head * p.stride_a_b + m0 * p.lda_b;
   const uint8_t *Bb = p.B + head * p.stride_b_b + n0 * p.ldb_b;
   uint8_t *Cb = p.C + head * p.stride_c_b;
@@ -1629,17 +1731,19 @@ __global__ __launch_bounds__(kPpThreads, 1) void gemm_tn_pp_kernel(Params p) {
   __syncthreads();
 
   const int64_t mb = m0 + wm * kPpWaveM, nb = n0 + grp * kPpWaveN;
+  const int elane = lane_id_fresh();   // not kept live across the loop (see lane_id_fresh)
   if (p.c_vec16_ok) {
-    store_c_pp<KIND>(p, Cb, acc, (lds_u8 *)smem + wave * 16384, mb, nb, lane);
+    store_c_pp<KIND>(p, Cb, acc, (lds_u8 *)smem + wave * 16384, mb, nb, elane);
   } else {
     // Runs of four rows, 8-byte or 2-byte stores.
+    const int erl = elane & 15, ekg = elane >> 4;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int64_t n = nb + 16 * j + rl;
+      const int64_t n = nb + 16 * j + erl;
       if (n >= p.N) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t m = mb + 16 * i + 4 * kg;
+        const int64_t m = mb + 16 * i + 4 * ekg;
         uint32_t w0, w1;
         pack_run<KIND>(p, acc[i][j], 0, w0, w1);
         uint16_t *dst = (uint16_t *)Cb + (n * p.ldc + m);
@@ -1655,6 +1759,7 @@ __global__ __launch_bounds__(kPpThreads, 1) void gemm_tn_pp_kernel(Params p) {
       }
     }
   }
+  clock_mark(clock_ptr<Params>(), kClockEnd, wave);
 }
 
 // Kernel configuration of a problem (the codes are the C ABI's
@@ -1697,6 +1802,16 @@ static Config choose_config(int es, int64_t M, int64_t N, int64_t K, int64_t bat
   const int64_t t_mid = ((mid_blocks + cus - 1) / cus) * kMidTile * kMidTile * kMidCost;
   if (t_mid < t_big) return Config{kCfgMid};
   return Config{ntn == 7 ? kCfg224 : kCfg256};
+}
+
+// DG_TILE_ORDER = row | grouped selects a measurement order for the TN
+// calls (see tile_of_block); anything else, or nothing, the library's own.
+static int tile_order_env() {
+  const char *o = getenv("DG_TILE_ORDER");
+  if (!o) return kOrderXcd;
+  if (!strcmp(o, "row")) return kOrderRow;
+  if (!strcmp(o, "grouped")) return kOrderGrouped;
+  return kOrderXcd;
 }
 
 // Host-side validation of a TN call (the rules the header states); -1 for a
@@ -1772,9 +1887,15 @@ static int launch(const Problem &pr, hipStream_t stream) {
   p.stride_a_b = pr.stride_a * es; p.stride_b_b = pr.stride_b * es; p.stride_c_b = pr.stride_c * 2;
   p.tiles_m = (int32_t)tiles_m; p.tiles_n = (int32_t)tiles_n;
   p.scale = pr.scale;
-  p.c_vec_ok = (pr.ldc % 4 == 0) ? 1 : 0;
-  p.c_vec16_ok = (pr.ldc % 8 == 0) ? 1 : 0;
+  // Store widths: a column start (and, with several heads, a head start) is
+  // 8-byte aligned when ldc (stride_c) is a multiple of 4 elements, 16-byte
+  // aligned when it is a multiple of 8 (C itself is 16-byte aligned).
+  const bool heads = pr.batch > 1;
+  p.c_vec_ok = (pr.ldc % 4 == 0 && (!heads || pr.stride_c % 4 == 0)) ? 1 : 0;
+  p.c_vec16_ok = (pr.ldc % 8 == 0 && (!heads || pr.stride_c % 8 == 0)) ? 1 : 0;
   p.sk_walk = (int32_t)walk;
+  p.order = tile_order_env();
+  p.clk = clock_slot(blocks);
 
   if (skinny)
     hipLaunchKernelGGL(gemm_tn_skinny_kernel<KIND>, dim3((unsigned)blocks), dim3(kThreads), 0,
@@ -1858,6 +1979,7 @@ static int launch_layout(char ta, char tb, const Problem &pr, hipStream_t stream
   p.c_vec_ok = (pr.ldc % 4 == 0) ? 1 : 0;
   p.c_vec16_ok = (pr.ldc % 8 == 0) ? 1 : 0;
   p.sk_walk = 1;
+  p.clk = clock_slot(blocks);
   const dim3 grid((unsigned)blocks), block(kThreads);
   // One kernel per (layout, configuration).
   typedef void (*kernel_t)(Params);
@@ -1926,21 +2048,24 @@ static int launch_splitk(const Problem &pr, int64_t splits, void *ws, int64_t ws
   p.k_slice = per * T::kstep;
   p.W = (float *)ws;
   p.ldw = ldw;
+  p.clk = clock_slot(blocks);
   hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false, true>), dim3((unsigned)blocks),
                      dim3(kThreads), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return DG_ERR_HIP;
+  p.clk = nullptr;
   hipLaunchKernelGGL(gemm_splitk_reduce_kernel<KIND>, dim3((unsigned)rblocks), dim3(kThreads), 0,
                      stream, p, (int32_t)S);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
 // Suggested split count: as many splits of the 128 x 128 tiles as fit one
-// block per CU (never a second round), doubled to two blocks per CU when each
-// range would still be 4 * kSplitMinSteps K-steps or longer (the second block
-// hides the first one's waits), each split keeping at least kSplitMinSteps
-// K-steps; 1 when the tiles alone fill half the CUs or K is short.  (Measured
-// on 512^2 x 32768, 256^2 x 65536, 1024^2 x 16384, 1024 x 512 x 16384 and
-// 768^2 x 8192: within 3 % of the best count of a sweep.)
+// block per CU (never a second round), doubled to two blocks per CU when the
+// one-block-per-CU ranges are 4 * kSplitMinSteps K-steps or longer (so the
+// doubled ranges keep at least 2 * kSplitMinSteps; the second block hides the
+// first one's waits), each split keeping at least kSplitMinSteps K-steps; 1
+// when the tiles alone fill half the CUs or K is short.  (Measured on 512^2 x
+// 32768, 256^2 x 65536, 1024^2 x 16384, 1024 x 512 x 16384 and 768^2 x 8192:
+// within 3 % of the best count of a sweep.)
 constexpr int64_t kSplitMinSteps = 16;
 static int64_t choose_splits(int es, int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 1;
@@ -2040,6 +2165,19 @@ int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch) {
   if (M < 0 || N < 0 || K < 0 || batch < 0) return -1;
   return dg::choose_config(fp8 ? 1 : 2, M, N, K, batch).kind;
 }
+
+int gemm_clock_record(void *buf, int64_t records) {
+  if (records < 0 || (buf == nullptr && records != 0) || (buf != nullptr && records == 0))
+    return DG_ERR_INVALID_ARGUMENT;
+  if (((uintptr_t)buf & 7u) != 0) return DG_ERR_UNSUPPORTED;
+  dg::g_clk_buf.store(nullptr, std::memory_order_release);
+  dg::g_clk_cap.store(records, std::memory_order_relaxed);
+  dg::g_clk_next.store(0, std::memory_order_relaxed);
+  dg::g_clk_buf.store((uint64_t *)buf, std::memory_order_release);
+  return DG_OK;
+}
+
+int64_t gemm_clock_records_used(void) { return dg::g_clk_next.load(std::memory_order_relaxed); }
 
 int64_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits) {
   if (M < 0 || N < 0 || splits < 1 || splits > dg::kSplitMax) return -1;

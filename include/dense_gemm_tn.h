@@ -12,10 +12,12 @@
  *   A[m*lda + k]   m < M, k < K    (row-major, row stride lda >= K)
  *   B[n*ldb + k]   n < N, k < K    (column n of B is K contiguous elements)
  *   C[m + n*ldc]   m < M, n < N    (column-major, ldc >= M)
- * Elements of A and B outside those index ranges are never read, and C is
- * written only at those M*N positions: ldc padding and memory around C are
- * left untouched (the tail rules of section 11.4 of the hello-gpu chapter:
- * out-of-range operand elements contribute zero, out-of-range C is not written).
+ * For these TN calls, elements of A and B outside those index ranges are
+ * never read, and C is written only at those M*N positions: ldc padding and
+ * memory around C are left untouched (the tail rules of section 11.4 of the
+ * hello-gpu chapter: out-of-range operand elements contribute zero,
+ * out-of-range C is not written).  (The op-code layout calls gemm_f16 and
+ * gemm_f8 relax the read rule for M- or N-contiguous operands; see there.)
  *
  * Ownership and ordering:
  *   All matrix pointers are DEVICE pointers on the current HIP device; the
@@ -77,8 +79,16 @@ int gemm_f16_tn(const void *A, const void *B, void *C,
  * Lower-case codes are accepted.  ('T', 'N') is exactly gemm_f16_tn, with its
  * tile configurations; the other three run 256 x 256 or 128 x 128 tiles (see
  * gemm_f16_config), each M- or N-contiguous operand staged in LDS as it lies
- * and turned by transposing LDS reads.  Rounding, tails,
- * ownership and ordering are those of gemm_f16_tn.  Row-major C = A B with
+ * and turned by transposing LDS reads.  Rounding, ownership, ordering and the
+ * C rule (only the M*N logical positions are written) are those of
+ * gemm_f16_tn.  Reads differ for an M- or N-contiguous operand (A of an 'N'
+ * op, B of a 'T' op): it is copied in whole K-rows of a block's 256 (or 128)
+ * columns, so elements past M (or N) in a K-row -- its lda (ldb) padding or,
+ * in the last block, the start of the next K-row -- may be read.  Every byte
+ * read still lies inside the operand's span, [A, A + ((K-1)*lda + M)*es) for
+ * A 'N' ([B, B + ((K-1)*ldb + N)*es) for B 'T'), and such elements only feed
+ * outputs past M (N), which are never stored, so their values (NaN included)
+ * never reach C.  K-contiguous operands keep the TN rule.  Row-major C = A B with
  * A row-major M x K and B row-major K x N (the NN indexing of section 11.1 of
  * the hello-gpu chapter) is this call with transa = transb = 'N' on the
  * operands swapped: C^T = B^T A^T, computed as gemm_f16('N', 'N', B, A, C,
@@ -120,7 +130,8 @@ int gemm_f8_tn(const void *A, const void *B, void *C,
  * ('T', 'N') is gemm_f8_tn.  The chunk granularity is 16 elements: lda, ldb,
  * K (when an operand is K-contiguous), M (transa 'N') and N (transb 'T') must
  * be multiples of 16, else DG_ERR_UNSUPPORTED; a K-step of an M/N-contiguous
- * operand is 128 K-rows here; other errors as for gemm_f16.
+ * operand is 128 K-rows here; other errors, and the read rule for M- or
+ * N-contiguous operands, as for gemm_f16.
  * Source: the FP8 GEMM of "AMD ROCm 4-wave interleave FP8 GEMM for Instinct
  * MI355X (CDNA 4)" and, for the layouts, "FP16 GEMM optimisation on AMD RDNA 3
  * and RDNA 4", section "What we compute".
@@ -143,7 +154,11 @@ int gemm_f8(char transa, char transb, const void *A, const void *B, void *C,
  * Source: the QK^T kernel sketch of the mlqm.cn TileLang attention page
  * (K dimension = head dim 128).  Strides are in elements; ldq, ldk >= D,
  * lds >= M; the per-head regions of S must not overlap (stride_s >= lds*N
- * when batch > 1), otherwise DG_ERR_INVALID_ARGUMENT.
+ * when batch > 1), otherwise DG_ERR_INVALID_ARGUMENT.  ldq, ldk, stride_q and
+ * stride_k must be multiples of 8 (16-byte rows and heads of Q and K), else
+ * DG_ERR_UNSUPPORTED; lds and stride_s may be any value: S is stored 16 bytes
+ * at a time when both are multiples of 8, 8 bytes at a time when both are
+ * multiples of 4, element by element otherwise.
  */
 int gemm_batched_qkt(const void *Q, const void *Kmat, void *S,
                      int64_t batch, int64_t M, int64_t N, int64_t D,
@@ -201,6 +216,11 @@ const char *gemm_status_string(int status);
  * hardware block id b the triple (head, tile_m, tile_n) to out[3*b .. 3*b+2].
  * `out` is a HOST buffer of 3*batch*tiles_m*tiles_n int64 values.  Returns
  * DG_ERR_INVALID_ARGUMENT for a null `out` or non-positive sizes.
+ * For measurement only, the environment variable DG_TILE_ORDER = grouped
+ * (the grouped order without the chiplet remap) or row (consecutive blocks
+ * along a row of tiles) changes the order the TN calls (gemm_f16_tn,
+ * gemm_f8_tn, gemm_batched_qkt) use; this function always reports the
+ * library's own order.
  */
 int gemm_tile_order(int64_t tiles_m, int64_t tiles_n, int64_t batch, int64_t *out);
 
@@ -280,15 +300,43 @@ int gemm_f8_tn_splitk(const void *A, const void *B, void *C,
                       int64_t splits, void *workspace, int64_t workspace_bytes,
                       void *stream);
 
+/*
+ * Per-block clock records, a measurement facility (off by default).  After
+ * gemm_clock_record(buf, records) with a device buffer of `records` records
+ * of ten uint64 words (80 bytes each, 8-byte aligned), every launch of the
+ * calls above takes one record per block, in launch order, while they fit
+ * (a launch that does not fit whole records nothing; the split-K reduction
+ * kernel records nothing).  Words 2p and 2p+1 of a block's record hold the
+ * shader-clock counter and the constant 100 MHz counter at point p: 0 the
+ * block's start, 1 the start of its pipelined K loop, 2 the end of that loop,
+ * 3 after its first wave's last stores completed (points 1 and 2 are left
+ * zero by kernels without a pipelined K loop: the 128 x 128, skinny-K,
+ * ping-pong and attention kernels); word 8 is the XCD it ran on and word 9
+ * its block index.  Counter ticks over real-time ticks are the clock it ran at.
+ * gemm_clock_record(NULL, 0) turns recording off; gemm_clock_records_used()
+ * returns the records taken (or asked for, if more) since the last
+ * gemm_clock_record call.  The setting is process-wide; the buffer must stay
+ * valid while recording is on.  Errors: DG_ERR_INVALID_ARGUMENT for a
+ * negative count or a NULL buffer with a nonzero count (or the reverse),
+ * DG_ERR_UNSUPPORTED for a misaligned buffer.
+ * Source: the benchmarking method of "AMD ROCm 4-wave interleave FP8 GEMM for
+ * Instinct MI355X (CDNA 4)", section "Hardware platform and chiplet-aware
+ * optimisation" (per-XCD behaviour of the 8-chiplet part), and the RDNA page's
+ * section "Measuring resources" (timing what the kernel does).
+ */
+int gemm_clock_record(void *buf, int64_t records);
+int64_t gemm_clock_records_used(void);
+
 /* Workspace bytes the split-K calls need for M x N and `splits`:
  * splits * N * (M rounded up to 4) * 4; -1 for invalid arguments. */
 int64_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
 
 /* Suggested split count for an M x N x K TN product (fp8 != 0: FP8): as many
- * splits of the 128 x 128 tiles as fit one block per compute unit (two per
- * compute unit when each range would still be 64 K-steps or longer), each
- * keeping at least 16 K-steps and at most 64 splits; 1 when the tiles alone
- * fill half the compute units.  -1 for negative sizes. */
+ * splits of the 128 x 128 tiles as fit one block per compute unit, doubled to
+ * two per compute unit when those one-per-unit ranges are 64 K-steps or longer
+ * (the doubled ranges then keep at least 32), each keeping at least 16 K-steps
+ * and at most 64 splits; 1 when the tiles alone fill half the compute units.
+ * -1 for negative sizes. */
 int64_t gemm_splitk_choose(int fp8, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus

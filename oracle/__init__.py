@@ -104,6 +104,16 @@ def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
 
 
+def _default_threads() -> int:
+    """Threads for the oracle's column ranges: the cores this process may run on,
+    capped by OMP_NUM_THREADS when it is set (the host's share of a shared box)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
 def decode(codes: np.ndarray, fmt: int) -> np.ndarray:
     """Exact binary64 value of every element code."""
     raw = _raw(codes, fmt)
@@ -142,7 +152,7 @@ def gemm_tn(A: np.ndarray, B: np.ndarray, fmt: int, M: int, N: int, K: int,
         raise ValueError("B is too small for N, K, ldb")
     C = np.zeros((N, M), dtype=np.float64)
     if nthreads is None:
-        nthreads = len(os.sched_getaffinity(0))
+        nthreads = _default_threads()
     rc = _load().oracle_gemm_tn(fmt, _ptr(ra), _ptr(rb), _ptr(C), M, N, K, lda, ldb, M,
                                 float(scale), int(nthreads))
     if rc:
@@ -188,7 +198,7 @@ def gemm_strided(A: np.ndarray, sam: int, sak: int, B: np.ndarray, sbk: int, sbn
         raise ValueError("C is too small for its strides")
     C = np.zeros(c_size, dtype=np.float64)
     if nthreads is None:
-        nthreads = len(os.sched_getaffinity(0))
+        nthreads = _default_threads()
     rc = _load().oracle_gemm_strided(fmt, _ptr(ra), sam, sak, _ptr(rb), sbk, sbn, _ptr(C), scm,
                                      scn, M, N, K, float(scale), int(nthreads))
     if rc:
@@ -284,7 +294,7 @@ def attention_rows(Q: np.ndarray, Kmat: np.ndarray, Vt: np.ndarray, N: int, D: i
         raise ValueError("K or Vt too small")
     out = np.empty((rows.size, D), dtype=np.float64)
     if nthreads is None:
-        nthreads = len(os.sched_getaffinity(0))
+        nthreads = _default_threads()
     rc = _load().oracle_attention_rows(_ptr(rq), _ptr(rk), _ptr(rv), N, D, ldq, ldk, ldv,
                                        _ptr(rows), rows.size, float(scale), _ptr(out),
                                        int(nthreads))

@@ -361,3 +361,94 @@ def test_splitk_workspace_and_choice():
     assert dg.splitk_choose(512, 512, 1024) == 1
     assert dg.splitk_choose(512, 512, 0) == 1
     assert dg.splitk_choose(-1, 512, 4096) == -1
+
+
+def test_splitk_choose_doubling_rule():
+    # One block per CU gives S = CUs / tiles; the count doubles when those
+    # ranges are >= 64 K-steps, so the doubled ranges are >= 32 steps
+    # (1024^2 x 16384 fp16: 64 tiles, 256 K-steps -> 4 ranges of 64 -> 8 of 32).
+    assert dg.splitk_choose(1024, 1024, 16384) == 8
+    assert dg.splitk_choose(1024, 1024, 16384, fp8=True) == 4   # 128 steps: 4 ranges of 32
+    assert dg.splitk_choose(1024, 512, 16384) == 8              # 256 steps / 8 = 32: no doubling
+    assert dg.splitk_choose(512, 512, 32768) == 16
+    assert dg.splitk_choose(768, 768, 8192) == 7                # 36 tiles: floor(256 / 36)
+    assert dg.splitk_choose(256, 256, 65536) == 64
+
+
+# ------------------------------------------------- tensor helpers (no launches)
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.mark.parametrize("call", [
+    # CPU tensors: host pointers must never reach a kernel.
+    lambda: dg.matmul_tn_f16(torch.zeros(16, 16, dtype=torch.float16),
+                             torch.zeros(16, 16, dtype=torch.float16)),
+    lambda: dg.matmul_tn_f8(torch.zeros(16, 16, dtype=torch.uint8),
+                            torch.zeros(16, 16, dtype=torch.uint8), 1.0, 1.0),
+    lambda: dg.qkt(torch.zeros(2, 8, 16, dtype=torch.float16),
+                   torch.zeros(2, 8, 16, dtype=torch.float16)),
+    lambda: dg.attention(torch.zeros(1, 8, 128, dtype=torch.float16),
+                         torch.zeros(1, 8, 128, dtype=torch.float16),
+                         torch.zeros(1, 128, 8, dtype=torch.float16)),
+    lambda: dg.matmul_f16(torch.zeros(16, 16, dtype=torch.float16),
+                          torch.zeros(16, 16, dtype=torch.float16)),
+])
+def test_helpers_reject_host_tensors(call):
+    with pytest.raises(ValueError, match="GPU"):
+        call()
+
+
+def test_helpers_reject_strided_rows():
+    a = torch.zeros(16, 32, dtype=torch.float16)[:, ::2]   # stride(1) == 2
+    b = torch.zeros(16, 16, dtype=torch.float16)
+    with pytest.raises(ValueError, match="contiguous"):
+        dg.matmul_tn_f16(a, b)
+    with pytest.raises(ValueError, match="contiguous"):
+        dg.matmul_tn_f8(torch.zeros(16, 32, dtype=torch.uint8)[:, ::2],
+                        torch.zeros(16, 16, dtype=torch.uint8), 1.0, 1.0)
+    q = torch.zeros(2, 8, 32, dtype=torch.float16)[:, :, ::2]
+    with pytest.raises(ValueError, match="contiguous"):
+        dg.qkt(q, torch.zeros(2, 8, 16, dtype=torch.float16))
+
+
+@pytest.mark.parametrize("out,match", [
+    (torch.zeros(8, 16, dtype=torch.float16), "shape"),          # fewer than N rows
+    (torch.zeros(16, 8, dtype=torch.float16), "shape"),          # fewer than M columns
+    (torch.zeros(16, 16, dtype=torch.float32), "dtype"),
+    (torch.zeros(16, 32, dtype=torch.float16)[:, ::2], "contiguous"),
+    (torch.zeros(16, 16, dtype=torch.float16).as_strided((16, 16), (4, 1)), "overlap"),
+])
+def test_helpers_reject_bad_out(out, match):
+    a = torch.zeros(16, 16, dtype=torch.float16)
+    with pytest.raises(ValueError, match=match):
+        dg.matmul_tn_f16(a, a, out=out)
+    if out.dtype == torch.float16 and match != "dtype":
+        with pytest.raises(ValueError, match=match):
+            dg.matmul_f16(a, a, out=out)
+
+
+def test_qkt_and_attention_reject_bad_out():
+    q = torch.zeros(2, 8, 16, dtype=torch.float16)
+    with pytest.raises(ValueError, match="shape"):
+        dg.qkt(q, q, out=torch.zeros(2, 8, 4, dtype=torch.float16))
+    with pytest.raises(ValueError, match="dtype"):
+        dg.qkt(q, q, out=torch.zeros(2, 8, 8, dtype=torch.bfloat16))
+    q = torch.zeros(1, 8, 128, dtype=torch.float16)
+    vt = torch.zeros(1, 128, 8, dtype=torch.float16)
+    with pytest.raises(ValueError, match="shape"):
+        dg.attention(q, q, vt, out=torch.zeros(1, 4, 128, dtype=torch.float16))
+    with pytest.raises(ValueError, match="dtype"):
+        dg.matmul_tn_f8(torch.zeros(16, 16, dtype=torch.uint8), torch.zeros(16, 16, dtype=torch.uint8),
+                        1.0, 1.0, out=torch.zeros(16, 16, dtype=torch.float16))
+
+
+def test_clock_record_validation():
+    L = dg.lib()
+    assert L.gemm_clock_record(None, 0) == dg.DG_OK
+    assert L.gemm_clock_records_used() == 0
+    assert L.gemm_clock_record(None, 5) == dg.DG_ERR_INVALID_ARGUMENT
+    assert L.gemm_clock_record(A_ADDR, 0) == dg.DG_ERR_INVALID_ARGUMENT
+    assert L.gemm_clock_record(A_ADDR, -1) == dg.DG_ERR_INVALID_ARGUMENT
+    assert L.gemm_clock_record(A_ADDR + 4, 8) == dg.DG_ERR_UNSUPPORTED
+    assert L.gemm_clock_record(None, 0) == dg.DG_OK

@@ -75,3 +75,29 @@ def test_traffic_lookup_needs_matching_source(tmp_path, monkeypatch):
 @pytest.mark.parametrize("name", sorted(inputs.WORKLOADS))
 def test_every_workload_names_its_kernel(name):
     assert bench.kernel_name(inputs.WORKLOADS[name])
+
+
+def test_default_list_starts_with_the_five_configurations():
+    five = ("f16_4096", "f8_8192", "f16_256_pm1", "f16_1920x13900x4096", "qkt_64x4096x4096x128")
+    assert bench.DEFAULT_WORKLOADS[:5] == five
+    assert all(n in inputs.WORKLOADS for n in bench.DEFAULT_WORKLOADS)
+    assert len(set(bench.DEFAULT_WORKLOADS)) == len(bench.DEFAULT_WORKLOADS)
+
+
+def test_clock_summary_from_records():
+    import numpy as np
+    # Block 0 on XCD 0: 2000 shader ticks in 100 real ticks (2 GHz), with the
+    # loop from real tick 10 to 90; block 1 on XCD 1 at 1.5 GHz without loop
+    # points; an empty record is skipped.
+    rec = np.array([[10, 0, 30, 10, 1830, 90, 2010, 100, 0, 0],
+                    [100, 50, 0, 0, 0, 0, 1600, 150, 1, 1],
+                    [0] * 10], dtype=np.uint64)
+    c = bench.clock_summary(rec)
+    assert c["blocks"] == 2
+    assert c["sclk_mhz_per_xcd"] == {0: 2000.0, 1: 1500.0}
+    assert c["sclk_mhz"] == 1750.0 and c["block_us_median"] == 1.0
+    assert "loop_us_median" not in c           # block 1 has no loop points
+    c = bench.clock_summary(rec[:1])
+    assert c["prologue_us_median"] == 0.1 and c["loop_us_median"] == 0.8
+    assert c["epilogue_us_median"] == 0.1 and c["loop_sclk_mhz"] == 2250.0
+    assert bench.clock_summary(np.zeros((3, 10), np.uint64)) is None

@@ -151,3 +151,22 @@ def test_matmul_helper_splitk(splits):
     ref = oracle.gemm_tn(x["A"], x["B"], oracle.FMT_F16, M, N, K)
     want = oracle.decode(oracle.encode(ref, oracle.FMT_F16), oracle.FMT_F16)
     assert np.array_equal(oracle.decode(c.cpu().numpy(), oracle.FMT_F16), want)
+
+
+@pytest.mark.parametrize("kind,M,N,K", [("f16", 1024, 1024, 16384), ("f8", 1024, 1024, 32768)])
+def test_splitk_chooser_doubled_configuration(kind, M, N, K):
+    """The chooser's two-blocks-per-CU branch (1024^2 x 16384 fp16: 64 tiles,
+    8 ranges of 32 K-steps on 256 CUs), run with the count it suggests: +-1
+    data exact against the oracle, canaries around C and past the workspace."""
+    splits = dg.splitk_choose(M, N, K, fp8=(kind == "f8"))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = (M // 128) * (N // 128)
+    assert splits == 2 * (cus // tiles)   # the doubled branch on this device
+    print("splitk chooser %s %dx%dx%d splits %d" % (kind, M, N, K, splits), flush=True)
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=23)
+    got, canary, ws_ok, _ = run(kind, x, M, N, K, splits)
+    assert canary and ws_ok
+    ref = oracle.gemm_tn(x["A"], x["B"], fmt_in(kind), M, N, K)
+    want = oracle.decode(oracle.encode(ref, fmt_out(kind)), fmt_out(kind))
+    g = oracle.decode(got, fmt_out(kind))
+    assert np.array_equal(g, want), "%d mismatches" % int((g != want).sum())

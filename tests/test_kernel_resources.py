@@ -1,0 +1,43 @@
+"""Compile-time resources of every kernel (no GPU needed).
+
+The device code of both sources is compiled with the build's flags and the
+compiler's resource-usage remarks (the resource report the RDNA page reads in
+"Measuring resources": registers, scratch, LDS).  Every kernel must run
+without scratch (no register spills: a spill in the 256-register kernels
+turns into memory traffic inside the block), the 256 x 256 kernels must hold
+their 256 accumulator registers as AGPRs at one wave per SIMD, and the report
+is written to profiles/kernel_resources.md.
+"""
+import pytest
+
+from dense_gemm_tn_amd import build
+
+
+@pytest.fixture(scope="module")
+def rows():
+    r = build.resources()
+    build.write_resource_report(r)
+    return r
+
+
+def test_every_kernel_reported(rows):
+    names = {r["kernel"] for r in rows}
+    for want in ("gemm_tn_kernel<0, 8, false, false>", "gemm_tn_kernel<1, 8, false, false>",
+                 "gemm_tn_skinny_kernel<0>", "gemm_tn_mid_kernel<0, false, false, false>",
+                 "gemm_splitk_reduce_kernel<0>", "attention_fwd_kernel"):
+        assert any(want in n for n in names), want
+    assert len(rows) >= 27
+
+
+def test_no_scratch_anywhere(rows):
+    bad = [(r["kernel"], r.get("ScratchSize [bytes/lane]"), r.get("VGPRs Spill"))
+           for r in rows
+           if r.get("ScratchSize [bytes/lane]") != "0" or r.get("VGPRs Spill", "0") != "0"]
+    assert not bad, bad
+
+
+def test_big_tiles_hold_accumulators_in_agprs(rows):
+    for r in rows:
+        if "gemm_tn_kernel<" in r["kernel"]:
+            assert int(r["AGPRs"]) >= 224 and r["Occupancy [waves/SIMD]"] == "1", r
+            assert int(r["LDS Size [bytes/block]"]) == 131072, r
