@@ -42,6 +42,7 @@ EXPORTS = (
     "gemm_splitk_choose",
     "gemm_clock_record",
     "gemm_clock_records_used",
+    "gemm_f16_tn_splitk_noalloc",
 )
 
 _lib = None
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_clock_record.restype = ctypes.c_int
         L.gemm_clock_records_used.argtypes = []
         L.gemm_clock_records_used.restype = i64
+        L.gemm_f16_tn_splitk_noalloc.argtypes = [vp, vp, vp] + [i64] * 7 + [vp]
+        L.gemm_f16_tn_splitk_noalloc.restype = ctypes.c_int
         for f in (L.gemm_f16_tn, L.gemm_f16, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
                   L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config, L.gemm_f16_config,
                   L.gemm_f8, L.gemm_f8_config, L.gemm_f16_tn_splitk, L.gemm_f8_tn_splitk):
@@ -188,6 +191,14 @@ def gemm_f16_tn_splitk(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc:
     _check("gemm_f16_tn_splitk",
            lib().gemm_f16_tn_splitk(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc, splits,
                                     _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def gemm_f16_tn_splitk_noalloc(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
+                               splits: int, stream=None) -> None:
+    """gemm_f16_tn_splitk with the partials in the library's static 32 MiB device array."""
+    _check("gemm_f16_tn_splitk_noalloc",
+           lib().gemm_f16_tn_splitk_noalloc(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                                            splits, _stream(stream)))
 
 
 def gemm_f8_tn_splitk(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,

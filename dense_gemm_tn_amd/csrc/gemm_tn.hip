@@ -70,6 +70,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "dense_gemm_tn.h"
@@ -2058,6 +2059,37 @@ static int launch_splitk(const Problem &pr, int64_t splits, void *ws, int64_t ws
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
+// The no-allocation split-K entry point keeps its fp32 partials in this
+// file-scope device array instead of a caller workspace: 32 MiB per device,
+// which the runtime places on each GPU the library runs on and keeps until
+// the process ends.  Host code never passes `scratch` itself to a kernel (on
+// the host that name is only a stand-in for the symbol): scratch_ptr() looks
+// the device address up once per device with hipGetSymbolAddress and every
+// launch takes that address.  Nothing in the array has to start at zero:
+// each launch writes every partial it later reads (the reduction's reads of
+// the row padding between M and the rounded-up M only feed rows that are not
+// stored).  All calls on one device share the array, so calls that overlap
+// in time on that device (concurrent streams) race.
+constexpr int64_t kScratchBytes = 32ll << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_dev[64];   // device address of `scratch` per device, once looked up
+
+// Device address of `scratch` on the current device (nullptr if the lookup fails).
+static void *scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return nullptr;
+    g_scratch_dev[dev] = ptr;
+  }
+  return g_scratch_dev[dev];
+}
+
 // Suggested split count: as many splits of the 128 x 128 tiles as fit one
 // block per CU (never a second round), doubled to two blocks per CU when the
 // one-block-per-CU ranges are 4 * kSplitMinSteps K-steps or longer (so the
@@ -2194,6 +2226,23 @@ int gemm_f16_tn_splitk(const void *A, const void *B, void *C, int64_t M, int64_t
                        int64_t workspace_bytes, void *stream) {
   dg::Problem pr{A, B, C, 1, M, N, K, lda, ldb, ldc, 0, 0, 0, 1.0f};
   return dg::launch_splitk<dg::kF16>(pr, splits, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int gemm_f16_tn_splitk_noalloc(const void *A, const void *B, void *C, int64_t M, int64_t N,
+                               int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int64_t splits,
+                               void *stream) {
+  // The size rule first, on the host: at most kScratchBytes of partials.
+  if (M < 0 || N < 0 || splits < 1 || splits > dg::kSplitMax) return DG_ERR_INVALID_ARGUMENT;
+  const uint64_t need = (uint64_t)splits * (uint64_t)N * (uint64_t)dg::splitk_ldw(M) * 4u;
+  if (need > (uint64_t)dg::kScratchBytes) return DG_ERR_UNSUPPORTED;
+  dg::Problem pr{A, B, C, 1, M, N, K, lda, ldb, ldc, 0, 0, 0, 1.0f};
+  // Argument errors are reported before the device array is looked up.
+  const int chk = dg::check_tn(pr, 2);
+  if (chk < 0) return DG_OK;
+  if (chk != DG_OK) return chk;
+  void *ws = dg::scratch_ptr();
+  if (ws == nullptr) return DG_ERR_HIP;
+  return dg::launch_splitk<dg::kF16>(pr, splits, ws, dg::kScratchBytes, (hipStream_t)stream);
 }
 
 int gemm_f8_tn_splitk(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,

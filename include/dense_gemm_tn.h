@@ -327,6 +327,25 @@ int gemm_f8_tn_splitk(const void *A, const void *B, void *C,
 int gemm_clock_record(void *buf, int64_t records);
 int64_t gemm_clock_records_used(void);
 
+/*
+ * gemm_f16_tn_splitk without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the fp32 partials live in a static
+ * 32 MiB device array of the library (one per device, held until the process
+ * ends), so the call itself allocates nothing.  Same product, validation and
+ * result as gemm_f16_tn_splitk with the same `splits` (bit for bit), plus:
+ *   DG_ERR_UNSUPPORTED  splits * N * (M rounded up to 4) * 4 bytes > 32 MiB
+ *                       (gemm_splitk_workspace_bytes(M, N, splits) > 2^25);
+ *   DG_ERR_HIP          the array's device address could not be looked up.
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (e.g. on two streams without ordering) race; calls
+ * ordered on one stream do not.
+ */
+int gemm_f16_tn_splitk_noalloc(const void *A, const void *B, void *C,
+                               int64_t M, int64_t N, int64_t K,
+                               int64_t lda, int64_t ldb, int64_t ldc,
+                               int64_t splits, void *stream);
+
 /* Workspace bytes the split-K calls need for M x N and `splits`:
  * splits * N * (M rounded up to 4) * 4; -1 for invalid arguments. */
 int64_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);

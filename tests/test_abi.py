@@ -452,3 +452,34 @@ def test_clock_record_validation():
     assert L.gemm_clock_record(A_ADDR, -1) == dg.DG_ERR_INVALID_ARGUMENT
     assert L.gemm_clock_record(A_ADDR + 4, 8) == dg.DG_ERR_UNSUPPORTED
     assert L.gemm_clock_record(None, 0) == dg.DG_OK
+
+
+def test_noalloc_splitk_host_rules():
+    L = dg.lib()
+    f = L.gemm_f16_tn_splitk_noalloc
+    # Beyond the 32 MiB array: rejected on the host, before any device call.
+    assert f(A_ADDR, B_ADDR, C_ADDR, 1024, 1024, 16384, 16384, 16384, 1024, 9, None) == \
+        dg.DG_ERR_UNSUPPORTED
+    assert f(A_ADDR, B_ADDR, C_ADDR, 4096, 4096, 8192, 8192, 8192, 4096, 64, None) == \
+        dg.DG_ERR_UNSUPPORTED
+    assert f(A_ADDR, B_ADDR, C_ADDR, 128, 128, 8192, 8192, 8192, 128, 0, None) == \
+        dg.DG_ERR_INVALID_ARGUMENT
+    assert f(A_ADDR, B_ADDR, C_ADDR, 128, 128, 8192, 8192, 8192, 128, 65, None) == \
+        dg.DG_ERR_INVALID_ARGUMENT
+    # The gemm_f16_tn rules still apply (K % 8, null A), and M = 0 is a no-op.
+    assert f(A_ADDR, B_ADDR, C_ADDR, 128, 128, 8188, 8192, 8192, 128, 4, None) == \
+        dg.DG_ERR_UNSUPPORTED
+    assert f(None, B_ADDR, C_ADDR, 128, 128, 8192, 8192, 8192, 128, 4, None) == \
+        dg.DG_ERR_INVALID_ARGUMENT
+    assert f(None, None, None, 0, 128, 8192, 8192, 8192, 128, 4, None) == dg.DG_OK
+
+
+def test_library_source_allocates_nothing():
+    """No entry point allocates device memory: the library's sources name no
+    allocation call (comments aside)."""
+    for name in ("gemm_tn.hip", "attention.hip"):
+        text = open(os.path.join(ROOT, "dense_gemm_tn_amd", "csrc", name)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        code = "\n".join(re.sub(r"//.*$", "", ln) for ln in text.splitlines())
+        for call in ("hipMalloc", "hipFree", "hipHostMalloc", "hipMallocAsync", "hipExtMalloc"):
+            assert call not in code, (name, call)
