@@ -15,16 +15,19 @@ normally distributed data, rotating buffers).  Per workload:
      the average kernel duration (`ms_per_step`), from which
      throughput = 2*M*N*K per step / time (section 11.1 of the hello-gpu
      chapter counts a multiply-add as two flops);
-  3. a second pass of K launches with an event pair around each gives the
-     per-launch median / min / max (the hello-gpu chapter, section 11.5, reports
-     medians with their range);
+  3. a second pass of the same K launches, back to back, writes per-block
+     clock records (gemm_clock_record): each launch's span from its first
+     block's start to its last block's end gives the per-launch median / min /
+     max (the hello-gpu chapter, section 11.5, reports medians with their
+     range); a third pass brackets each launch with its own event pair
+     (isolated launches, reported beside it);
   4. set 0 is launched again and its output must equal, bit for bit, the one
      checked in step 1 (parity after timing);
-  5. the launches of step 3 also write per-block clock records (the kernels'
-     shader-clock and 100 MHz counters at each block's start and end, and the
-     XCD it ran on): the clock the kernel actually ran at, overall and per
-     XCD, which explains run-to-run and box-to-box spread of a power-limited
-     part.
+  5. the clock records of step 3 (the kernels' shader-clock and 100 MHz
+     counters at each block's start, K-loop start and end, and end, and the XCD
+     it ran on) give the clock the kernel actually ran at, overall and per XCD,
+     and the split of a block's time into prologue, K loop and epilogue, which
+     explains run-to-run and box-to-box spread of a power-limited part.
 Before the warm-up steps, each workload runs back to back for --settle-ms
 (0.25 s) so timing starts at the clock the load sustains rather than on the
 ramp up from idle.
@@ -244,6 +247,27 @@ def clock_summary(rec) -> dict | None:
     return out
 
 
+def launch_spans_us(rec, blocks: int) -> dict | None:
+    """Per-launch durations from clock records taken in launch order: for each
+    launch, the first block's start to the last block's end on the 100 MHz
+    counter (microseconds) -> median, min, max and count."""
+    import numpy as np
+
+    rec = np.asarray(rec, dtype=np.uint64).reshape(-1, CLOCK_WORDS)
+    n = rec.shape[0] // blocks if blocks > 0 else 0
+    spans = []
+    for j in range(n):
+        r = rec[j * blocks:(j + 1) * blocks]
+        ok = (r[:, 7] > r[:, 1]) & (r[:, 1] > 0)
+        if ok.all():
+            spans.append(float(r[:, 7].max() - r[:, 1].min()) / 100.0)
+    if not spans:
+        return None
+    spans.sort()
+    return {"median": float(np.median(spans)), "min": spans[0], "max": spans[-1],
+            "launches": len(spans)}
+
+
 def sample_check(w, x, out):
     """The GPU output of set 0 against the oracle on sampled entries: corners,
     tile edges and seeded random entries (attention: sampled query rows of the
@@ -336,8 +360,10 @@ def time_workload(w, steps, warmup, dev, check=True, settle_s=0.25):
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # Second pass: an event pair around every launch, and the per-block clock
-    # records of these launches (one launch first, to learn its block count).
+    # Second pass: the same K launches back to back with per-block clock
+    # records (one launch first, to learn its block count).  Each launch's
+    # span, first block start to last block end on the 100 MHz counter, gives
+    # the per-launch distribution without host-side gaps between launches.
     probe = torch.zeros(CLOCK_WORDS, dtype=torch.int64, device=dev)
     dg.clock_record(probe, 1)
     launch(0)
@@ -346,6 +372,26 @@ def time_workload(w, steps, warmup, dev, check=True, settle_s=0.25):
     n_rec = min(steps, max(1, (256 << 20) // (8 * CLOCK_WORDS * blocks)))
     recs = torch.zeros((n_rec * blocks, CLOCK_WORDS), dtype=torch.int64, device=dev)
     dg.clock_record(recs, n_rec * blocks)
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record()
+    for i in range(steps):
+        launch(i)
+    r1.record()
+    torch.cuda.synchronize()
+    dg.clock_record(None, 0)
+    rec_np = recs.cpu().numpy().view("uint64")
+    clock = clock_summary(rec_np)
+    spans = launch_spans_us(rec_np, blocks)
+    if clock is not None:
+        clock["launches_recorded"] = n_rec
+        clock["ms_per_step_recorded_pass"] = r0.elapsed_time(r1) / steps
+    del recs, probe
+    # Third pass: each launch bracketed by its own event pair.  The event
+    # packets leave the GPU idle for some microseconds between launches, and
+    # launches that start from idle run measurably slower than back-to-back
+    # ones, so this distribution is reported beside the others, not as the
+    # per-launch figure.
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
     for i, (e0, e1) in enumerate(evs):
@@ -353,11 +399,6 @@ def time_workload(w, steps, warmup, dev, check=True, settle_s=0.25):
         launch(i)
         e1.record()
     torch.cuda.synchronize()
-    dg.clock_record(None, 0)
-    clock = clock_summary(recs.cpu().numpy().view("uint64"))
-    if clock is not None:
-        clock["launches_recorded"] = n_rec
-    del recs, probe
     per = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in evs)   # microseconds
     # Parity after timing: set 0 again, bit for bit the output checked before.
     launch(0)
@@ -373,8 +414,9 @@ def time_workload(w, steps, warmup, dev, check=True, settle_s=0.25):
         "settle_launches": n_settle,
         "ms_per_step": ev_ms / steps,
         "wall_ms_per_step": wall * 1e3 / steps,
-        "per_launch_us": {"median": st.median(per), "min": per[0], "max": per[-1],
-                          "launches": len(per)},
+        "per_launch_us": spans,
+        "per_launch_us_isolated": {"median": st.median(per), "min": per[0], "max": per[-1],
+                                   "launches": len(per)},
         "tflops": tflops,
         "frac_of_peak": tflops / PEAK_TFLOPS[w.kind],
         "hbm_gbs_algorithmic": algorithmic_bytes(w) / kernel_s / 1e9,

@@ -101,3 +101,17 @@ def test_clock_summary_from_records():
     assert c["prologue_us_median"] == 0.1 and c["loop_us_median"] == 0.8
     assert c["epilogue_us_median"] == 0.1 and c["loop_sclk_mhz"] == 2250.0
     assert bench.clock_summary(np.zeros((3, 10), np.uint64)) is None
+
+
+def test_launch_spans_from_records():
+    import numpy as np
+    rec = np.zeros((4, 10), np.uint64)
+    # launch 0: blocks from 100..300 and 120..350 ticks -> 2.5 us; launch 1: 1000..1400 -> 4 us
+    rec[0, [1, 7]] = [100, 300]
+    rec[1, [1, 7]] = [120, 350]
+    rec[2, [1, 7]] = [1000, 1300]
+    rec[3, [1, 7]] = [1100, 1400]
+    s = bench.launch_spans_us(rec, 2)
+    assert s == {"median": 3.25, "min": 2.5, "max": 4.0, "launches": 2}
+    rec[3, 7] = 0                                  # an unfinished record drops its launch
+    assert bench.launch_spans_us(rec, 2)["launches"] == 1
