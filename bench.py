@@ -80,12 +80,25 @@ def kernel_name(w):
         return "gemm_tn_kernel<%d, 8, %s, %s>" % (kind, amn, bmn)
     if w.extra.get("splitk") and dg.splitk_choose(w.M, w.N, w.K, fp8=(w.kind == "f8")) > 1:
         return "gemm_tn_mid_kernel<%d, false, false, true>" % kind
-    cfg = dg.tn_config(w.M, w.N, w.K, w.batch, fp8=(w.kind == "f8"))
-    return {0: "gemm_tn_kernel<%d, 8, false, false>" % kind,
-            1: "gemm_tn_kernel<%d, 7, false, false>" % kind,
-            2: "gemm_tn_mid_kernel<%d, false, false>" % kind,
-            3: "gemm_tn_skinny_kernel<%d>" % kind,
-            4: "gemm_tn_pp_kernel<%d>" % kind}[cfg]
+    names = {0: "gemm_tn_kernel<%d, 8, false, false>" % kind,
+             1: "gemm_tn_kernel<%d, 7, false, false>" % kind,
+             2: "gemm_tn_mid_kernel<%d, false, false>" % kind,
+             3: "gemm_tn_skinny_kernel<%d>" % kind,
+             4: "gemm_tn_pp_kernel<%d>" % kind}
+    fp8 = w.kind == "f8"
+    ws = dg.tn_workspace_bytes(w.M, w.N, w.K, fp8=fp8) if w.extra.get("ws") else 0
+    plan = dg.tn_plan(w.M, w.N, w.K, w.batch, ws, fp8=fp8)
+    if plan["dp_cols"] > 0 or plan["splits"] > 1:
+        # Two launches per call (whole rounds of columns, then the rest, or
+        # split-K and its reduction): the label names both.
+        split = "gemm_tn_mid_kernel<%d, false, false, true>" % kind
+        if plan["dp_cols"] == 0:
+            return split
+        nt = w.N - plan["dp_cols"]
+        tail = split if plan["splits"] > 1 else \
+            names[dg.tn_config(w.M, nt, w.K, w.batch, fp8=fp8)]
+        return "%s + %s" % (names[plan["dp_config"]], tail)
+    return names[dg.tn_config(w.M, w.N, w.K, w.batch, fp8=fp8)]
 
 
 # The five configurations of the hot path first (the headline FP16 4096^3, FP8
@@ -170,6 +183,10 @@ def make_launcher(w, dev):
 
     scale = 1.0 / w.K ** 0.5
     splits, ws, ws_bytes = 1, None, 0
+    if w.extra.get("ws"):
+        # The planned call with the workspace its plan asks for.
+        ws_bytes = dg.tn_workspace_bytes(w.M, w.N, w.K, fp8=(w.kind == "f8"))
+        ws = torch.empty(max(ws_bytes, 16) // 4, dtype=torch.float32, device=dev)
     if w.extra.get("splitk"):
         # One workspace serves every set: the launches are ordered on one stream.
         splits = dg.splitk_choose(w.M, w.N, w.K, fp8=(w.kind == "f8"))
@@ -186,6 +203,8 @@ def make_launcher(w, dev):
         if w.kind == "f16" and layout != "TN":
             dg.gemm_f16(layout[0], layout[1], a, b, c, w.M, w.N, w.K, a.stride(0), b.stride(0),
                         w.M)
+        elif w.kind == "f16" and w.extra.get("ws"):
+            dg.gemm_f16_tn_ws(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M, ws, ws_bytes)
         elif w.kind == "f16" and splits > 1:
             dg.gemm_f16_tn_splitk(a, b, c, w.M, w.N, w.K, w.K, w.K, w.M, splits, ws, ws_bytes)
         elif w.kind == "f16":

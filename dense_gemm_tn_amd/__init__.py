@@ -43,6 +43,10 @@ EXPORTS = (
     "gemm_clock_record",
     "gemm_clock_records_used",
     "gemm_f16_tn_splitk_noalloc",
+    "gemm_f16_tn_ws",
+    "gemm_f8_tn_ws",
+    "gemm_tn_workspace_bytes",
+    "gemm_tn_plan",
 )
 
 _lib = None
@@ -91,9 +95,15 @@ def lib() -> ctypes.CDLL:
         L.gemm_clock_records_used.restype = i64
         L.gemm_f16_tn_splitk_noalloc.argtypes = [vp, vp, vp] + [i64] * 7 + [vp]
         L.gemm_f16_tn_splitk_noalloc.restype = ctypes.c_int
+        L.gemm_f16_tn_ws.argtypes = [vp, vp, vp] + [i64] * 6 + [vp, i64, vp]
+        L.gemm_f8_tn_ws.argtypes = [vp, vp, vp] + [i64] * 6 + [f32, f32, vp, i64, vp]
+        L.gemm_tn_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64]
+        L.gemm_tn_workspace_bytes.restype = i64
+        L.gemm_tn_plan.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, vp]
         for f in (L.gemm_f16_tn, L.gemm_f16, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
                   L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config, L.gemm_f16_config,
-                  L.gemm_f8, L.gemm_f8_config, L.gemm_f16_tn_splitk, L.gemm_f8_tn_splitk):
+                  L.gemm_f8, L.gemm_f8_config, L.gemm_f16_tn_splitk, L.gemm_f8_tn_splitk,
+                  L.gemm_f16_tn_ws, L.gemm_f8_tn_ws, L.gemm_tn_plan):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -191,6 +201,40 @@ def gemm_f16_tn_splitk(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc:
     _check("gemm_f16_tn_splitk",
            lib().gemm_f16_tn_splitk(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc, splits,
                                     _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def gemm_f16_tn_ws(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int, workspace,
+                   workspace_bytes: int, stream=None) -> None:
+    """gemm_f16_tn by the library's plan within `workspace_bytes` of `workspace` (None, 0: none)."""
+    _check("gemm_f16_tn_ws",
+           lib().gemm_f16_tn_ws(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc,
+                                _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def gemm_f8_tn_ws(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
+                  scale_a: float, scale_b: float, workspace, workspace_bytes: int,
+                  stream=None) -> None:
+    """gemm_f8_tn by the library's plan within `workspace_bytes` of `workspace`."""
+    _check("gemm_f8_tn_ws",
+           lib().gemm_f8_tn_ws(_ptr(A), _ptr(B), _ptr(C), M, N, K, lda, ldb, ldc, scale_a,
+                               scale_b, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def tn_workspace_bytes(M: int, N: int, K: int, fp8: bool = False) -> int:
+    """Workspace bytes the best plan for an M x N x K TN product uses (0: none)."""
+    return int(lib().gemm_tn_workspace_bytes(1 if fp8 else 0, M, N, K))
+
+
+def tn_plan(M: int, N: int, K: int, batch: int = 1, workspace_bytes: int = 0,
+            fp8: bool = False) -> dict:
+    """The library's plan: single-launch configuration, columns run in whole
+    rounds first (dp_cols, 0: none) and their configuration, K ranges of the
+    rest (splits) and workspace bytes used."""
+    out = (ctypes.c_int64 * 5)()
+    _check("gemm_tn_plan", lib().gemm_tn_plan(1 if fp8 else 0, M, N, K, batch, workspace_bytes,
+                                              ctypes.addressof(out)))
+    return {"config": out[0], "dp_cols": out[1], "dp_config": out[2], "splits": out[3],
+            "workspace_bytes": out[4]}
 
 
 def gemm_f16_tn_splitk_noalloc(A, B, C, M: int, N: int, K: int, lda: int, ldb: int, ldc: int,
@@ -311,11 +355,13 @@ def _empty_on(stream, shape, dtype, device):
 def matmul_tn_f16(a, b, out=None, stream=None, splits=1):
     """a: [M, K] fp16 (row-major A), b: [N, K] fp16 (column-major B) -> C as [N, M] fp16.
 
-    splits > 1, or "auto" (the library's suggestion), runs the split-K call with
-    a workspace allocated on the launch stream (so the caching allocator hands
-    it out only after earlier work on that stream).  A new `out` is allocated
-    on the launch stream too; a caller's `out` must be [N, M] fp16 with
-    contiguous rows."""
+    splits > 1 runs the split-K call with that many K ranges; "auto" runs the
+    library's plan with the workspace it asks for (gemm_f16_tn_ws: split-K,
+    a split tail of a ragged last round, or a single launch).  Workspaces are
+    allocated on the launch stream (so the caching allocator hands them out
+    only after earlier work on that stream).  A new `out` is allocated on the
+    launch stream too; a caller's `out` must be [N, M] fp16 with contiguous
+    rows."""
     import torch
 
     if a.dim() != 2 or b.dim() != 2:
@@ -334,7 +380,11 @@ def matmul_tn_f16(a, b, out=None, stream=None, splits=1):
     if out is None:
         out = _empty_on(stream, (N, M), torch.float16, a.device)
     if splits == "auto":
-        splits = splitk_choose(M, N, K)
+        nbytes = tn_workspace_bytes(M, N, K)
+        ws = _empty_on(stream, (max(nbytes, 16) // 4,), torch.float32, a.device) if nbytes else None
+        gemm_f16_tn_ws(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), ws, nbytes,
+                       stream)
+        return out
     if splits == 1:
         gemm_f16_tn(a, b, out, M, N, K, a.stride(0), b.stride(0), out.stride(0), stream)
         return out

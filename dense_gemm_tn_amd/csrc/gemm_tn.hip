@@ -1851,15 +1851,11 @@ static int check_tn(const Problem &pr, int es) {
   return DG_OK;
 }
 
+// One launch of a validated TN problem in configuration `cfg`.
 template <int KIND>
-static int launch(const Problem &pr, hipStream_t stream) {
+static int launch_cfg(const Problem &pr, Config cfg, hipStream_t stream) {
   typedef Traits<KIND> T;
   const int es = T::es;
-  const int chk = check_tn(pr, es);
-  if (chk < 0) return DG_OK;
-  if (chk != DG_OK) return chk;
-
-  const Config cfg = choose_config(es, pr.M, pr.N, pr.K, pr.batch);
   const bool skinny = cfg.kind == kCfgSkinny, mid = cfg.kind == kCfgMid;
   const bool pp = cfg.kind == kCfgPingPong;
   const int ntn = cfg.kind == kCfg224 ? 7 : 8;
@@ -1915,6 +1911,10 @@ static int launch(const Problem &pr, hipStream_t stream) {
                        dim3(kThreads), 0, stream, p);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
+
+// The planned TN launch (defined with the planner below).
+template <int KIND>
+static int launch(const Problem &pr, hipStream_t stream);
 
 // Products in any of the four op-code layouts (fp16 in and out, or fp8 E4M3FN
 // in and bf16 out with per-tensor scales).  TN goes through launch<> and its
@@ -2114,6 +2114,160 @@ static int64_t choose_splits(int es, int64_t M, int64_t N, int64_t K) {
   return s < 1 ? 1 : s;
 }
 
+// ---------------------------------------------------------------------------
+// Plans for grids with a ragged last round.  With one block per CU, a grid of
+// T tiles of the 256-row kernel takes ceil(T / CUs) rounds however few tiles
+// the last one holds (4096 x 4608 in 256 x 256 tiles: 288 tiles, a second
+// round of 32), and the selector's fallback, the 128 x 128 kernel, pays its
+// own per-element cost on the whole product.  A plan may instead run the
+// first dp_cols columns of C as whole rounds of the 256-row kernel and the
+// remaining columns as a second launch: the selector's configuration for that
+// narrower product or, given a caller workspace, the split-K kernels with the
+// tail's K range cut into `splits` ranges, so the few tail tiles spread over
+// every CU (the data-parallel + split-tail hybrid that stream-K scheduling
+// generalises; here the split points are K-step boundaries).  A plan that
+// splits nothing computes every element exactly as the single launch does
+// (same products, same K order).  Plans are compared with a time model fitted
+// to MI355X measurements, and a split is taken only when it models at least
+// kPlanGain faster than the single launch.
+//
+// Time model, microseconds:
+//   * 256-row kernel: a round of one block per CU takes nk K-steps of
+//     kStepUs (x kNarrow for 256 x 224 tiles) plus kRoundUs of prologue and
+//     epilogue;
+//   * 128 x 128 kernel: kMidRel of that K-step per block-step, counted per CU
+//     in blocks -- two co-resident blocks take two units, a lone block
+//     kMidLone (no second block hides its waits);
+//   * split-K: its partial products plus the fp32 partials written and read
+//     back (and C written) at kHbmBytesPerUs;
+//   * kLaunchUs per launch.
+struct TnPlan {
+  int whole;         // configuration of the single launch (dp_cols == 0, splits == 1)
+  int64_t dp_cols;   // columns of C run in whole rounds first (0: no column split)
+  int dp_cfg;        // kCfg256 or kCfg224 for those columns
+  int64_t splits;    // K ranges of the tail (of the whole product when dp_cols == 0)
+  int64_t ws_bytes;  // workspace bytes the plan uses
+  double us;         // modelled time
+};
+constexpr double kStepUsF16 = 1.5, kStepUsF8 = 1.25;
+constexpr double kNarrow = 0.8;
+constexpr double kRoundUs = 7.0;
+constexpr double kMidRel = kMidCost / 64.0 / 4.0;
+constexpr double kMidLone = 1.35;
+constexpr double kHbmBytesPerUs = 5.0e6;
+constexpr double kLaunchUs = 2.0;
+constexpr double kPlanGain = 0.05;
+
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static double step_us(int es) { return es == 1 ? kStepUsF8 : kStepUsF16; }
+static double mid_units(int64_t blocks, int64_t cus) {
+  return blocks <= cus ? kMidLone : (double)cdiv(blocks, cus);
+}
+static double model_big(int es, int64_t tiles, int ntn, int64_t nk, int64_t cus) {
+  return cdiv(tiles, cus) * (nk * step_us(es) * (ntn == 8 ? 1.0 : kNarrow) + kRoundUs) +
+         kLaunchUs;
+}
+static double model_splitk(int es, int64_t M, int64_t N, int64_t nk, int64_t S, int64_t cus) {
+  const int64_t tiles = cdiv(M, kMidTile) * cdiv(N, kMidTile);
+  const double bytes = (double)M * (double)N * (8.0 * S + 2.0);
+  return mid_units(tiles * S, cus) * cdiv(nk, S) * step_us(es) * kMidRel +
+         bytes / kHbmBytesPerUs + 2 * kLaunchUs;
+}
+static double model_cfg(int es, int kind, int64_t M, int64_t N, int64_t nk, int64_t batch,
+                        int64_t cus) {
+  if (kind == kCfgMid)
+    return mid_units(cdiv(M, kMidTile) * cdiv(N, kMidTile) * batch, cus) * nk * step_us(es) *
+               kMidRel + kLaunchUs;
+  const int ntn = kind == kCfg224 ? 7 : 8;
+  return model_big(es, cdiv(M, kTile) * cdiv(N, 32 * ntn) * batch, ntn, nk, cus);
+}
+
+// The plan for a TN problem given `ws_avail` bytes of workspace (0: none).
+static TnPlan plan_tn(int es, int64_t M, int64_t N, int64_t K, int64_t batch, int64_t ws_avail) {
+  const int whole = choose_config(es, M, N, K, batch).kind;
+  TnPlan best{whole, 0, kCfg256, 1, 0, 0.0};
+  // Forced tiles, skinny-K problems and empty ones run as one launch.
+  if (getenv("DG_GEMM_TILE") || whole == kCfgSkinny || M <= 0 || N <= 0 || K <= 0 || batch <= 0)
+    return best;
+  const int64_t cus = cu_count();
+  const int64_t nk = cdiv(K, 128 / es);
+  best.us = model_cfg(es, whole, M, N, nk, batch, cus);
+  const double bar = best.us * (1.0 - kPlanGain);
+  auto consider = [&](const TnPlan &c) {
+    if (c.us < bar && c.us < best.us) best = c;
+  };
+  const int64_t ldw = splitk_ldw(M);
+  // Split-K of the whole product (few tiles, long K).
+  if (batch == 1) {
+    const int64_t s = choose_splits(es, M, N, K);
+    const int64_t need = s * N * ldw * 4;
+    if (s > 1 && need <= ws_avail)
+      consider(TnPlan{whole, 0, kCfg256, s, need, model_splitk(es, M, N, nk, s, cus)});
+  }
+  // Whole rounds of 256 x 256 or 256 x 224 tiles, then the remaining columns.
+  const int64_t tm = cdiv(M, kTile) * batch;  // tiles per tile column, all heads
+  for (const int ntn : {8, 7}) {
+    const int64_t w = 32 * ntn;
+    const int64_t rounds = cdiv(tm * cdiv(N, w), cus);
+    if (rounds < 2) continue;
+    const int64_t kcols = (rounds - 1) * cus / tm;
+    const int64_t dp = kcols * w;
+    if (kcols < 1 || dp >= N) continue;
+    const int64_t nt = N - dp;
+    const int dp_cfg = ntn == 8 ? kCfg256 : kCfg224;
+    const double t_dp = model_big(es, tm * kcols, ntn, nk, cus);
+    const int tail = choose_config(es, M, nt, K, batch).kind;
+    consider(TnPlan{whole, dp, dp_cfg, 1, 0, t_dp + model_cfg(es, tail, M, nt, nk, batch, cus)});
+    if (batch != 1) continue;
+    for (const int64_t S : {2, 4, 8}) {
+      const int64_t need = S * nt * ldw * 4;
+      if (S > nk || need > ws_avail) continue;
+      consider(TnPlan{whole, dp, dp_cfg, S, need, t_dp + model_splitk(es, M, nt, nk, S, cus)});
+    }
+  }
+  return best;
+}
+
+// A TN problem by its plan: one launch, split-K, or whole rounds of columns
+// followed by the rest (as one launch or split-K).  `ws` may be null (no
+// workspace: plans that need none).
+template <int KIND>
+static int launch_ws(const Problem &pr, void *ws, int64_t ws_bytes, hipStream_t stream) {
+  const int es = Traits<KIND>::es;
+  if (ws_bytes < 0 || (ws == nullptr && ws_bytes != 0)) return DG_ERR_INVALID_ARGUMENT;
+  const int chk = check_tn(pr, es);
+  if (chk < 0) return DG_OK;
+  if (chk != DG_OK) return chk;
+  if (ws != nullptr) {
+    const uint64_t a_all = span_bytes(pr.M, pr.K, pr.lda, es) + (uint64_t)(pr.batch - 1) * pr.stride_a * es;
+    const uint64_t b_all = span_bytes(pr.N, pr.K, pr.ldb, es) + (uint64_t)(pr.batch - 1) * pr.stride_b * es;
+    const uint64_t c_all = span_bytes(pr.N, pr.M, pr.ldc, 2) + (uint64_t)(pr.batch - 1) * pr.stride_c * 2;
+    if (overlaps(ws, (uint64_t)ws_bytes, pr.A, a_all) || overlaps(ws, (uint64_t)ws_bytes, pr.B, b_all) ||
+        overlaps(ws, (uint64_t)ws_bytes, pr.C, c_all))
+      return DG_ERR_INVALID_ARGUMENT;
+    if (!aligned16(ws)) return DG_ERR_UNSUPPORTED;
+  }
+  const TnPlan plan = plan_tn(es, pr.M, pr.N, pr.K, pr.batch, ws != nullptr ? ws_bytes : 0);
+  if (plan.dp_cols == 0) {
+    if (plan.splits > 1) return launch_splitk<KIND>(pr, plan.splits, ws, ws_bytes, stream);
+    return launch_cfg<KIND>(pr, Config{plan.whole}, stream);
+  }
+  Problem dp = pr, tail = pr;
+  dp.N = plan.dp_cols;
+  tail.N = pr.N - plan.dp_cols;
+  tail.B = (const uint8_t *)pr.B + plan.dp_cols * pr.ldb * es;
+  tail.C = (uint8_t *)pr.C + plan.dp_cols * pr.ldc * 2;
+  const int st = launch_cfg<KIND>(dp, Config{plan.dp_cfg}, stream);
+  if (st != DG_OK) return st;
+  if (plan.splits > 1) return launch_splitk<KIND>(tail, plan.splits, ws, ws_bytes, stream);
+  return launch_cfg<KIND>(tail, choose_config(es, tail.M, tail.N, tail.K, tail.batch), stream);
+}
+
+template <int KIND>
+static int launch(const Problem &pr, hipStream_t stream) {
+  return launch_ws<KIND>(pr, nullptr, 0, stream);
+}
+
 }  // namespace dg
 
 extern "C" {
@@ -2251,6 +2405,38 @@ int gemm_f8_tn_splitk(const void *A, const void *B, void *C, int64_t M, int64_t 
   const float s = scale_a * scale_b;
   dg::Problem pr{A, B, C, 1, M, N, K, lda, ldb, ldc, 0, 0, 0, s};
   return dg::launch_splitk<dg::kF8>(pr, splits, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int gemm_f16_tn_ws(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldb, int64_t ldc, void *workspace,
+                   int64_t workspace_bytes, void *stream) {
+  dg::Problem pr{A, B, C, 1, M, N, K, lda, ldb, ldc, 0, 0, 0, 1.0f};
+  return dg::launch_ws<dg::kF16>(pr, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int gemm_f8_tn_ws(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K,
+                  int64_t lda, int64_t ldb, int64_t ldc, float scale_a, float scale_b,
+                  void *workspace, int64_t workspace_bytes, void *stream) {
+  dg::Problem pr{A, B, C, 1, M, N, K, lda, ldb, ldc, 0, 0, 0, scale_a * scale_b};
+  return dg::launch_ws<dg::kF8>(pr, workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int64_t gemm_tn_workspace_bytes(int fp8, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return -1;
+  return dg::plan_tn(fp8 ? 1 : 2, M, N, K, 1, INT64_MAX).ws_bytes;
+}
+
+int gemm_tn_plan(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch,
+                 int64_t workspace_bytes, int64_t *out) {
+  if (!out || M < 0 || N < 0 || K < 0 || batch < 0 || workspace_bytes < 0)
+    return DG_ERR_INVALID_ARGUMENT;
+  const dg::TnPlan p = dg::plan_tn(fp8 ? 1 : 2, M, N, K, batch, workspace_bytes);
+  out[0] = p.whole;
+  out[1] = p.dp_cols;
+  out[2] = p.dp_cols > 0 ? p.dp_cfg : -1;
+  out[3] = p.splits;
+  out[4] = p.ws_bytes;
+  return DG_OK;
 }
 
 }  // extern "C"

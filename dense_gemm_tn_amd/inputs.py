@@ -82,6 +82,20 @@ WORKLOADS = {
                  extra={"tile": "pingpong"}),
         Workload("f8_8192_pingpong", "f8", 8192, 8192, 8192, "normal", seed=0,
                  extra={"tile": "pingpong"}),
+        # A ragged last round (288 tiles of 256 x 256 on 256 CUs): the library's
+        # plan (whole rounds of columns, then the rest), the same product as a
+        # single launch of the selector's configuration, and a plan whose tail
+        # is split along K through a workspace.
+        Workload("f16_4096x4608x4096", "f16", 4096, 4608, 4096, "normal", seed=0),
+        Workload("f16_4096x4608x4096_single", "f16", 4096, 4608, 4096, "normal", seed=0,
+                 extra={"tile": "128"}),
+        Workload("f8_4096x4608x4096", "f8", 4096, 4608, 4096, "normal", seed=0),
+        Workload("f8_4096x4608x4096_single", "f8", 4096, 4608, 4096, "normal", seed=0,
+                 extra={"tile": "128"}),
+        Workload("f16_4096x4352x4096_ws", "f16", 4096, 4352, 4096, "normal", seed=0,
+                 extra={"ws": True}),
+        Workload("f16_4096x4352x4096_single", "f16", 4096, 4352, 4096, "normal", seed=0,
+                 extra={"tile": "128"}),
         Workload("qkt_64x4096x4096x128", "qkt", 4096, 4096, 128, "normal", seed=0, batch=64,
                  std=1.0 / math.sqrt(128.0)),
         Workload("attn_64x4096x4096x128", "attn", 4096, 4096, 128, "normal", seed=0, batch=64),

@@ -23,8 +23,10 @@
  *   All matrix pointers are DEVICE pointers on the current HIP device; the
  *   caller allocates and owns them.  `stream` is a hipStream_t (NULL = the
  *   default stream).  Each call validates its arguments on the host, enqueues
- *   exactly one kernel on `stream` and returns without synchronising; results
- *   are visible after the caller synchronises with the stream.  The library
+ *   its kernels on `stream` -- one, or two when the plan of gemm_tn_plan runs
+ *   the columns of C in two parts (split-K calls add a reduction kernel) --
+ *   and returns without synchronising; results are visible after the caller
+ *   synchronises with the stream.  The library
  *   allocates nothing, keeps no per-call state and is safe to call from
  *   several host threads.  C must not overlap A or B.
  *
@@ -228,9 +230,10 @@ int gemm_tile_order(int64_t tiles_m, int64_t tiles_n, int64_t batch, int64_t *ou
 int gemm_block_tile(void);
 
 /*
- * The kernel configuration the GEMM entry points choose for a problem of the
- * given sizes on the current HIP device (fp8 != 0: one-byte elements, else
- * fp16).  One tile shape does not suit every size, so the library has a small
+ * The kernel configuration of a single launch of the GEMM entry points for a
+ * problem of the given sizes on the current HIP device (fp8 != 0: one-byte
+ * elements, else fp16; gemm_tn_plan tells when a TN call splits its columns
+ * over two launches instead).  One tile shape does not suit every size, so the library has a small
  * set and a selector ("FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4",
  * sections "Final results" and "Further tuning"):
  *   0  256 x 256 output tiles, one block per CU, pipelined K loop;
@@ -299,6 +302,61 @@ int gemm_f8_tn_splitk(const void *A, const void *B, void *C,
                       float scale_a, float scale_b,
                       int64_t splits, void *workspace, int64_t workspace_bytes,
                       void *stream);
+
+/*
+ * Plans for grids with a ragged last round.  The 256-row kernel runs one block
+ * per compute unit, so a grid of T tiles takes ceil(T / CUs) rounds however
+ * few tiles the last round holds (4096 x 4608 in 256 x 256 tiles: 288 tiles,
+ * a second round of 32 on 256 CUs).  The TN calls (gemm_f16_tn, gemm_f8_tn,
+ * gemm_batched_qkt for K * es > 256, and the *_ws calls below) then may run the
+ * first dp_cols columns of C as whole rounds of the 256-row kernel and the
+ * remaining columns as a second launch on the same stream, in the
+ * configuration gemm_tn_config gives for that narrower product.  Every
+ * element is then computed exactly as by a single launch (the same products
+ * in the same K order): only the time changes.  With a caller workspace (the
+ * *_ws calls) the remaining columns may instead have their K range cut into
+ * `splits` ranges summed through the workspace (as gemm_f16_tn_splitk), which
+ * spreads the few tail tiles over every compute unit -- the data-parallel
+ * plus split-tail schedule that stream-K generalises -- and a product of few
+ * tiles with a long K may be split-K as a whole; such plans differ from the
+ * single launch by the fp32 summation order only.  Plans are chosen with a
+ * time model fitted to MI355X measurements and taken only when modelled at
+ * least 5 % faster than the single launch; DG_GEMM_TILE (see gemm_tn_config)
+ * turns them off.
+ * Source: "FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", section "Further
+ * tuning" (per-shape configurations and their selection).
+ *
+ * gemm_f16_tn_ws / gemm_f8_tn_ws: gemm_f16_tn / gemm_f8_tn by the plan that
+ *   fits `workspace_bytes` bytes of `workspace` (device memory, 16-byte
+ *   aligned, overlapping none of A, B and C; NULL with 0 bytes allowed: then
+ *   only plans without a workspace).  Ownership, ordering and the C rule are
+ *   those of gemm_f16_tn; the workspace is the caller's, its contents are
+ *   undefined afterwards, and calls that may run concurrently must not share
+ *   it.  Errors: as gemm_f16_tn, plus DG_ERR_INVALID_ARGUMENT for negative
+ *   workspace_bytes, a NULL workspace with nonzero bytes, or a workspace
+ *   overlapping A, B or C, and DG_ERR_UNSUPPORTED for a misaligned one.
+ * gemm_tn_workspace_bytes: bytes of workspace the best plan for an M x N x K
+ *   product uses (0 when it needs none; -1 for negative sizes).
+ * gemm_tn_plan: the plan for the given sizes, head count and workspace bytes:
+ *   out[0] the single launch's configuration (as gemm_tn_config), out[1]
+ *   dp_cols (0: the columns are not split), out[2] the configuration of the
+ *   dp_cols columns (0 or 1; -1 when not split), out[3] the K ranges of the
+ *   remaining columns (of the whole product when out[1] is 0; 1: not split),
+ *   out[4] the workspace bytes used.  DG_ERR_INVALID_ARGUMENT for a NULL out
+ *   or negative arguments.
+ */
+int gemm_f16_tn_ws(const void *A, const void *B, void *C,
+                   int64_t M, int64_t N, int64_t K,
+                   int64_t lda, int64_t ldb, int64_t ldc,
+                   void *workspace, int64_t workspace_bytes, void *stream);
+int gemm_f8_tn_ws(const void *A, const void *B, void *C,
+                  int64_t M, int64_t N, int64_t K,
+                  int64_t lda, int64_t ldb, int64_t ldc,
+                  float scale_a, float scale_b,
+                  void *workspace, int64_t workspace_bytes, void *stream);
+int64_t gemm_tn_workspace_bytes(int fp8, int64_t M, int64_t N, int64_t K);
+int gemm_tn_plan(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch,
+                 int64_t workspace_bytes, int64_t *out);
 
 /*
  * Per-block clock records, a measurement facility (off by default).  After

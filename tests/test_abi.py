@@ -483,3 +483,110 @@ def test_library_source_allocates_nothing():
         code = "\n".join(re.sub(r"//.*$", "", ln) for ln in text.splitlines())
         for call in ("hipMalloc", "hipFree", "hipHostMalloc", "hipMallocAsync", "hipExtMalloc"):
             assert call not in code, (name, call)
+
+
+# ------------------------------------------------- plans (host logic, no launches)
+
+def _no_device():
+    if torch_device_count() > 0:
+        pytest.skip("plan expectations assume the 256-CU default of a device-less host")
+
+
+@pytest.mark.parametrize("M,N,K,batch,fp8", [
+    (4096, 4096, 4096, 1, False),    # one full round
+    (8192, 8192, 8192, 1, True),     # four full rounds
+    (1920, 13900, 4096, 1, False),   # 224-wide tiles: 504 of 512 slots
+    (256, 256, 256, 1, False),
+    (255, 257, 256, 1, False),
+    (4096, 4096, 128, 64, False),    # skinny-K heads
+    (8192, 8192, 8192, 1, False),
+    (6144, 6144, 4096, 1, False),
+    (8192, 8448, 4096, 1, False),
+])
+def test_plan_keeps_single_launch(M, N, K, batch, fp8, monkeypatch):
+    monkeypatch.delenv("DG_GEMM_TILE", raising=False)
+    _no_device()
+    for ws in (0, 1 << 40):
+        p = dg.tn_plan(M, N, K, batch=batch, workspace_bytes=ws, fp8=fp8)
+        assert p == {"config": dg.tn_config(M, N, K, batch, fp8), "dp_cols": 0, "dp_config": -1,
+                     "splits": 1, "workspace_bytes": 0}
+
+
+@pytest.mark.parametrize("M,N,K,batch,fp8", [
+    (4096, 4608, 4096, 1, False),    # 288 tiles of 256 x 256: a second round of 32
+    (4096, 4608, 4096, 1, True),
+    (4096, 4352, 4096, 1, False),
+    (4000, 4352, 4096, 1, True),
+    (2048, 9216, 8192, 1, False),
+    (4096, 4352, 256, 2, False),     # two heads, 256-deep contraction
+])
+def test_plan_splits_ragged_last_round(M, N, K, batch, fp8, monkeypatch):
+    monkeypatch.delenv("DG_GEMM_TILE", raising=False)
+    _no_device()
+    p = dg.tn_plan(M, N, K, batch=batch, fp8=fp8)
+    assert p["config"] == dg.tn_config(M, N, K, batch, fp8)
+    assert p["dp_config"] in (0, 1) and p["splits"] == 1 and p["workspace_bytes"] == 0
+    w = 256 if p["dp_config"] == 0 else 224
+    assert 0 < p["dp_cols"] < N and p["dp_cols"] % w == 0
+    # The first columns fill whole rounds of one block per CU (at most one
+    # round fewer than the single launch of that tile width would take).
+    col_tiles = -(-M // 256) * batch
+    rounds = -(-col_tiles * -(-N // w) // 256)
+    assert col_tiles * (p["dp_cols"] // w) <= 256 * (rounds - 1)
+    assert col_tiles * (p["dp_cols"] // w + 1) > 256 * (rounds - 1)
+    # DG_GEMM_TILE forces one launch.
+    monkeypatch.setenv("DG_GEMM_TILE", "256")
+    assert dg.tn_plan(M, N, K, batch=batch, fp8=fp8)["dp_cols"] == 0
+
+
+def test_plan_workspace_rules(monkeypatch):
+    monkeypatch.delenv("DG_GEMM_TILE", raising=False)
+    _no_device()
+    M, N, K = 4096, 4352, 4096
+    need = dg.tn_workspace_bytes(M, N, K)
+    p = dg.tn_plan(M, N, K, workspace_bytes=need)
+    assert need > 0 and p["workspace_bytes"] == need and p["splits"] > 1 and p["dp_cols"] > 0
+    # The tail's split-K partials: splits x tail columns of padded M.
+    assert need == dg.splitk_workspace_bytes(M, N - p["dp_cols"], p["splits"])
+    q = dg.tn_plan(M, N, K, workspace_bytes=need - 1)
+    assert q["workspace_bytes"] <= need - 1
+    # Few tiles and a long K: split-K of the whole product, the chooser's count.
+    r = dg.tn_plan(512, 512, 32768, workspace_bytes=1 << 30)
+    assert r["dp_cols"] == 0 and r["splits"] == dg.splitk_choose(512, 512, 32768) > 1
+    assert r["workspace_bytes"] == dg.splitk_workspace_bytes(512, 512, r["splits"])
+    assert dg.tn_workspace_bytes(4096, 4096, 4096) == 0
+    assert dg.tn_workspace_bytes(-1, 4, 4) == -1
+    L = dg.lib()
+    assert L.gemm_tn_plan(0, 4, 4, 4, 1, 0, None) == dg.DG_ERR_INVALID_ARGUMENT
+    out = (ctypes.c_int64 * 5)()
+    assert L.gemm_tn_plan(0, 4, 4, 4, 1, -1, ctypes.addressof(out)) == dg.DG_ERR_INVALID_ARGUMENT
+    assert L.gemm_tn_plan(0, 4, -4, 4, 1, 0, ctypes.addressof(out)) == dg.DG_ERR_INVALID_ARGUMENT
+
+
+# 4096 x 4352 x 4096 at the fake addresses (A 32 MiB, B and C 34 MiB each).
+WS = (A_ADDR, B_ADDR, C_ADDR, 4096, 4352, 4096, 4096, 4096, 4096)
+
+
+@pytest.mark.parametrize("tail,status", [
+    ((None, 16), dg.DG_ERR_INVALID_ARGUMENT),                  # no workspace, nonzero bytes
+    ((0x20000000, -1), dg.DG_ERR_INVALID_ARGUMENT),            # negative size
+    ((A_ADDR + 4096, 1 << 20), dg.DG_ERR_INVALID_ARGUMENT),    # overlaps A
+    ((B_ADDR - 4096, 1 << 20), dg.DG_ERR_INVALID_ARGUMENT),    # overlaps B
+    ((C_ADDR + (1 << 20), 1 << 20), dg.DG_ERR_INVALID_ARGUMENT),  # overlaps C
+    ((0x20000008, 1 << 20), dg.DG_ERR_UNSUPPORTED),            # misaligned
+])
+def test_ws_call_validation(tail, status):
+    L = dg.lib()
+    assert L.gemm_f16_tn_ws(*WS, *tail, None) == status
+    assert L.gemm_f8_tn_ws(*WS, 1.0, 1.0, *tail, None) == status
+
+
+def test_ws_call_keeps_tn_rules():
+    L = dg.lib()
+    # K % 8 and a null A fail as for gemm_f16_tn; M = 0 is a no-op.
+    assert L.gemm_f16_tn_ws(A_ADDR, B_ADDR, C_ADDR, 128, 128, 8188, 8192, 8192, 128, None, 0,
+                            None) == dg.DG_ERR_UNSUPPORTED
+    assert L.gemm_f16_tn_ws(None, B_ADDR, C_ADDR, 128, 128, 8192, 8192, 8192, 128, None, 0,
+                            None) == dg.DG_ERR_INVALID_ARGUMENT
+    assert L.gemm_f16_tn_ws(None, None, None, 0, 128, 8192, 8192, 8192, 128, None, 0,
+                            None) == dg.DG_OK
