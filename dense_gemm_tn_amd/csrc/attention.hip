@@ -246,7 +246,9 @@ static_assert(kGroups % kRing == 0 && kAhead < kRing, "fragment ring");
 
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The wave index as a uniform value, so LDS destinations of the copies and
+  // other per-wave addresses are computed in scalar registers.
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15, g = lane >> 4;
 
   // Hardware block b runs on XCD b % 8 as its (b / 8)-th block; XCD x takes the
@@ -304,12 +306,14 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(kd + q * 16 * kKRow), 16,
                                              kbase + koff[q], 0, 0, 0);
   };
-  auto copy_v1 = [&](int kb, int q) {
+  // masked: block kb may be cut by N.  Only whole 8-key chunks are copied; a
+  // chunk that straddles N is filled by finish_v, so nothing past a row's N
+  // keys is ever read.
+  auto copy_v1 = [&](int kb, int q, auto masked) {
     lds_u8 *vd = vslot(kb) + (8 * w) * kVRow;
-    // Only whole 8-key chunks are copied; a chunk that straddles N is filled
-    // by finish_v, so nothing past a row's N keys is ever read.
-    const uint32_t off =
-        (int64_t)kb * kBN + vkey[q] + 8 <= p.N ? voff[q] + (uint32_t)(kb * kVRow) : kOob;
+    uint32_t off = voff[q] + (uint32_t)(kb * kVRow);
+    if constexpr (decltype(masked)::value)
+      if ((int64_t)kb * kBN + vkey[q] + 8 > p.N) off = kOob;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vd + q * 32 * kVRow), 16, off, 0,
                                              0, 0);
   };
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
   };
   auto copy_v = [&](int kb) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) copy_v1(kb, q);
+    for (int q = 0; q < 4; ++q) copy_v1(kb, q, std::true_type{});
   };
   // After this wave's copies have landed: if N cuts an 8-key chunk of Vt
   // block kb, the lane that owns the chunk's LDS slot (its copy read zeros)
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
           if constexpr ((k >> 1) < 4) {
             if (more_k) copy_k1(kb + 2, k >> 1);
           } else {
-            copy_v1(kb + 1, (k >> 1) - 4);
+            copy_v1(kb + 1, (k >> 1) - 4, mask_next);
           }
         }
         // VALU share.
