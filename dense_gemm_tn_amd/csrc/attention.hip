@@ -261,8 +261,6 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
   clock_mark(p.clk, kClockStart);
 
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.Q + head * p.sq_b, p.q_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.K + head * p.sk_b, p.k_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.V + head * p.sv_b, p.v_bytes);
 
   // Q fragments (AGPRs): query tile u, K-step s (32 dims): lane (i, g) holds
   // query q0 + 16u + i, dims 32s + 8g .. +7.
@@ -299,23 +297,30 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
   auto kslot = [&](int kb) { return lds + (kb % 3) * kKBytes; };
   auto vslot = [&](int kb) { return lds + 3 * kKBytes + (kb & 1) * kVBytes; };
 
-  // Load q (0..3) of this wave's share of K block kb / Vt block kb.
+  // Load q (0..3) of this wave's share of K block kb / Vt block kb.  Each
+  // block's loads go through a descriptor rebased on the block's first key
+  // (scalar arithmetic), so the lanes' offsets need no per-block add; the
+  // descriptor's end stays the head's, so rows past N still read zero.
+  const uint8_t *kh = p.K + head * p.sk_b, *vh = p.V + head * p.sv_b;
   auto copy_k1 = [&](int kb, int q) {
     lds_u8 *kd = kslot(kb) + (4 * w) * kKRow;
     const uint32_t kbase = (uint32_t)((int64_t)kb * kBN * p.ldk_b);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(kd + q * 16 * kKRow), 16,
-                                             kbase + koff[q], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(kh + kbase, p.k_bytes - kbase),
+                                             (lds_void_t *)(kd + q * 16 * kKRow), 16, koff[q], 0,
+                                             0, 0);
   };
   // masked: block kb may be cut by N.  Only whole 8-key chunks are copied; a
   // chunk that straddles N is filled by finish_v, so nothing past a row's N
   // keys is ever read.
   auto copy_v1 = [&](int kb, int q, auto masked) {
     lds_u8 *vd = vslot(kb) + (8 * w) * kVRow;
-    uint32_t off = voff[q] + (uint32_t)(kb * kVRow);
+    const uint32_t vbase = (uint32_t)(kb * kVRow);
+    uint32_t off = voff[q];
     if constexpr (decltype(masked)::value)
       if ((int64_t)kb * kBN + vkey[q] + 8 > p.N) off = kOob;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vd + q * 32 * kVRow), 16, off, 0,
-                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(make_rsrc(vh + vbase, p.v_bytes - vbase),
+                                             (lds_void_t *)(vd + q * 32 * kVRow), 16, off, 0, 0,
+                                             0);
   };
   auto copy_k = [&](int kb) {
 #pragma unroll
