@@ -5,9 +5,10 @@ no other stream, allocates nothing and issues no memset, so its launches can be
 ordered on a side stream and captured into a HIP graph.  The tests below check
 both with +-1 inputs, whose products are small integers and must match the
 oracle exactly: a GEMM on a side stream that also produces its inputs, and a
-captured graph of six different calls (fp16 TN, fp8 TN, fp16 NN, batched
-QK^T, fused attention, split-K fp16 TN with its workspace) replayed several
-times.  Between replays, eager copies
+captured graph of eight different calls (fp16 TN, fp8 TN, fp16 NN, batched
+QK^T, fused attention, split-K fp16 TN with its workspace, and two planned
+calls of several launches each: QK^T heads whose columns run in two parts,
+and a workspace plan with a split-K tail) replayed several times.  Between replays, eager copies
 on the current stream put new inputs in place, and every replay is checked
 against the oracle (the attention output within its tolerance of
 test_gpu_attention).
@@ -85,6 +86,21 @@ def test_graph_capture_replays_match_oracle():
     c6 = torch.empty((N6, M6), dtype=torch.float16, device=DEV)
     ws6_bytes = dg.splitk_workspace_bytes(M6, N6, S6)
     ws6 = torch.empty(ws6_bytes // 4, dtype=torch.float32, device=DEV)
+    # Planned launches: two QK^T heads with a 256-deep contraction whose
+    # columns run in two launches, and a workspace plan (whole rounds of
+    # columns, then split-K of the rest and its reduction: three launches).
+    H7, M7, N7, D7 = 2, 4096, 4352, 256
+    q7 = torch.empty((H7, M7, D7), dtype=torch.float16, device=DEV)
+    k7 = torch.empty((H7, N7, D7), dtype=torch.float16, device=DEV)
+    s7 = torch.empty((H7, N7, M7), dtype=torch.float16, device=DEV)
+    M8, N8, K8 = 4096, 4352, 4096
+    a8 = torch.empty((M8, K8), dtype=torch.float16, device=DEV)
+    b8 = torch.empty((N8, K8), dtype=torch.float16, device=DEV)
+    c8 = torch.empty((N8, M8), dtype=torch.float16, device=DEV)
+    ws8_bytes = dg.tn_workspace_bytes(M8, N8, K8)
+    ws8 = torch.empty(max(ws8_bytes, 16) // 4, dtype=torch.float32, device=DEV)
+    print("plans: qkt %s, ws %s" % (dg.tn_plan(M7, N7, D7, batch=H7),
+                                    dg.tn_plan(M8, N8, K8, workspace_bytes=ws8_bytes)), flush=True)
 
     def calls():
         dg.gemm_f16_tn(a1, b1, c1, M1, N1, K1, K1, K1, M1)
@@ -94,6 +110,8 @@ def test_graph_capture_replays_match_oracle():
         dg.attention_fwd_f16(q5, k5, vt5, o5, H5, M5, N5, D5, D5, D5, N5, D5, M5 * D5, N5 * D5,
                              D5 * N5, M5 * D5, scale5)
         dg.gemm_f16_tn_splitk(a6, b6, c6, M6, N6, K6, K6, K6, M6, S6, ws6, ws6_bytes)
+        dg.gemm_batched_qkt(q7, k7, s7, H7, M7, N7, D7, D7, D7, M7, M7 * D7, N7 * D7, N7 * M7)
+        dg.gemm_f16_tn_ws(a8, b8, c8, M8, N8, K8, K8, K8, M8, ws8, ws8_bytes)
 
     def load(seed):
         x1 = inputs.make_shape("f16", M1, N1, K1, dist="pm1", seed=seed)
@@ -102,6 +120,8 @@ def test_graph_capture_replays_match_oracle():
         x4 = inputs.make_shape("qkt", M4, N4, D4, dist="pm1", seed=seed + 3, batch=H)
         x5 = inputs.make_shape("attn", M5, N5, D5, seed=seed + 4, batch=H5)
         x6 = inputs.make_shape("f16", M6, N6, K6, dist="pm1", seed=seed + 5)
+        x7 = inputs.make_shape("qkt", M7, N7, D7, dist="pm1", seed=seed + 6, batch=H7)
+        x8 = inputs.make_shape("f16", M8, N8, K8, dist="pm1", seed=seed + 7)
         a1.copy_(torch.from_numpy(x1["A"]))
         b1.copy_(torch.from_numpy(x1["B"]))
         a2.copy_(torch.from_numpy(x2["A"]))
@@ -115,12 +135,16 @@ def test_graph_capture_replays_match_oracle():
         vt5.copy_(torch.from_numpy(x5["Vt"]))
         a6.copy_(torch.from_numpy(x6["A"]))
         b6.copy_(torch.from_numpy(x6["B"]))
-        for t in (c1, c2, c3, s4, o5, c6, ws6):
+        q7.copy_(torch.from_numpy(x7["Q"]))
+        k7.copy_(torch.from_numpy(x7["K"]))
+        a8.copy_(torch.from_numpy(x8["A"]))
+        b8.copy_(torch.from_numpy(x8["B"]))
+        for t in (c1, c2, c3, s4, o5, c6, ws6, s7, c8, ws8):
             t.fill_(0)
         torch.cuda.synchronize()
-        return x1, x2, x3, x4, x5, x6
+        return x1, x2, x3, x4, x5, x6, x7, x8
 
-    def check(x1, x2, x3, x4, x5, x6):
+    def check(x1, x2, x3, x4, x5, x6, x7, x8):
         exact(c1.cpu().numpy().view(np.uint16),
               oracle.gemm_tn(x1["A"], x1["B"], oracle.FMT_F16, M1, N1, K1), oracle.FMT_F16)
         exact(c2.cpu().numpy().view(np.uint16),
@@ -136,6 +160,10 @@ def test_graph_capture_replays_match_oracle():
             assert np.all(np.abs(o[h] - want) <= tol(want, x5["Vt"][h])), h
         exact(c6.cpu().numpy().view(np.uint16),
               oracle.gemm_tn(x6["A"], x6["B"], oracle.FMT_F16, M6, N6, K6), oracle.FMT_F16)
+        exact(s7.cpu().numpy().view(np.uint16),
+              oracle.batched_qkt(x7["Q"], x7["K"], H7, M7, N7, D7), oracle.FMT_F16)
+        exact(c8.cpu().numpy().view(np.uint16),
+              oracle.gemm_tn(x8["A"], x8["B"], oracle.FMT_F16, M8, N8, K8), oracle.FMT_F16)
 
     # Eager run first (also settles the library's one-time device queries).
     xs = load(100)
