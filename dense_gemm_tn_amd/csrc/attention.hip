@@ -235,13 +235,16 @@ __device__ __forceinline__ void static_for(F &&f) {
 //   64..95  scores of half 0, block kb + 1     probabilities of half 1, block kb
 //   96..127 output of half 1, block kb         ... and maxima of half 0, block kb + 1
 //
-// Each group of two slots shares one operand fragment read from LDS
-// (K rows for scores, Vt rows for outputs), three groups ahead.  A half's
-// reference maximum is checked (and, rarely, moved) right after its maxima.
+// Each group of two slots shares one operand fragment (K rows for scores, Vt
+// rows for outputs), read from LDS three groups ahead.  The 16 Vt fragments of
+// block kb are read once, for half 0's output products, and kept in registers
+// for half 1's (slots 96..127); the K fragments cycle through a ring.  A
+// half's reference maximum is checked (and, rarely, moved) right after its
+// maxima.
 constexpr int kSlots = 128;
 constexpr int kGroups = kSlots / 2;   // one fragment per group of two MFMAs
 constexpr int kAhead = 3;             // fragment lookahead in groups
-constexpr int kRing = 8;              // fragment registers (divides kGroups)
+constexpr int kRing = 8;              // K-fragment ring registers (divides kGroups)
 static_assert(kGroups % kRing == 0 && kAhead < kRing, "fragment ring");
 
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnParams p) {
@@ -397,6 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
   float mloc[2][2], mx[2][2];
   float pv8[8];
   half8_t fr[kRing];
+  half8_t vsave[16];  // Vt fragments of the body's block, read once for both halves
 
   auto fence_accumulators = [&]() {
     mfma_drain();
@@ -537,7 +541,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
         if constexpr (uu == 0) {
           constexpr int fn = f + kAhead;
           if constexpr (fn < kGroups) {
-            if constexpr (kNext || !(fn >= 32 && fn < 48))
+            if constexpr (fn >= 16 && fn < 32)
+              vsave[fn - 16] = frag(kb, std::integral_constant<int, fn>{});
+            else if constexpr (fn >= 48)
+              ;  // the same Vt fragments again: kept from groups 16 .. 31
+            else if constexpr (kNext || !(fn >= 32 && fn < 48))
               fr[fn % kRing] = frag(kb, std::integral_constant<int, fn>{});
           } else if constexpr (kNext) {
             fr[fn % kRing] = frag(kb + 1, std::integral_constant<int, fn - kGroups>{});
@@ -569,7 +577,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
         // The MFMA.
         if constexpr (kNext || ph != 2)
           slot_mfma(std::integral_constant<int, f>{}, std::integral_constant<int, uu>{},
-                    fr[f % kRing]);
+                    (ph & 1) ? vsave[f & 15] : fr[f % kRing]);
         __builtin_amdgcn_sched_barrier(0);
       });
     };
