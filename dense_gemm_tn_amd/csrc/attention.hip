@@ -236,16 +236,15 @@ __device__ __forceinline__ void static_for(F &&f) {
 //   96..127 output of half 1, block kb         ... and maxima of half 0, block kb + 1
 //
 // Each group of two slots shares one operand fragment (K rows for scores, Vt
-// rows for outputs), read from LDS three groups ahead.  The 16 Vt fragments of
-// block kb are read once, for half 0's output products, and kept in registers
-// for half 1's (slots 96..127); the K fragments cycle through a ring.  A
-// half's reference maximum is checked (and, rarely, moved) right after its
-// maxima.
+// rows for outputs).  Every fragment is read from LDS once, three groups
+// ahead of its first use, and kept in registers for its second: the 16 Vt
+// fragments of block kb from half 0's output products (slots 32..63) to half
+// 1's (96..127), the 16 K fragments of block kb + 1 from half 0's score
+// products (64..95) to half 1's, which open the next body (0..31).  A half's
+// reference maximum is checked (and, rarely, moved) right after its maxima.
 constexpr int kSlots = 128;
 constexpr int kGroups = kSlots / 2;   // one fragment per group of two MFMAs
 constexpr int kAhead = 3;             // fragment lookahead in groups
-constexpr int kRing = 8;              // K-fragment ring registers (divides kGroups)
-static_assert(kGroups % kRing == 0 && kAhead < kRing, "fragment ring");
 
 __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kLdsBytes];
@@ -399,8 +398,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
   half8_t pf[2][2][2];   // probabilities [half][j][uu] as output-product operands
   float mloc[2][2], mx[2][2];
   float pv8[8];
-  half8_t fr[kRing];
-  half8_t vsave[16];  // Vt fragments of the body's block, read once for both halves
+  half8_t vsave[16];  // Vt fragments of block kb, read once for both halves
+  half8_t ksave[16];  // K fragments of block kb + 1, read once for both halves
 
   auto fence_accumulators = [&]() {
     mfma_drain();
@@ -524,8 +523,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
 
   // One body.  kNext: block kb + 1 exists (its half-0 scores and maxima are
   // part of this body).  mask_cur: block kb may be cut by N; mask_next: block
-  // kb + 1 may be.  Fragments of this body's first kAhead groups were read by
-  // the previous body (or the prologue); this body reads the next body's.
+  // kb + 1 may be.  The K fragments of this body's first 16 groups were read
+  // by the previous body (or the prologue).
   auto body = [&](int kb, auto has_next, auto mask_cur, auto mask_next) {
     constexpr bool kNext = decltype(has_next)::value;
     const int64_t rest = p.N - (int64_t)kb * kBN;
@@ -536,19 +535,17 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
     auto run_slots = [&](auto lo, auto hi) {
       static_for<decltype(lo)::value, decltype(hi)::value>([&](auto kc) {
         constexpr int k = decltype(kc)::value, f = k >> 1, uu = k & 1, ph = f >> 4;
-        // Fragment read kAhead groups ahead (the next body's first groups are
-        // K fragments of block kb + 1, which is resident now).
+        // Fragment read kAhead groups ahead of its first use.
         if constexpr (uu == 0) {
           constexpr int fn = f + kAhead;
           if constexpr (fn < kGroups) {
             if constexpr (fn >= 16 && fn < 32)
               vsave[fn - 16] = frag(kb, std::integral_constant<int, fn>{});
-            else if constexpr (fn >= 48)
-              ;  // the same Vt fragments again: kept from groups 16 .. 31
-            else if constexpr (kNext || !(fn >= 32 && fn < 48))
-              fr[fn % kRing] = frag(kb, std::integral_constant<int, fn>{});
-          } else if constexpr (kNext) {
-            fr[fn % kRing] = frag(kb + 1, std::integral_constant<int, fn - kGroups>{});
+            else if constexpr (fn >= 32 && fn < 48) {
+              if constexpr (kNext) ksave[fn - 32] = frag(kb, std::integral_constant<int, fn>{});
+            }
+            // groups 0 .. 15 use the K fragments kept from the previous body
+            // (or the prologue), groups 48 .. 63 the Vt fragments of 16 .. 31
           }
         }
         // Copies of K block kb + 2 and Vt block kb + 1, one every other slot
@@ -577,7 +574,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
         // The MFMA.
         if constexpr (kNext || ph != 2)
           slot_mfma(std::integral_constant<int, f>{}, std::integral_constant<int, uu>{},
-                    (ph & 1) ? vsave[f & 15] : fr[f % kRing]);
+                    (ph & 1) ? vsave[f & 15] : ksave[f & 15]);
         __builtin_amdgcn_sched_barrier(0);
       });
     };
@@ -614,6 +611,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
       constexpr int y = decltype(yc)::value, t = y >> 2, s = y & 3;
       const half8_t a = *(const __attribute__((address_space(3))) half8_t *)(
           kslot(0) + ksw[s] + (32 * (t >> 1) + 4 * (t & 1)) * kKRow);
+      ksave[y] = a;
       if constexpr (s == 0) {
         mma_s0(a, qf[0][s], sc[0][t][0]);
         mma_s0(a, qf[1][s], sc[0][t][1]);
@@ -636,10 +634,6 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(const AttnPa
 #pragma unroll
     for (int uu = 0; uu < 2; ++uu) m_run[uu] = max_over_column(mloc[0][uu]) * c;
   }
-  static_for<0, kAhead>([&](auto fc) {
-    constexpr int f = decltype(fc)::value;
-    fr[f % kRing] = frag(0, fc);
-  });
 
   const std::true_type T;
   const std::false_type F;
