@@ -58,6 +58,11 @@
 //   MI355X FP8 GEMM page weighs against its 4-wave one); measured slower here,
 //   so only used when forced.
 //
+// Plans (plan_tn): when the 256-row tiles leave a ragged last round of one
+//   block per CU, a TN call may run the first columns of C in whole rounds and
+//   the rest as a second launch (the selector's configuration for it, or, with
+//   a caller workspace, split-K), each element computed by exactly one kernel.
+//
 // Other op-code layouts (gemm_f16, gemm_f8): the 256 x 256 and 128 x 128
 //   kernels take template flags AMN / BMN for an M- or N-contiguous operand,
 //   staged in LDS as it lies (K-rows of the tile's columns) and turned into
