@@ -2243,16 +2243,19 @@ static int launch_ws(const Problem &pr, void *ws, int64_t ws_bytes, hipStream_t 
   const int chk = check_tn(pr, es);
   if (chk < 0) return DG_OK;
   if (chk != DG_OK) return chk;
-  if (ws != nullptr) {
+  const TnPlan plan = plan_tn(es, pr.M, pr.N, pr.K, pr.batch, ws != nullptr ? ws_bytes : 0);
+  if (plan.ws_bytes > 0) {
+    // The bytes the plan uses must not overlap an operand (a larger arena
+    // around them may).
+    const uint64_t used = (uint64_t)plan.ws_bytes;
     const uint64_t a_all = span_bytes(pr.M, pr.K, pr.lda, es) + (uint64_t)(pr.batch - 1) * pr.stride_a * es;
     const uint64_t b_all = span_bytes(pr.N, pr.K, pr.ldb, es) + (uint64_t)(pr.batch - 1) * pr.stride_b * es;
     const uint64_t c_all = span_bytes(pr.N, pr.M, pr.ldc, 2) + (uint64_t)(pr.batch - 1) * pr.stride_c * 2;
-    if (overlaps(ws, (uint64_t)ws_bytes, pr.A, a_all) || overlaps(ws, (uint64_t)ws_bytes, pr.B, b_all) ||
-        overlaps(ws, (uint64_t)ws_bytes, pr.C, c_all))
+    if (overlaps(ws, used, pr.A, a_all) || overlaps(ws, used, pr.B, b_all) ||
+        overlaps(ws, used, pr.C, c_all))
       return DG_ERR_INVALID_ARGUMENT;
     if (!aligned16(ws)) return DG_ERR_UNSUPPORTED;
   }
-  const TnPlan plan = plan_tn(es, pr.M, pr.N, pr.K, pr.batch, ws != nullptr ? ws_bytes : 0);
   if (plan.dp_cols == 0) {
     if (plan.splits > 1) return launch_splitk<KIND>(pr, plan.splits, ws, ws_bytes, stream);
     return launch_cfg<KIND>(pr, Config{plan.whole}, stream);

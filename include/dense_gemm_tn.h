@@ -327,14 +327,16 @@ int gemm_f8_tn_splitk(const void *A, const void *B, void *C,
  * tuning" (per-shape configurations and their selection).
  *
  * gemm_f16_tn_ws / gemm_f8_tn_ws: gemm_f16_tn / gemm_f8_tn by the plan that
- *   fits `workspace_bytes` bytes of `workspace` (device memory, 16-byte
- *   aligned, overlapping none of A, B and C; NULL with 0 bytes allowed: then
- *   only plans without a workspace).  Ownership, ordering and the C rule are
- *   those of gemm_f16_tn; the workspace is the caller's, its contents are
- *   undefined afterwards, and calls that may run concurrently must not share
- *   it.  Errors: as gemm_f16_tn, plus DG_ERR_INVALID_ARGUMENT for negative
- *   workspace_bytes, a NULL workspace with nonzero bytes, or a workspace
- *   overlapping A, B or C, and DG_ERR_UNSUPPORTED for a misaligned one.
+ *   fits `workspace_bytes` bytes of `workspace` (device memory; NULL with 0
+ *   bytes allowed: then only plans without a workspace).  The bytes a plan
+ *   uses, the first gemm_tn_plan(...)[4] of the workspace, must be 16-byte
+ *   aligned and overlap none of A, B and C.  Ownership, ordering and the C
+ *   rule are those of gemm_f16_tn; the workspace is the caller's, the bytes
+ *   used are undefined afterwards (the rest is not touched), and calls that
+ *   may run concurrently must not share it.  Errors: as gemm_f16_tn, plus
+ *   DG_ERR_INVALID_ARGUMENT for negative workspace_bytes, a NULL workspace
+ *   with nonzero bytes, or used bytes overlapping A, B or C, and
+ *   DG_ERR_UNSUPPORTED for a misaligned workspace whose plan uses it.
  * gemm_tn_workspace_bytes: bytes of workspace the best plan for an M x N x K
  *   product uses (0 when it needs none; -1 for negative sizes).
  * gemm_tn_plan: the plan for the given sizes, head count and workspace bytes:
