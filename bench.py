@@ -30,7 +30,11 @@ normally distributed data, rotating buffers).  Per workload:
      explains run-to-run and box-to-box spread of a power-limited part.
 Before the warm-up steps, each workload runs back to back for --settle-ms
 (0.25 s) so timing starts at the clock the load sustains rather than on the
-ramp up from idle.
+ramp up from idle.  All of this runs in --processes (3) independent processes,
+one after another; each workload is reported as measured by the process with
+the median time, with every process's mean and per-launch median, the median
+of those medians and their range (the hello-gpu chapter, section 11.5: three
+processes, median of medians with the range).
 
 Prints ONE JSON line.  The headline `value` is the FP16 TN 4096^3 workload;
 every other workload of the default list (the five configurations of the
@@ -509,6 +513,82 @@ def cpu_baseline(w, x, sets, target_s=10.0):
     }
 
 
+def strip_processes(argv):
+    """argv without any --processes option (the children get --processes 1)."""
+    out, skip = [], False
+    for a in argv:
+        if skip:
+            skip = False
+        elif a == "--processes":
+            skip = True
+        elif not a.startswith("--processes="):
+            out.append(a)
+    return out
+
+
+def merge_processes(lines):
+    """One line from the lines of several processes (the timing protocol's
+    independent processes): each workload as measured by the process with the
+    median ms_per_step, plus every process's mean and per-launch median, the
+    median of those medians and their range; the CPU baseline from the first
+    process (the others skip it)."""
+    import statistics
+
+    P = len(lines)
+    first = lines[0]
+    merged = {}
+    for name in first["workloads"]:
+        recs = [ln["workloads"][name] for ln in lines]
+        ms = [r["ms_per_step"] for r in recs]
+        mid = sorted(range(P), key=lambda i: ms[i])[P // 2]
+        r = dict(recs[mid])
+        meds = [rr["per_launch_us"]["median"] for rr in recs if rr.get("per_launch_us")]
+        r["processes"] = {
+            "count": P,
+            "reported_process": mid,
+            "ms_per_step": ms,
+            "per_launch_median_us": meds,
+            "median_of_medians_us": statistics.median(meds) if meds else None,
+            "range_of_medians_us": [min(meds), max(meds)] if meds else None,
+        }
+        merged[name] = r
+    head = first["config"]["workload"]
+    hr = merged[head]
+    line = dict(first)
+    line.update({
+        "value": hr["tflops"],
+        "ms_per_step": hr["ms_per_step"],
+        "frac_of_peak": hr["frac_of_peak"],
+        "roofline": {k: hr["roofline"][k] for k in
+                     ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+        "clock": hr.get("clock"),
+        "parity_ok": all(ln["parity_ok"] for ln in lines),
+        "processes": P,
+        "workloads": merged,
+        "cpu_baseline": first.get("cpu_baseline"),
+    })
+    return line
+
+
+def run_processes(P, argv):
+    """Run the measurement in P child processes, one after another on the one
+    GPU, and merge their lines."""
+    import subprocess
+
+    base = [sys.executable, os.path.abspath(__file__)] + strip_processes(argv) + ["--processes", "1"]
+    lines = []
+    for i in range(P):
+        cmd = base + (["--no-cpu"] if i > 0 and "--no-cpu" not in base else [])
+        print("bench: process %d of %d" % (i + 1, P), file=sys.stderr, flush=True)
+        out = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+        if out.returncode != 0:
+            sys.stderr.write(out.stdout[-2000:])
+            sys.exit(out.returncode)
+        js = [ln for ln in out.stdout.splitlines() if ln.startswith("{")]
+        lines.append(json.loads(js[-1]))
+    return merge_processes(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -525,6 +605,10 @@ def main():
                     help="skip the sampled oracle checks before timing (profiling runs)")
     ap.add_argument("--settle-ms", type=float, default=250.0,
                     help="back-to-back launches for this long before the warm-up steps")
+    ap.add_argument("--processes", type=int, default=3,
+                    help="independent processes, run one after another; the line reports "
+                         "each workload from the process with the median time, plus every "
+                         "process's per-launch median and their median and range")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (a known-size kernel for "
                          "scaling HBM byte counters), then exit")
@@ -546,6 +630,11 @@ def main():
               "--gpus %d is not supported (a multi-GPU run would shard N across GPUs with no "
               "exchange, see the design notes)." % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.processes > 1:
+        # The parent only starts the children and merges their lines: it never
+        # touches the GPU itself.
+        print(json.dumps(run_processes(args.processes, sys.argv[1:])), flush=True)
+        return
 
     import torch
 

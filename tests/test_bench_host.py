@@ -115,3 +115,32 @@ def test_launch_spans_from_records():
     assert s == {"median": 3.25, "min": 2.5, "max": 4.0, "launches": 2}
     rec[3, 7] = 0                                  # an unfinished record drops its launch
     assert bench.launch_spans_us(rec, 2)["launches"] == 1
+
+
+def test_processes_option_is_stripped_for_children():
+    assert bench.strip_processes(["--steps", "5", "--processes", "3", "--no-cpu"]) == \
+        ["--steps", "5", "--no-cpu"]
+    assert bench.strip_processes(["--processes=2", "--workload", "f16_4096"]) == \
+        ["--workload", "f16_4096"]
+
+
+def test_merge_processes_reports_the_median_process():
+    def line(ms, med, cpu):
+        w = {"tflops": 1.0 / ms, "ms_per_step": ms, "frac_of_peak": 0.5,
+             "per_launch_us": {"median": med, "min": med, "max": med},
+             "roofline": {"bound": "mfma", "achieved": 1.0 / ms, "peak": 2.0, "unit": "x",
+                          "frac": 0.5 / ms, "traffic": None, "kernel": "k"},
+             "clock": {"sclk_mhz": 2000.0 + ms}}
+        return {"metric": "m", "value": 1.0 / ms, "ms_per_step": ms, "parity_ok": True,
+                "config": {"workload": "f16_4096"}, "cpu_baseline": cpu,
+                "workloads": {"f16_4096": w}}
+    merged = bench.merge_processes([line(0.30, 300.0, {"v": 1}), line(0.10, 100.0, None),
+                                    line(0.20, 210.0, None)])
+    w = merged["workloads"]["f16_4096"]
+    assert merged["ms_per_step"] == 0.20 and merged["value"] == 5.0   # the median process
+    assert w["processes"]["reported_process"] == 2
+    assert w["processes"]["ms_per_step"] == [0.30, 0.10, 0.20]
+    assert w["processes"]["median_of_medians_us"] == 210.0
+    assert w["processes"]["range_of_medians_us"] == [100.0, 300.0]
+    assert merged["cpu_baseline"] == {"v": 1} and merged["processes"] == 3
+    assert merged["clock"]["sclk_mhz"] == 2000.2
