@@ -593,7 +593,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", action="append", default=None,
                     help="workload names (default: DEFAULT_WORKLOADS: the five configurations "
                          "f16_4096, f8_8192, f16_256_pm1, f16_1920x13900x4096, "
