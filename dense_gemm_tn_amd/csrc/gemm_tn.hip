@@ -553,12 +553,16 @@ __device__ __forceinline__ void store_c(
 
 // Epilogue through LDS: the wave's 128 x 128 tile is converted to 16-bit
 // values and written column-major into the wave's own 32 KiB of LDS (column n
-// at n * 256 B, its 16-byte chunk c stored in slot c ^ (n & 15)), then read
+// at n * 256 B, its 16-byte chunk c stored in slot c ^ (n & 15), with the
+// slot's two 8-byte halves swapped when n & 8), then read
 // back as 16 contiguous bytes (8 rows) per lane, so each global store
 // instruction writes four full 256-byte column segments of C.  The stores are
 // non-temporal: C is not read again here, and keeping it out of L2 leaves the
 // room to the A and B strips.  Needs 16-byte aligned columns (ldc % 8 == 0);
-// rows or columns past M, N are masked.
+// rows or columns past M, N are masked.  The half swap makes the writes
+// conflict-free: the 16 lanes of a write phase hold one 4-row run of 16
+// columns, whose slots differ but whose half would otherwise be the same, so
+// columns n and n + 8 met in the same bank (a bank period is 128 bytes).
 template <int KIND, int NTN>
 __device__ __forceinline__ void store_c_lds(
     const Params &p, uint8_t *Cb,
@@ -583,7 +587,7 @@ __device__ __forceinline__ void store_c_lds(
         w.x = w0;
         w.y = w1;
         const int chunk = (m >> 3) ^ (n & 15);
-        *(lds_u2 *)(buf + n * 256 + chunk * 16 + (m & 7) * 2) = w;
+        *(lds_u2 *)(buf + n * 256 + chunk * 16 + (((m & 7) * 2) ^ (n & 8))) = w;
       }
     }
   }
@@ -593,7 +597,8 @@ __device__ __forceinline__ void store_c_lds(
   for (int r = 0; r < S::WN / 4; ++r) {
     const int n = 4 * r + (lane >> 4);
     const int mc = lane & 15;
-    const u32x4 v = *(lds_u4 *)(buf + n * 256 + ((mc ^ (n & 15)) * 16));
+    u32x4 v = *(lds_u4 *)(buf + n * 256 + ((mc ^ (n & 15)) * 16));
+    if (r & 2) v = v.zwxy;   // n & 8: the slot's two halves are swapped
     const int64_t gm = m_base + 8 * mc, gn = n_base + n;
     uint16_t *dst = (uint16_t *)Cb + (gn * p.ldc + gm);
     if (full || (gn < p.N && gm + 7 < p.M)) {
@@ -1071,7 +1076,8 @@ __device__ __forceinline__ void sk_compute(float4_t_v (&acc)[kSkSub][kSkSub], ld
 
 // Converted accumulators of wave (wm, wn) into the tile's 32 KiB transpose
 // buffer: column n (0..127) at n * 256 B, its 16-byte chunk c (rows 8c ..
-// 8c+7) in slot c ^ (n & 15).  Lane (rl, grp) of tile (i, j) holds rows
+// 8c+7) in slot c ^ (n & 15), the slot's 8-byte halves swapped when n & 8
+// (conflict-free writes, as in store_c_lds).  Lane (rl, grp) of tile (i, j) holds rows
 // 16i + 4 grp .. +3 of column 16j + rl: one 8-byte write per tile.  A 16-lane
 // read phase covers one whole column (all 16 slots of a bank period).
 template <int KIND>
@@ -1089,7 +1095,7 @@ __device__ __forceinline__ void sk_to_lds(const Params &p, const float4_t_v (&ac
       w.x = w0;
       w.y = w1;
       *(__attribute__((address_space(3))) u32x2 *)(buf + n * 256 + (((m >> 3) ^ (n & 15)) * 16) +
-                                                 (m & 7) * 2) = w;
+                                                 (((m & 7) * 2) ^ (n & 8))) = w;
     }
   }
 }
@@ -1138,6 +1144,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_tn_skinny_kernel(Params p) {
     for (int r = 0; r < 8; ++r) {
       const int n = 32 * wave + 4 * r + (lane >> 4);
       v[r] = *(__attribute__((address_space(3))) u32x4 *)(a_st + n * 256 + (((lane & 15) ^ (n & 15)) * 16));
+      if (r & 2) v[r] = v[r].zwxy;   // n & 8: the slot's two halves are swapped
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of the A space are done
     __syncthreads();                     // everyone's are: the next A strip may land
@@ -1563,8 +1570,10 @@ constexpr int kPpWaveM = 64;     // rows per wave
 constexpr int kPpWaveN = 128;    // columns per wave
 
 // Epilogue of a 64 x 128 wave tile through the wave's 16 KiB of LDS: column n
-// at n * 128 B, its 16-byte chunk c (8 rows) in slot c ^ (n & 7); read back as
-// 8 rows per lane, eight 128-byte column segments per store instruction.
+// at n * 128 B, its 16-byte chunk c (8 rows) in slot c ^ (n & 7), the slot's
+// 8-byte halves swapped when n & 8 (conflict-free writes, as in store_c_lds);
+// read back as 8 rows per lane, eight 128-byte column segments per store
+// instruction.
 template <int KIND>
 __device__ __forceinline__ void store_c_pp(const Params &p, uint8_t *Cb,
                                            const float4_t_v (&acc)[4][8],
@@ -1585,7 +1594,7 @@ __device__ __forceinline__ void store_c_pp(const Params &p, uint8_t *Cb,
       u32x2 w;
       w.x = w0;
       w.y = w1;
-      *(lds_u2 *)(buf + n * 128 + (((m >> 3) ^ (n & 7)) * 16) + (m & 7) * 2) = w;
+      *(lds_u2 *)(buf + n * 128 + (((m >> 3) ^ (n & 7)) * 16) + (((m & 7) * 2) ^ (n & 8))) = w;
     }
   }
   const bool full = (m_base + kPpWaveM <= p.M) && (n_base + kPpWaveN <= p.N);
@@ -1593,7 +1602,8 @@ __device__ __forceinline__ void store_c_pp(const Params &p, uint8_t *Cb,
   for (int r = 0; r < kPpWaveN / 8; ++r) {
     const int n = 8 * r + (lane >> 3);
     const int mc = lane & 7;
-    const u32x4 v = *(lds_u4 *)(buf + n * 128 + ((mc ^ (n & 7)) * 16));
+    u32x4 v = *(lds_u4 *)(buf + n * 128 + ((mc ^ (n & 7)) * 16));
+    if (r & 1) v = v.zwxy;   // n & 8: the slot's two halves are swapped
     const int64_t gm = m_base + 8 * mc, gn = n_base + n;
     uint16_t *dst = (uint16_t *)Cb + (gn * p.ldc + gm);
     if (full || (gn < p.N && gm + 7 < p.M)) {
