@@ -75,34 +75,52 @@ def kernel_name(w):
         return "attention_fwd_kernel"
     kind = 1 if w.kind == "f8" else 0
     layout = w.extra.get("layout", "TN")
+    kstep = 128 if w.kind == "f8" else 64
+
+    def tiles128(M, N):
+        return ((M + 127) // 128) * ((N + 127) // 128)
+
+    def mid(M, N, batch, K, split=False, splits=1):
+        """The 128 x 128 kernel on that grid (its ring depth from the library)."""
+        nk = (K + kstep - 1) // kstep
+        per = (nk + splits - 1) // splits if nk else 0
+        ranges = (nk + per - 1) // per if per else 0
+        blocks = tiles128(M, N) * (ranges if split else batch)
+        return "gemm_tn_mid_kernel<%d, false, false, %s, %d>" % (
+            kind, "true" if split else "false", dg.mid_stages(blocks, per if split else nk))
+
     if layout != "TN":
         amn = "true" if layout[0] == "N" else "false"
         bmn = "true" if layout[1] == "T" else "false"
         cfg_of = dg.f8_config if w.kind == "f8" else dg.f16_config
         if cfg_of(layout[0], layout[1], w.M, w.N, w.K) == 2:
-            return "gemm_tn_mid_kernel<%d, %s, %s>" % (kind, amn, bmn)
+            return "gemm_tn_mid_kernel<%d, %s, %s, false, 2>" % (kind, amn, bmn)
         return "gemm_tn_kernel<%d, 8, %s, %s>" % (kind, amn, bmn)
-    if w.extra.get("splitk") and dg.splitk_choose(w.M, w.N, w.K, fp8=(w.kind == "f8")) > 1:
-        return "gemm_tn_mid_kernel<%d, false, false, true>" % kind
-    names = {0: "gemm_tn_kernel<%d, 8, false, false>" % kind,
-             1: "gemm_tn_kernel<%d, 7, false, false>" % kind,
-             2: "gemm_tn_mid_kernel<%d, false, false>" % kind,
-             3: "gemm_tn_skinny_kernel<%d>" % kind,
-             4: "gemm_tn_pp_kernel<%d>" % kind}
     fp8 = w.kind == "f8"
+    if w.extra.get("splitk"):
+        s = dg.splitk_choose(w.M, w.N, w.K, fp8=fp8)
+        if s > 1:
+            return mid(w.M, w.N, 1, w.K, split=True, splits=s)
+
+    def names(cfg, M, N):
+        return {0: "gemm_tn_kernel<%d, 8, false, false>" % kind,
+                1: "gemm_tn_kernel<%d, 7, false, false>" % kind,
+                3: "gemm_tn_skinny_kernel<%d>" % kind,
+                4: "gemm_tn_pp_kernel<%d>" % kind}.get(cfg) or mid(M, N, w.batch, w.K)
+
     ws = dg.tn_workspace_bytes(w.M, w.N, w.K, fp8=fp8) if w.extra.get("ws") else 0
     plan = dg.tn_plan(w.M, w.N, w.K, w.batch, ws, fp8=fp8)
     if plan["dp_cols"] > 0 or plan["splits"] > 1:
         # Two launches per call (whole rounds of columns, then the rest, or
         # split-K and its reduction): the label names both.
-        split = "gemm_tn_mid_kernel<%d, false, false, true>" % kind
+        nt = w.N - plan["dp_cols"]
+        split = mid(w.M, nt, 1, w.K, split=True, splits=plan["splits"])
         if plan["dp_cols"] == 0:
             return split
-        nt = w.N - plan["dp_cols"]
         tail = split if plan["splits"] > 1 else \
-            names[dg.tn_config(w.M, nt, w.K, w.batch, fp8=fp8)]
-        return "%s + %s" % (names[plan["dp_config"]], tail)
-    return names[dg.tn_config(w.M, w.N, w.K, w.batch, fp8=fp8)]
+            names(dg.tn_config(w.M, nt, w.K, w.batch, fp8=fp8), w.M, nt)
+        return "%s + %s" % (names(plan["dp_config"], w.M, plan["dp_cols"]), tail)
+    return names(dg.tn_config(w.M, w.N, w.K, w.batch, fp8=fp8), w.M, w.N)
 
 
 # The five configurations of the hot path first (the headline FP16 4096^3, FP8

@@ -33,6 +33,7 @@ EXPORTS = (
     "gemm_tile_order",
     "gemm_block_tile",
     "gemm_tn_config",
+    "gemm_mid_stages",
     "gemm_f16_config",
     "gemm_f8",
     "gemm_f8_config",
@@ -79,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.gemm_tile_order.argtypes = [i64, i64, i64, vp]
         L.gemm_block_tile.argtypes = []
         L.gemm_tn_config.argtypes = [ctypes.c_int, i64, i64, i64, i64]
+        L.gemm_mid_stages.argtypes = [i64, i64]
         L.gemm_f16_config.argtypes = [ctypes.c_char, ctypes.c_char, i64, i64, i64]
         L.gemm_f8.argtypes = [ctypes.c_char, ctypes.c_char, vp, vp, vp, i64, i64, i64, i64, i64,
                               i64, f32, f32, vp]
@@ -101,7 +103,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_tn_workspace_bytes.restype = i64
         L.gemm_tn_plan.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, vp]
         for f in (L.gemm_f16_tn, L.gemm_f16, L.gemm_f8_tn, L.gemm_batched_qkt, L.attention_fwd_f16,
-                  L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config, L.gemm_f16_config,
+                  L.gemm_tile_order, L.gemm_block_tile, L.gemm_tn_config, L.gemm_mid_stages,
+                  L.gemm_f16_config,
                   L.gemm_f8, L.gemm_f8_config, L.gemm_f16_tn_splitk, L.gemm_f8_tn_splitk,
                   L.gemm_f16_tn_ws, L.gemm_f8_tn_ws, L.gemm_tn_plan):
             f.restype = ctypes.c_int
@@ -289,6 +292,11 @@ def block_tile() -> int:
 
 CONFIG_NAMES = {0: "256x256", 1: "256x224", 2: "128x128", 3: "skinny-K",
                 4: "256x256 8-wave ping-pong"}
+
+
+def mid_stages(blocks: int, ksteps: int) -> int:
+    """LDS stages of the 128 x 128 kernel's ring for a grid (see gemm_mid_stages)."""
+    return lib().gemm_mid_stages(blocks, ksteps)
 
 
 def tn_config(M: int, N: int, K: int, batch: int = 1, fp8: bool = False) -> int:

@@ -253,6 +253,21 @@ int gemm_block_tile(void);
 int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch);
 
 /*
+ * LDS stages of the K ring the 128 x 128 kernel (configuration 2, and the
+ * partial-product kernel of the split-K calls) uses for a TN grid of `blocks`
+ * blocks of `ksteps` K-steps each (64 fp16 or 128 fp8 elements per step) on
+ * the current HIP device: 4 (a 128 KiB ring, copies three steps ahead, one
+ * block per compute unit) when the grid has at most one block per compute
+ * unit and ksteps >= 8 -- there no second block covers a step whose copies
+ * wait on DRAM -- else 2 (64 KiB, two blocks per compute unit).  The number
+ * of LDS buffers is traded against occupancy and chosen by measurement per
+ * shape ("FP16 GEMM optimisation on AMD RDNA 3 and RDNA 4", step 8 and
+ * section "Further tuning").  -1 for negative arguments.  A query for
+ * measurement labels and tests; results are identical either way.
+ */
+int gemm_mid_stages(int64_t blocks, int64_t ksteps);
+
+/*
  * Kernel configuration gemm_f16 picks for op codes (transa, transb) and an
  * M x N x K problem: for ('T', 'N') that of gemm_tn_config; for the other
  * layouts 0 (256 x 256) or 2 (128 x 128) -- the 224-wide and skinny-K

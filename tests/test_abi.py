@@ -295,6 +295,18 @@ def test_tile_config_selector(M, N, K, batch, fp8, want, monkeypatch):
     assert dg.tn_config(M, N, K, batch, fp8) == want
 
 
+def test_mid_ring_stages():
+    """Ring depth of the 128 x 128 kernel: four stages for grids of at most one
+    block per CU (the 256-CU default of a device-less host) with at least
+    eight K-steps per block, else two."""
+    if torch_device_count() > 0:
+        pytest.skip("expectations assume the 256-CU default of a device-less host")
+    assert dg.mid_stages(256, 8) == 4 and dg.mid_stages(1, 512) == 4
+    assert dg.mid_stages(257, 64) == 2 and dg.mid_stages(256, 7) == 2
+    assert dg.mid_stages(0, 0) == 2
+    assert dg.mid_stages(-1, 8) == -1 and dg.mid_stages(8, -1) == -1
+
+
 def test_tile_config_override(monkeypatch):
     for force, code in (("256", 0), ("224", 1), ("128", 2), ("pingpong", 4)):
         monkeypatch.setenv("DG_GEMM_TILE", force)

@@ -170,3 +170,21 @@ def test_splitk_chooser_doubled_configuration(kind, M, N, K):
     want = oracle.decode(oracle.encode(ref, fmt_out(kind)), fmt_out(kind))
     g = oracle.decode(got, fmt_out(kind))
     assert np.array_equal(g, want), "%d mismatches" % int((g != want).sum())
+
+
+# Split ranges of 8 to 11 K-steps on a grid of one block per CU (the partial
+# kernel's four-stage ring), the last range short, and 7 (two-stage ring).
+@pytest.mark.parametrize("kind,M,N,K,splits", [("f16", 300, 200, 64 * 8 * 6 - 40, 6),
+                                               ("f16", 256, 256, 64 * 9 * 5, 5),
+                                               ("f16", 130, 250, 64 * 10 * 4 + 64 * 3, 5),
+                                               ("f16", 256, 128, 64 * 7 * 8, 8),
+                                               ("f8", 256, 200, 128 * 11 * 3 - 16, 3)])
+def test_splitk_ring_ranges_exact(kind, M, N, K, splits):
+    print("splitk ring %s %dx%dx%d splits %d" % (kind, M, N, K, splits), flush=True)
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=M + N + K)
+    got, canary, ws_ok, _ = run(kind, x, M, N, K, splits)
+    assert canary and ws_ok
+    ref = oracle.gemm_tn(x["A"], x["B"], fmt_in(kind), M, N, K)
+    want = oracle.decode(oracle.encode(ref, fmt_out(kind)), fmt_out(kind))
+    g = oracle.decode(got, fmt_out(kind))
+    assert np.array_equal(g, want), "%d mismatches" % int((g != want).sum())

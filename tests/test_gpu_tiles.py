@@ -89,3 +89,22 @@ def test_selector_sends_2048_cube_to_128_tiles(monkeypatch):
     ref = oracle.gemm_tn_entries(x["A"], x["B"], oracle.FMT_F16, w.K, ms, ns)
     g = oracle.decode(got[ns, ms], oracle.FMT_F16)
     assert np.max(np.abs(g - ref)) / np.max(np.abs(ref)) <= F16_TOL
+
+
+# The 128 x 128 kernel's four-stage ring (grids of at most one block per CU
+# with at least eight K-steps): step counts at and just past the floor, so the
+# loop's last three steps take each of its waits (no, one, two later steps in
+# flight), with a K tail inside the last step; and one count below the floor
+# (the two-stage ring).  fp16 K-steps are 64 elements, fp8 128.
+RING = [("f16", 300, 260, 64 * n - 8) for n in (7, 8, 9, 10, 11, 33)] + \
+       [("f8", 257, 300, 128 * n - 16) for n in (7, 8, 9, 10, 21)]
+
+
+@pytest.mark.parametrize("kind,M,N,K", RING)
+def test_mid_ring_step_counts_exact(force, kind, M, N, K):
+    force("128")
+    print("mid ring %s %dx%dx%d" % (kind, M, N, K), flush=True)
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=M + N + K)
+    got, canary = run_gemm(kind, x, M, N, K, ldc=M + 4)
+    assert canary
+    assert_exact(kind, got, reference(kind, x, M, N, K))

@@ -23,10 +23,12 @@ def rows():
 def test_every_kernel_reported(rows):
     names = {r["kernel"] for r in rows}
     for want in ("gemm_tn_kernel<0, 8, false, false>", "gemm_tn_kernel<1, 8, false, false>",
-                 "gemm_tn_skinny_kernel<0>", "gemm_tn_mid_kernel<0, false, false, false>",
+                 "gemm_tn_skinny_kernel<0>", "gemm_tn_mid_kernel<0, false, false, false, 2>",
+                 "gemm_tn_mid_kernel<0, false, false, false, 4>",
+                 "gemm_tn_mid_kernel<1, false, false, true, 4>",
                  "gemm_splitk_reduce_kernel<0>", "attention_fwd_kernel"):
         assert any(want in n for n in names), want
-    assert len(rows) >= 27
+    assert len(rows) >= 31
 
 
 def test_no_scratch_anywhere(rows):
@@ -41,3 +43,18 @@ def test_big_tiles_hold_accumulators_in_agprs(rows):
         if "gemm_tn_kernel<" in r["kernel"]:
             assert int(r["AGPRs"]) >= 224 and r["Occupancy [waves/SIMD]"] == "1", r
             assert int(r["LDS Size [bytes/block]"]) == 131072, r
+
+
+def test_mid_kernel_rings_fit_their_occupancy(rows):
+    """The 128 x 128 kernel: two-stage ring (64 KiB) at two blocks per CU, the
+    four-stage ring (128 KiB) for grids of one block per CU."""
+    seen = set()
+    for r in rows:
+        if "gemm_tn_mid_kernel<" in r["kernel"]:
+            stages = r["kernel"].split(",")[-1].split(">")[0].strip()
+            lds = int(r["LDS Size [bytes/block]"])
+            assert (stages, lds) in (("2", 65536), ("4", 131072)), r
+            if stages == "2":
+                assert int(r["Occupancy [waves/SIMD]"]) >= 2, r
+            seen.add(stages)
+    assert seen == {"2", "4"}
