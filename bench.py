@@ -94,7 +94,9 @@ def kernel_name(w):
         bmn = "true" if layout[1] == "T" else "false"
         cfg_of = dg.f8_config if w.kind == "f8" else dg.f16_config
         if cfg_of(layout[0], layout[1], w.M, w.N, w.K) == 2:
-            return "gemm_tn_mid_kernel<%d, %s, %s, false, 2>" % (kind, amn, bmn)
+            nk = (w.K + kstep - 1) // kstep
+            return "gemm_tn_mid_kernel<%d, %s, %s, false, %d>" % (
+                kind, amn, bmn, dg.mid_stages(tiles128(w.M, w.N), nk))
         return "gemm_tn_kernel<%d, 8, %s, %s>" % (kind, amn, bmn)
     fp8 = w.kind == "f8"
     if w.extra.get("splitk"):

@@ -2036,11 +2036,15 @@ static int launch_layout(char ta, char tb, const Problem &pr, hipStream_t stream
   static const kernel_t mids[3] = {gemm_tn_mid_kernel<KIND, true, false>,
                                    gemm_tn_mid_kernel<KIND, false, true>,
                                    gemm_tn_mid_kernel<KIND, true, true>};
+  static const kernel_t mids4[3] = {gemm_tn_mid_kernel<KIND, true, false, false, 4>,
+                                    gemm_tn_mid_kernel<KIND, false, true, false, 4>,
+                                    gemm_tn_mid_kernel<KIND, true, true, false, 4>};
   static const kernel_t bigs[3] = {gemm_tn_kernel<KIND, 8, true, false>,
                                    gemm_tn_kernel<KIND, 8, false, true>,
                                    gemm_tn_kernel<KIND, 8, true, true>};
   const int li = amn && bmn ? 2 : amn ? 0 : 1;
-  const kernel_t k = mid ? mids[li] : bigs[li];
+  const bool deep = mid && mid_deep_ring(blocks, (pr.K + T::kstep - 1) / T::kstep);
+  const kernel_t k = deep ? mids4[li] : mid ? mids[li] : bigs[li];
   hipLaunchKernelGGL(k, grid, block, 0, stream, p);
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }

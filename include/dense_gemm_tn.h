@@ -253,10 +253,10 @@ int gemm_block_tile(void);
 int gemm_tn_config(int fp8, int64_t M, int64_t N, int64_t K, int64_t batch);
 
 /*
- * LDS stages of the K ring the 128 x 128 kernel (configuration 2, and the
- * partial-product kernel of the split-K calls) uses for a TN grid of `blocks`
- * blocks of `ksteps` K-steps each (64 fp16 or 128 fp8 elements per step) on
- * the current HIP device: 4 (a 128 KiB ring, copies three steps ahead, one
+ * LDS stages of the K ring the 128 x 128 kernel (configuration 2 in every
+ * layout, and the partial-product kernel of the split-K calls) uses for a grid
+ * of `blocks` blocks of `ksteps` K-steps each (64 fp16 or 128 fp8 elements per
+ * step) on the current HIP device: 4 (a 128 KiB ring, copies three steps ahead, one
  * block per compute unit) when the grid has at most one block per compute
  * unit and ksteps >= 8 -- there no second block covers a step whose copies
  * wait on DRAM -- else 2 (64 KiB, two blocks per compute unit).  The number
