@@ -201,3 +201,22 @@ def test_attention_full_workload_sampled_rows():
         rows = np.unique(np.concatenate([[0, 127, 128, 4095], rng.integers(0, w.M, 28)]))
         check_head(got[h], inp["Q"][h], inp["K"][h], inp["Vt"][h], w.N, rows, scale,
                    "head %d" % h)
+
+
+def test_attention_million_keys():
+    """2^20 + 37 keys per head (16 385 key blocks, the last cut by N; K and Vt
+    heads of 256 MiB, so each block's copy offsets span far past 2^24 bytes)
+    and 300 queries over two heads: sampled rows of both heads against the
+    oracle, every output inside the range of V."""
+    batch, M, N = 2, 300, (1 << 20) + 37
+    print("attention %d keys" % N, flush=True)
+    inp = inputs.make_shape("attn", M, N, D, seed=21, batch=batch)
+    scale = 1.0 / math.sqrt(D)
+    got = run(inp, scale)
+    assert np.all(np.isfinite(got))
+    vt = inp["Vt"].astype(np.float32)
+    assert np.all(got >= vt.min(axis=2)[:, None, :] - 1e-2)
+    assert np.all(got <= vt.max(axis=2)[:, None, :] + 1e-2)
+    rows = np.array([0, 1, 127, 128, 255, 256, 299])
+    for h in range(batch):
+        check_head(got[h], inp["Q"][h], inp["K"][h], inp["Vt"][h], N, rows, scale, "head %d" % h)
