@@ -45,8 +45,10 @@
 //   all of K fits one LDS row, so there is no K pipeline; blocks walk a column
 //   of 128 x 128 tiles with B's strip resident, bound by writing C.
 //
-// gemm_tn_mid_kernel: 128 x 128 tiles, two blocks per CU, for grids the
-//   256-wide tiles cannot fill.
+// gemm_tn_mid_kernel: 128 x 128 tiles, two blocks per CU with a two-stage
+//   LDS ring, for grids the 256-wide tiles cannot fill; on grids of at most
+//   one block per CU (and at least eight K-steps) one block per CU with a
+//   four-stage ring, whose copies run three steps ahead of the products.
 //
 // Split-K (gemm_f16_tn_splitk, gemm_f8_tn_splitk): for few output tiles and a
 //   long K, the 128 x 128 kernel with SPLIT multiplies one K range per block
