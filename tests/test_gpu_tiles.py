@@ -108,3 +108,27 @@ def test_mid_ring_step_counts_exact(force, kind, M, N, K):
     got, canary = run_gemm(kind, x, M, N, K, ldc=M + 4)
     assert canary
     assert_exact(kind, got, reference(kind, x, M, N, K))
+
+
+def test_mid_ring_batched_heads_exact(force):
+    """Strided heads through the four-stage ring (three 300 x 300 heads, a
+    1024-deep contraction: 27 blocks of 16 K-steps), head gaps untouched."""
+    import torch
+    from test_gpu_parity import CANARY16, DEV
+    force("128")
+    H, M, N, D = 3, 300, 300, 1024
+    assert dg.mid_stages(H * 9, D // 64) == 4 or torch.cuda.get_device_properties(0).multi_processor_count < 27
+    x = inputs.make_shape("qkt", M, N, D, dist="pm1", seed=17, batch=H)
+    q = torch.from_numpy(x["Q"]).to(DEV)
+    k = torch.from_numpy(x["K"]).to(DEV)
+    ld, stride = M + 4, N * (M + 4) + 40
+    s = torch.full((H * stride,), CANARY16, dtype=torch.int32, device=DEV).to(torch.int16)
+    dg.gemm_batched_qkt(q, k, s, H, M, N, D, D, D, ld, M * D, N * D, stride)
+    torch.cuda.synchronize()
+    host = s.cpu().numpy().view(np.uint16)
+    for h in range(H):
+        blk = host[h * stride:(h + 1) * stride]
+        body = blk[:N * ld].reshape(N, ld)
+        assert np.all(body[:, M:] == CANARY16) and np.all(blk[N * ld:] == CANARY16)
+        ref = oracle.gemm_tn(x["Q"][h], x["K"][h], oracle.FMT_F16, M, N, D)
+        assert_exact("qkt", np.ascontiguousarray(body[:, :M]), ref)
