@@ -842,10 +842,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   constexpr int kBarSlot = (T::subs - 1) * kQ + kBarQ;
   constexpr int kAfter = T::subs * kQ - kBarSlot;  // window slots in the barrier's step
   constexpr int kCopies = 8 + (BMN ? 8 : NTN);     // copy instructions per wave per step
-  // Copy window in slots (about 1000 cycles of MFMA for either), chosen by
-  // measurement (fp16 4096^3, fp8 8192^3), capped by the slots before the
-  // next step's barrier.
-  constexpr int kWin0 = (KIND == kF16) ? 64 : 32;
+  // Copy window in slots (fp16: 64 slots of 16-cycle products, fp8: 48 of
+  // 32-cycle ones), chosen by measurement (fp16 4096^3, fp8 8192^3), capped
+  // by the slots before the next step's barrier.
+  constexpr int kWin0 = (KIND == kF16) ? 64 : 48;
   constexpr int kWin = kWin0 < kAfter + kBarQ ? kWin0 : kAfter + kBarQ;
   static_assert(kWin >= kCopies && kWin - kAfter <= kBarQ, "copy window");
   auto first_copy = [](int x) { return (x * kCopies + kWin - 1) / kWin; };
