@@ -97,16 +97,20 @@ def kernel_name(w):
             nk = (w.K + kstep - 1) // kstep
             return "gemm_tn_mid_kernel<%d, %s, %s, false, %d>" % (
                 kind, amn, bmn, dg.mid_stages(tiles128(w.M, w.N), nk))
-        return "gemm_tn_kernel<%d, 8, %s, %s>" % (kind, amn, bmn)
+        return "gemm_tn_kernel<%d, 8, %s, %s, false>" % (kind, amn, bmn)
     fp8 = w.kind == "f8"
     if w.extra.get("splitk"):
         s = dg.splitk_choose(w.M, w.N, w.K, fp8=fp8)
         if s > 1:
             return mid(w.M, w.N, 1, w.K, split=True, splits=s)
 
+    # The 256-row kernel with whole K-steps (K a multiple of the K-step) is the
+    # instantiation with fixed copy offsets (last template flag).
+    kf = "true" if w.K % (64 if kind == 0 else 128) == 0 else "false"
+
     def names(cfg, M, N):
-        return {0: "gemm_tn_kernel<%d, 8, false, false>" % kind,
-                1: "gemm_tn_kernel<%d, 7, false, false>" % kind,
+        return {0: "gemm_tn_kernel<%d, 8, false, false, %s>" % (kind, kf),
+                1: "gemm_tn_kernel<%d, 7, false, false, %s>" % (kind, kf),
                 3: "gemm_tn_skinny_kernel<%d>" % kind,
                 4: "gemm_tn_pp_kernel<%d>" % kind}.get(cfg) or mid(M, N, w.batch, w.K)
 

@@ -353,6 +353,12 @@ __device__ __forceinline__ void dma16(const v4u32 &r, uint32_t voff, uint32_t ld
                :: "v"(voff), "s"(r), "{m0}"(lds) : "memory");
 }
 
+// One 16-byte-per-lane buffer load into LDS (64 lanes fill 1 KiB at `lds`).
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t r, lds_void_t *lds,
+                                           uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, voff, 0, 0, 0);
+}
+
 // M/N-contiguous operands of the 256 x 256 kernel (A of an 'N' op, B of a 'T'
 // op) are staged as they lie: a stage strip is T::kstep K-rows of the block's
 // 256 columns (fp16: 64 K-rows of 512 B; fp8: 128 K-rows of 256 B), the
@@ -627,9 +633,11 @@ static_assert(extra_slot<8>(8) == 25 && extra_slot<7>(0) == 8 && extra_slot<7>(3
 
 // NTN = 16-column MFMA tiles per wave along N: 8 (256 x 256 block tiles) or 7
 // (256 x 224, which the host picks when it packs the grid into fewer rounds
-// of one block per CU).
-template <int KIND, int NTN, bool AMN, bool BMN>
+// of one block per CU).  KF (TN only): K is a multiple of the K-step, so no
+// step has a K tail (see the copy offsets below).
+template <int KIND, int NTN, bool AMN, bool BMN, bool KF>
 __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
+  static_assert(!KF || (!AMN && !BMN), "whole K-steps: TN only");
   typedef Traits<KIND> T;
   typedef Mn<KIND> G;                    // M/N-contiguous staging geometry
   constexpr int kTileN = 2 * 16 * NTN;   // block tile width (columns of B / C)
@@ -677,6 +685,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   const uint32_t qs_a = (uint32_t)((AMN ? 1 : 32) * p.lda_b);
   const uint32_t qs_b = (uint32_t)((BMN ? 1 : 32) * p.ldb_b);
   const int kchunk = gchunk * (16 / T::es);           // K offset of the chunk in a step
+  // With whole K-steps (KF) every lane's chunk is inside K in every step
+  // inside the matrix, so the lane offsets of the step's copies are the same
+  // in every step: they are formed once and held in registers, and the K loop
+  // issues its copies with no address arithmetic (steps outside the matrix
+  // get an empty descriptor instead of out-of-range lane offsets).  The empty
+  // asm statements keep the compiler from re-deriving them inside the loop.
+  uint32_t cva[8], cvb[8];
+  if constexpr (KF) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      cva[q] = voff_a + (uint32_t)q * qs_a;
+      asm volatile("" : "+v"(cva[q]));
+    }
+#pragma unroll
+    for (int q = 0; q < NTN; ++q) {
+      cvb[q] = voff_b + (uint32_t)q * qs_b;
+      asm volatile("" : "+v"(cvb[q]));
+    }
+  }
 
   // Fragment geometry: an MFMA operand covers 16 rows; lane l reads row l % 16
   // of the tile and serves K group g = l / 16 of the instruction.  fp16
@@ -697,6 +724,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     a_off[x] = lo + wm * kWaveTile * kRowBytes;
     b_off[x] = lo + kStageBytes + wn * S::WN * kRowBytes;
   }
+  // The same offsets for each stage, held in registers: a fragment read is
+  // then one register plus an immediate offset below 64 KiB (the stage base
+  // alone would overflow the immediate for stage 1).
+  uint32_t a_st[2][4], b_st[2][4];
+#pragma unroll
+  for (int st = 0; st < 2; ++st)
+#pragma unroll
+    for (int x = 0; x < T::subs * T::reads; ++x) {
+      a_st[st][x] = a_off[x] + (uint32_t)(st * 2 * kStageBytes);
+      b_st[st][x] = b_off[x] + (uint32_t)(st * 2 * kStageBytes);
+      if constexpr (!AMN) asm volatile("" : "+v"(a_st[st][x]));
+      if constexpr (!BMN) asm volatile("" : "+v"(b_st[st][x]));
+    }
   // M/N-contiguous fragments.  fp16: lane (rl, grp) reads K-row 8 grp + rl / 4
   // at elements 4 (rl % 4) .. +3 of the 16-wide tile whose first chunk is c0,
   // i.e. slot (c0 + (rl % 4) / 2) ^ key, byte 8 (rl % 2); c0 is even and the
@@ -713,8 +753,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   constexpr int kTileChunks = 16 * T::es / 16;
   typedef typename T::frag_t frag_t;
   constexpr int kTileBytes = MT * kRowBytes;      // LDS bytes between MFMA tiles
-  // Fragment g of A (16 rows at wave row 16 g) and j of B, sub-step s, from the
-  // stage at `st`.
+  // Fragment g of A (16 rows at wave row 16 g) and j of B, sub-step s, from
+  // stage `stg`.
   auto mn_read = [&](lds_cptr strip, int c0, int s) -> frag_t {
     const uint32_t off = mn_lane ^ (uint32_t)(16 * c0);
     if constexpr (KIND == kF16)
@@ -722,17 +762,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     else
       return mn_frag8<Mn<kF8>::row_bytes>(strip, off);
   };
-  auto frag_a = [&](lds_cptr st, int g, int s) -> frag_t {
+  auto frag_a = [&](int stg, int g, int s) -> frag_t {
     if constexpr (AMN)
-      return mn_read(st, kTileChunks * (kWaveTile / 16 * wm + g), s);
+      return mn_read((lds_cptr)smem + stg * 2 * kStageBytes,
+                     kTileChunks * (kWaveTile / 16 * wm + g), s);
     else
-      return read_frag<KIND>(st + g * kTileBytes, a_off, s);
+      return read_frag<KIND>((lds_cptr)smem + g * kTileBytes, a_st[stg], s);
   };
-  auto frag_b = [&](lds_cptr st, int j, int s) -> frag_t {
+  auto frag_b = [&](int stg, int j, int s) -> frag_t {
     if constexpr (BMN)
-      return mn_read(st + kStageBytes, kTileChunks * (S::WN / 16 * wn + j), s);
+      return mn_read((lds_cptr)smem + stg * 2 * kStageBytes + kStageBytes,
+                     kTileChunks * (S::WN / 16 * wn + j), s);
     else
-      return read_frag<KIND>(st + j * kTileBytes, b_off, s);
+      return read_frag<KIND>((lds_cptr)smem + j * kTileBytes, b_st[stg], s);
   };
 
   typename S::acc_t acc[NTM][NTN];
@@ -746,9 +788,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   // One loop iteration runs two K-steps, stage 0 then stage 1.  An odd K-step
   // count gets one leading step whose chunks all read as zero (adding exact
   // zeros).
-  const int64_t nk = (p.K + T::kstep - 1) / T::kstep;
-  const int64_t pad = nk & 1;
-  const int64_t nk2 = nk + pad;
+  // (32-bit step arithmetic: the host keeps K * es below 2^31.)
+  const int nk = (int)((p.K + T::kstep - 1) / T::kstep);
+  const int pad = nk & 1;
+  const int nk2 = nk + pad;
+  const int Ki = (int)p.K;
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   // Copy plan of step t, in three parts so the main loop can spread its
   // instructions over three MFMA slots.  Steps outside the matrix (the leading
@@ -760,13 +804,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     int stage;
     int64_t k0;    // first K index of the step (M/N-contiguous operands)
   };
-  auto step_scalars = [&](int64_t t) {
-    const int64_t k0 = (t - pad) * T::kstep;
+  auto step_scalars = [&](int t) {
+    const int k0 = (t - pad) * T::kstep;
     const bool inside = (k0 >= 0) && (t < nk2);
-    const int64_t rem = p.K - k0;
+    const int rem = Ki - k0;
     StepScalars u;
     u.kb = inside ? (uint32_t)(k0 * T::es) : 0u;
-    u.left = !inside ? 0 : (rem >= T::kstep ? T::kstep : (int)rem);
+    u.left = !inside ? 0 : (rem >= T::kstep ? T::kstep : rem);
     u.stage = (int)(t & 1);
     if constexpr (AMN || BMN) u.k0 = inside ? k0 : -1;
     return u;
@@ -792,19 +836,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
       c.la = st + (AMN ? G::wave_row(wave) * G::row_bytes : wave * 1024);
       c.lb = st + kStageBytes + (BMN ? G::wave_row(wave) * G::row_bytes : wave * 1024);
     } else {
-      c.ra = make_rsrc(Ab + u.kb, rec_a - u.kb);
-      c.rb = make_rsrc(Bb + u.kb, rec_b - u.kb);
+      c.ra = make_rsrc(Ab + u.kb, KF && u.left == 0 ? 0u : rec_a - u.kb);
+      c.rb = make_rsrc(Bb + u.kb, KF && u.left == 0 ? 0u : rec_b - u.kb);
       lds_u8 *st = (lds_u8 *)smem + u.stage * 2 * kStageBytes + wave * 1024;
       c.la = st;
       c.lb = st + kStageBytes;
     }
   };
   auto step_lanes = [&](const StepScalars &u, Copy &c) {
+    if constexpr (KF) return;   // the fixed lane offsets cva / cvb
     const bool valid = kchunk < u.left;   // this lane's chunk is inside K
     c.va = (AMN || valid) ? voff_a : kOob;
     c.vb = (BMN || valid) ? voff_b : kOob;
   };
-  auto step_copy = [&](int64_t t) {
+  // Issue copy d of a step (d < 8: A, else B).
+  auto issue = [&](const Copy &c, int d) {
+    if constexpr (KF) {
+      if (d < 8)
+        lds_copy16(c.ra, (lds_void_t *)(c.la + d * 4096), cva[d]);
+      else
+        lds_copy16(c.rb, (lds_void_t *)(c.lb + (d - 8) * 4096), cvb[d - 8]);
+    } else {
+      copy_one<AMN, BMN, KIND>(c, d, qs_a, qs_b);
+    }
+  };
+  auto step_copy = [&](int t) {
     const StepScalars u = step_scalars(t);
     Copy c;
     step_rsrc(u, c);
@@ -859,19 +915,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
     // only (loads complete in order) and publish it.
     const Copy c0 = step_copy(0);
 #pragma unroll
-    for (int d = 0; d < kCopies; ++d) copy_one<AMN, BMN, KIND>(c0, d, qs_a, qs_b);
+    for (int d = 0; d < kCopies; ++d) issue(c0, d);
     const Copy c1 = step_copy(1);
 #pragma unroll
-    for (int d = 0; d < kPost; ++d) copy_one<AMN, BMN, KIND>(c1, d, qs_a, qs_b);
+    for (int d = 0; d < kPost; ++d) issue(c1, d);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPost));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    lds_cptr st0 = (lds_cptr)smem;
 #pragma unroll
-    for (int j = 0; j < NTN; ++j) fb[0][j] = frag_b(st0, j, 0);
+    for (int j = 0; j < NTN; ++j) fb[0][j] = frag_b(0, j, 0);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) fa[g] = frag_a(st0, g, 0);
+    for (int g = 0; g < 8; ++g) fa[g] = frag_a(0, g, 0);
   }
   // cn: copies of step t + 1 (its last ones are issued early in step t);
   // cnn: step t + 2's, planned in slots kPlan .. kPlan + 2 of step t.
@@ -880,17 +935,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   constexpr int kPlan = kBarSlot - 6;
   static_assert(kPlan >= 0 && kPlan >= kWin - kAfter, "plan after the last copy of step t + 1");
   clock_mark(clock_ptr<Params>(), kClockLoop, wave);
-  for (int64_t t0 = 0; t0 < nk2; t0 += 2) {
+  for (int t0 = 0; t0 < nk2; t0 += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {            // K-step t0 + h lives in stage h
-      const int64_t t = t0 + h;
-      lds_cptr cur = (lds_cptr)smem + h * 2 * kStageBytes;
-      lds_cptr nxt = (lds_cptr)smem + (1 - h) * 2 * kStageBytes;
+      const int t = t0 + h;
 #pragma unroll
       for (int s = 0; s < T::subs; ++s) {
         const bool last = (s == T::subs - 1);
         const int par = (h * T::subs + s) & 1;  // sub-step parity
-        lds_cptr src = last ? nxt : cur;       // where the next sub-step's data is
+        const int src = last ? 1 - h : h;      // stage of the next sub-step's data
         const int s_n = last ? 0 : s + 1;
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
@@ -911,10 +964,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
             if (slot == kPlan + 2) step_lanes(un, cnn);
             if (slot < kWin - kAfter) {
               const int x = slot + kAfter;     // at most one copy per slot
-              if (first_copy(x) < first_copy(x + 1)) copy_one<AMN, BMN, KIND>(cn, first_copy(x), qs_a, qs_b);
+              if (first_copy(x) < first_copy(x + 1)) issue(cn, first_copy(x));
             } else if (slot >= kBarSlot && slot - kBarSlot < kWin) {
               const int x = slot - kBarSlot;
-              if (first_copy(x) < first_copy(x + 1)) copy_one<AMN, BMN, KIND>(cnn, first_copy(x), qs_a, qs_b);
+              if (first_copy(x) < first_copy(x + 1)) issue(cnn, first_copy(x));
             }
             if (g == 7 && par == 1) acc[g][j] = mma(fx, fb[par][j], acc[g][j]);
             else acc[g][j] = mma(fa[g], fb[par][j], acc[g][j]);
@@ -950,10 +1003,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   clock_mark(clock_ptr<Params>(), kClockEnd, wave);
 }
 
-template __global__ void gemm_tn_kernel<kF16, 8, false, false>(Params);
-template __global__ void gemm_tn_kernel<kF16, 7, false, false>(Params);
-template __global__ void gemm_tn_kernel<kF8, 8, false, false>(Params);
-template __global__ void gemm_tn_kernel<kF8, 7, false, false>(Params);
+template __global__ void gemm_tn_kernel<kF16, 8, false, false, false>(Params);
+template __global__ void gemm_tn_kernel<kF16, 7, false, false, false>(Params);
+template __global__ void gemm_tn_kernel<kF8, 8, false, false, false>(Params);
+template __global__ void gemm_tn_kernel<kF8, 7, false, false, false>(Params);
+template __global__ void gemm_tn_kernel<kF16, 8, false, false, true>(Params);
+template __global__ void gemm_tn_kernel<kF16, 7, false, false, true>(Params);
+template __global__ void gemm_tn_kernel<kF8, 8, false, false, true>(Params);
+template __global__ void gemm_tn_kernel<kF8, 7, false, false, true>(Params);
 
 // ----------------------------------------------------------------- skinny K
 // Kernels for K * es <= 256 bytes (the QK^T shape: K = head dim 128): the whole
@@ -1954,12 +2011,16 @@ static int launch_cfg(const Problem &pr, Config cfg, hipStream_t stream) {
   else if (mid)
     hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, p);
-  else if (ntn == 8)
-    hipLaunchKernelGGL((gemm_tn_kernel<KIND, 8, false, false>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm_tn_kernel<KIND, 7, false, false>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, p);
+  else {
+    // Whole K-steps take the kernel with fixed copy offsets.
+    const bool kf = pr.K % T::kstep == 0;
+    typedef void (*kernel_t)(Params);
+    const kernel_t k = ntn == 8 ? (kf ? gemm_tn_kernel<KIND, 8, false, false, true>
+                                      : gemm_tn_kernel<KIND, 8, false, false, false>)
+                                : (kf ? gemm_tn_kernel<KIND, 7, false, false, true>
+                                      : gemm_tn_kernel<KIND, 7, false, false, false>);
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
@@ -2041,9 +2102,9 @@ static int launch_layout(char ta, char tb, const Problem &pr, hipStream_t stream
   static const kernel_t mids4[3] = {gemm_tn_mid_kernel<KIND, true, false, false, 4>,
                                     gemm_tn_mid_kernel<KIND, false, true, false, 4>,
                                     gemm_tn_mid_kernel<KIND, true, true, false, 4>};
-  static const kernel_t bigs[3] = {gemm_tn_kernel<KIND, 8, true, false>,
-                                   gemm_tn_kernel<KIND, 8, false, true>,
-                                   gemm_tn_kernel<KIND, 8, true, true>};
+  static const kernel_t bigs[3] = {gemm_tn_kernel<KIND, 8, true, false, false>,
+                                   gemm_tn_kernel<KIND, 8, false, true, false>,
+                                   gemm_tn_kernel<KIND, 8, true, true, false>};
   const int li = amn && bmn ? 2 : amn ? 0 : 1;
   const bool deep = mid && mid_deep_ring(blocks, (pr.K + T::kstep - 1) / T::kstep);
   const kernel_t k = deep ? mids4[li] : mid ? mids[li] : bigs[li];

@@ -22,7 +22,10 @@ def rows():
 
 def test_every_kernel_reported(rows):
     names = {r["kernel"] for r in rows}
-    for want in ("gemm_tn_kernel<0, 8, false, false>", "gemm_tn_kernel<1, 8, false, false>",
+    for want in ("gemm_tn_kernel<0, 8, false, false, true>",
+                 "gemm_tn_kernel<1, 8, false, false, true>",
+                 "gemm_tn_kernel<0, 8, false, false, false>",
+                 "gemm_tn_kernel<1, 8, false, false, false>",
                  "gemm_tn_skinny_kernel<0>", "gemm_tn_mid_kernel<0, false, false, false, 2>",
                  "gemm_tn_mid_kernel<0, false, false, false, 4>",
                  "gemm_tn_mid_kernel<1, false, false, true, 4>",
