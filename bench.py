@@ -104,13 +104,13 @@ def kernel_name(w):
         if s > 1:
             return mid(w.M, w.N, 1, w.K, split=True, splits=s)
 
-    # The 256-row kernel with whole K-steps (K a multiple of the K-step) is the
-    # instantiation with fixed copy offsets (last template flag).
+    # The 256-row TN kernel with whole K-steps (K a multiple of the K-step) is
+    # the instantiation with fixed copy offsets (last template flag).
     kf = "true" if w.K % (64 if kind == 0 else 128) == 0 else "false"
 
     def names(cfg, M, N):
-        return {0: "gemm_tn_kernel<%d, 8, false, false, %s>" % (kind, kf),
-                1: "gemm_tn_kernel<%d, 7, false, false, %s>" % (kind, kf),
+        return {0: "gemm_tn_ring_kernel<%d, 8, %s>" % (kind, kf),
+                1: "gemm_tn_ring_kernel<%d, 7, %s>" % (kind, kf),
                 3: "gemm_tn_skinny_kernel<%d>" % kind,
                 4: "gemm_tn_pp_kernel<%d>" % kind}.get(cfg) or mid(M, N, w.batch, w.K)
 

@@ -8,7 +8,8 @@
 // Kernel design.  Four kernels, each with fp16 and fp8 instantiations and an
 // optional head index; a host selector picks one per problem:
 //
-// gemm_tn_kernel (K * es > 256 bytes):
+// gemm_tn_ring_kernel / gemm_tn_kernel (K * es > 256 bytes; TN calls take the
+// first, the other op-code layouts the second):
 //   * 256 x 256 output tile per workgroup, 4 waves (one per SIMD), each wave owns
 //     a 128 x 128 quarter as 8 x 8 MFMA tiles of 16 x 16 (256 accumulator
 //     registers per lane) -- the 4-wave layout of the MI355X FP8 GEMM page,
@@ -16,7 +17,9 @@
 //     (v_mfma_f32_16x16x32_f16, v_mfma_f32_16x16x128_f8f6f4), which sustain a
 //     higher clock under load than the 32x32 shapes.
 //   * A K-step moves 128 bytes of K per row (64 fp16 or 128 fp8 elements):
-//     256 rows x 128 B of A and of B per stage, two stages in LDS (128 KiB).
+//     a 256-row x 128 B strip of A and of B.  TN: three A strips and two B
+//     strips in LDS (160 KiB), so A's copies are issued two steps ahead and
+//     B's one; other layouts: two [A | B] stages (128 KiB).
 //   * Global -> LDS copies are buffer loads that write LDS directly (no VGPR
 //     staging).  The buffer resource descriptor makes out-of-range reads return
 //     zero, which handles M and N tails ("FP16 GEMM optimisation ...", Step 4);
@@ -30,7 +33,10 @@
 //     (the prefetch interleaving of "FP16 GEMM optimisation ...", Step 7, and
 //     the MFMA / ds_read interleave of the MI355X FP8 GEMM page): fragments of
 //     the next sub-step are read while the current one computes, one barrier
-//     per K-step; sched_barrier pins the order.
+//     per K-step; sched_barrier pins the order.  With K a multiple of the step
+//     the copies' lane offsets are fixed registers and fragment reads use a
+//     register plus an immediate: the K loop issues no vector ALU instruction
+//     besides its MFMAs.
 //   * Block ids are remapped so each XCD (workgroups are dealt round-robin over
 //     the 8 XCDs) receives a contiguous range of tiles, and that range is walked
 //     in the grouped order of "FP16 GEMM optimisation ...", Step 6 (groups of 8
@@ -1003,6 +1009,306 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_tn_kernel(Params p) {
   clock_mark(clock_ptr<Params>(), kClockEnd, wave);
 }
 
+// ------------------------------------------------- 256-row TN kernel, 3 + 2 ring
+// gemm_tn_ring_kernel: the TN form of the 256 x 256 (or 256 x 224) tile with
+// the LDS split into a three-stage ring for A and a two-stage ring for B
+// (5 x 32 KiB, all of the 160 KiB a gfx950 workgroup may hold).  After the
+// barrier of step t a wave issues B's copies of step t + 2 and then A's of
+// step t + 3: B's land within the step after their issue, A's have two steps,
+// and the barrier waits only until B's copies of step t + 1 are in (the A
+// copies issued after them stay in flight).  With two [A | B] stages every
+// copy had to land within one step of its issue, and with operands coming
+// from HBM the barrier waited for them (fp8 8192^3: a fifth of the loop).
+// Tile, waves, MFMA schedule, fragment reads, swizzle, tile order and
+// epilogue are those of gemm_tn_kernel.
+template <int KIND, int NTN, bool KF>
+__global__ __launch_bounds__(kThreads, 1) void gemm_tn_ring_kernel(Params p) {
+  typedef Traits<KIND> T;
+  constexpr int kTileN = 2 * 16 * NTN;
+  constexpr int kHalf = kStageBytes;            // one 256-row strip of one operand
+  constexpr int kBBase = 3 * kHalf;             // B stages follow A's three
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[5 * kHalf];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int head, tm, tn;
+  tile_of_block<int>((int)blockIdx.x, (int)gridDim.x, p.tiles_m, p.tiles_n, &head, &tm, &tn,
+                     p.order);
+  const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTileN;
+  clock_mark(clock_ptr<Params>(), kClockStart, wave);
+
+  const uint8_t *Ab = p.A + head * p.stride_a_b + m0 * p.lda_b;
+  const uint8_t *Bb = p.B + head * p.stride_b_b + n0 * p.ldb_b;
+  uint8_t *Cb = p.C + head * p.stride_c_b;
+  const int64_t rows_a = (p.M - m0) < kTile ? (p.M - m0) : kTile;
+  const int64_t rows_b = (p.N - n0) < kTileN ? (p.N - n0) : kTileN;
+  const uint32_t kbytes = (uint32_t)(p.K * T::es);
+  const uint32_t rec_a = (uint32_t)((rows_a - 1) * p.lda_b) + kbytes;
+  const uint32_t rec_b = (uint32_t)((rows_b - 1) * p.ldb_b) + kbytes;
+
+  // Copies (as in gemm_tn_kernel): load q of wave w fills strip rows
+  // 32q + 8w + (l >> 3), slot l & 7, with the global chunk the swizzle keeps
+  // there; with whole K-steps the lane offsets are fixed (cva, cvb).
+  const int crow = 8 * wave + (lane >> 3);
+  const int gchunk = (lane & 7) ^ ((crow >> 1) & 7);
+  const uint32_t voff_a = (uint32_t)(crow * p.lda_b) + gchunk * 16;
+  const uint32_t voff_b = (uint32_t)(crow * p.ldb_b) + gchunk * 16;
+  const uint32_t qs_a = (uint32_t)(32 * p.lda_b);
+  const uint32_t qs_b = (uint32_t)(32 * p.ldb_b);
+  const int kchunk = gchunk * (16 / T::es);
+  uint32_t cva[8], cvb[8];
+  if constexpr (KF) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      cva[q] = voff_a + (uint32_t)q * qs_a;
+      asm volatile("" : "+v"(cva[q]));
+    }
+#pragma unroll
+    for (int q = 0; q < NTN; ++q) {
+      cvb[q] = voff_b + (uint32_t)q * qs_b;
+      asm volatile("" : "+v"(cvb[q]));
+    }
+  }
+
+  // Fragment offsets within a strip (see gemm_tn_kernel); B's per stage
+  // (compile-time stage of the unrolled step pair), A's rebased each step on
+  // the step's A stage (a runtime value, t mod 3).
+  typedef AccShape<KIND, NTN> S;
+  constexpr int MT = S::MT, NTM = S::NTM;
+  constexpr int kX = T::subs * T::reads;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int rl = lane % MT, grp = lane / MT;
+  uint32_t a_off[4], b_st[2][4];   // read_frag takes four offsets (kX used)
+#pragma unroll
+  for (int x = 0; x < kX; ++x) {
+    const int chunk = (x / T::reads) * (8 / T::subs) + grp + 4 * (x % T::reads);
+    const uint32_t lo = (uint32_t)(rl * kRowBytes + ((chunk ^ ((rl >> 1) & 7)) * 16));
+    a_off[x] = lo + wm * kWaveTile * kRowBytes;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      b_st[st][x] = lo + (uint32_t)(kBBase + st * kHalf) + wn * S::WN * kRowBytes;
+      asm volatile("" : "+v"(b_st[st][x]));
+    }
+  }
+  constexpr int kTileBytes = MT * kRowBytes;
+  typedef typename T::frag_t frag_t;
+  uint32_t a_cur[4], a_nxt[4];   // A offsets of the current and the next step
+  auto a_rebase = [&](uint32_t (&dst)[4], int stage) {
+#pragma unroll
+    for (int x = 0; x < kX; ++x) dst[x] = a_off[x] + (uint32_t)stage * kHalf;
+  };
+  auto frag_a = [&](const uint32_t (&base)[4], int g, int s) -> frag_t {
+    return read_frag<KIND>((lds_cptr)smem + g * kTileBytes, base, s);
+  };
+  auto frag_b = [&](int stg, int j, int s) -> frag_t {
+    return read_frag<KIND>((lds_cptr)smem + j * kTileBytes, b_st[stg], s);
+  };
+
+  typename S::acc_t acc[NTM][NTN];
+#pragma unroll
+  for (int i = 0; i < NTM; ++i)
+#pragma unroll
+    for (int j = 0; j < NTN; ++j)
+#pragma unroll
+      for (int e = 0; e < MT * MT / 64; ++e) acc[i][j][e] = 0.f;
+
+  // K-steps as in gemm_tn_kernel: two per loop iteration (B stage = step
+  // parity), an odd count led by an all-zero step; steps outside the matrix
+  // read zeros and touch no memory.
+  const int nk = (int)((p.K + T::kstep - 1) / T::kstep);
+  const int pad = nk & 1;
+  const int nk2 = nk + pad;
+  const int Ki = (int)p.K;
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  struct StepScalars {
+    uint32_t kb;
+    int left;
+  };
+  auto step_scalars = [&](int t) {
+    const int k0 = (t - pad) * T::kstep;
+    const bool inside = (k0 >= 0) && (t < nk2);
+    const int rem = Ki - k0;
+    StepScalars u;
+    u.kb = inside ? (uint32_t)(k0 * T::es) : 0u;
+    u.left = !inside ? 0 : (rem >= T::kstep ? T::kstep : rem);
+    return u;
+  };
+  // One window's copies: B of step t + 2 and A of step t + 3.
+  struct Window {
+    __amdgpu_buffer_rsrc_t rb, ra;
+    lds_u8 *lb, *la;
+    uint32_t vb, va;     // lane offsets (unused with whole K-steps)
+  };
+  auto plan_b = [&](const StepScalars &u, int bstage, Window &w) {
+    w.rb = make_rsrc(Bb + u.kb, KF && u.left == 0 ? 0u : rec_b - u.kb);
+    w.lb = (lds_u8 *)smem + kBBase + bstage * kHalf + wave * 1024;
+    if constexpr (!KF) w.vb = kchunk < u.left ? voff_b : kOob;
+  };
+  auto plan_a = [&](const StepScalars &u, int astage, Window &w) {
+    w.ra = make_rsrc(Ab + u.kb, KF && u.left == 0 ? 0u : rec_a - u.kb);
+    w.la = (lds_u8 *)smem + astage * kHalf + wave * 1024;
+    if constexpr (!KF) w.va = kchunk < u.left ? voff_a : kOob;
+  };
+  // Copy d of a window: d < NTN is B's load d, else A's load d - NTN.
+  auto issue = [&](const Window &w, int d) {
+    if (d < NTN) {
+      const int q = d;
+      lds_copy16(w.rb, (lds_void_t *)(w.lb + q * 4096),
+                 KF ? cvb[q] : w.vb + (uint32_t)q * qs_b);
+    } else {
+      const int q = d - NTN;
+      lds_copy16(w.ra, (lds_void_t *)(w.la + q * 4096),
+                 KF ? cva[q] : w.va + (uint32_t)q * qs_a);
+    }
+  };
+  // Copies issued after the last of B's copies of step t + 1 and before step
+  // t's barrier: A's copies of step t + 2 (the same window, B's first).
+  constexpr int kRingVm = 8;
+  auto sync = [&]() {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kRingVm) & 0xF0FF);  // + lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // Slots as in gemm_tn_kernel; the window of step t starts at its barrier
+  // slot and spreads NTN + 8 copies over kWin slots, wrapping into step t + 1
+  // before that step's planning slots.
+  static_assert(MT == 16 && NTM == 8 && (NTN == 8 || NTN == 7), "8 x NTN tiles of 16 x 16");
+  constexpr int kQ = 8 * NTN, kBarQ = NTN, kSlots = T::subs * kQ;
+  constexpr int kBarSlot = (T::subs - 1) * kQ + kBarQ;
+  constexpr int kAfter = kSlots - kBarSlot;
+  constexpr int kCopies = NTN + 8;
+  // Window in slots, chosen by measurement: fp16 (4096^3, 8192^3) 96 slots of
+  // 16-cycle products against 48 / 64 / 80 / 104; fp8 (8192^3) 48 slots of
+  // 32-cycle ones against 24 / 32 / 40 / 50.
+  constexpr int kWin = (KIND == kF16) ? 96 : 48;
+  constexpr int kPlan = kBarSlot - 6;
+  static_assert(kWin >= kCopies && kWin <= kSlots && kPlan >= 0 && kWin - kAfter <= kPlan,
+                "copy window");
+  auto first_copy = [](int x) { return (x * kCopies + kWin - 1) / kWin; };
+  constexpr int kPost0 = (kAfter * kCopies + kWin - 1) / kWin;
+  constexpr int kPost = kPost0 < kCopies ? kPost0 : kCopies;  // window copies in its own step
+  static_assert(kPost >= NTN, "B's copies are issued in the window's own step");
+
+  frag_t fa[8], fx, fb[2][NTN];
+  Window wc, wn_;          // the previous window (its tail) and this step's
+  int sa = 0;              // A stage of the current step (t mod 3)
+  a_rebase(a_cur, 0);
+  if (nk2 > 0) {
+    // Steps 0 and 1 of A, step 0 of B, then window -1 (B of step 1, A of
+    // step 2) up to its part in its own step; wait for step 0 and publish it.
+    Window w0;
+    const StepScalars u0 = step_scalars(0), u1 = step_scalars(1), u2 = step_scalars(2);
+    plan_a(u0, 0, w0);
+    plan_b(u0, 0, w0);
+#pragma unroll
+    for (int d = 0; d < kCopies; ++d) issue(w0, (d + NTN) % kCopies);   // A_0, then B_0
+    plan_a(u1, 1, w0);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) issue(w0, NTN + d);                     // A_1
+    plan_b(u1, 1, wc);
+    plan_a(u2, 2, wc);
+#pragma unroll
+    for (int d = 0; d < kPost; ++d) issue(wc, d);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + kPost));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < NTN; ++j) fb[0][j] = frag_b(0, j, 0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) fa[g] = frag_a(a_cur, g, 0);
+  }
+#pragma unroll
+  for (int x = 0; x < kX; ++x) asm volatile("" : "+v"(a_cur[x]));
+  StepScalars ub, ua;
+  clock_mark(clock_ptr<Params>(), kClockLoop, wave);
+  for (int t0 = 0; t0 < nk2; t0 += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {            // step t = t0 + h: B stage h, A stage sa
+      const int t = t0 + h;
+      const int sa1 = sa == 2 ? 0 : sa + 1;  // A stage of step t + 1
+#pragma unroll
+      for (int s = 0; s < T::subs; ++s) {
+        const bool last = (s == T::subs - 1);
+        const int par = (h * T::subs + s) & 1;
+        const int s_n = last ? 0 : s + 1;
+        const int bsrc = last ? 1 - h : h;
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+#pragma unroll
+          for (int j = 0; j < NTN; ++j) {
+            const int q = NTN * g + j;
+            const int slot = kQ * s + q;
+            if (slot == kBarSlot) sync();
+            if (j == 0 && g >= 1) fa[g - 1] = frag_a(last ? a_nxt : a_cur, g - 1, s_n);
+            if (q == extra_slot<NTN>(0)) {
+              if (par == 0) fx = frag_a(last ? a_nxt : a_cur, 7, s_n);
+              else fa[7] = frag_a(last ? a_nxt : a_cur, 7, s_n);
+            }
+#pragma unroll
+            for (int jj = 0; jj < NTN; ++jj)
+              if (q == extra_slot<NTN>(jj + 1)) fb[par ^ 1][jj] = frag_b(bsrc, jj, s_n);
+            // Plan this step's window (B of t + 2 into B stage h, A of t + 3
+            // into A stage sa, both freed by this step's barrier) and the A
+            // offsets of step t + 1.
+            if (slot == kPlan) {
+              ub = step_scalars(t + 2);
+              ua = step_scalars(t + 3);
+            }
+            if (slot == kPlan + 1) plan_b(ub, h, wn_);
+            if (slot == kPlan + 2) plan_a(ua, sa, wn_);
+            if (slot == kPlan + 3) a_rebase(a_nxt, sa1);
+            if (slot < kWin - kAfter) {
+              const int x = slot + kAfter;
+              if (first_copy(x) < first_copy(x + 1)) issue(wc, first_copy(x));
+            } else if (slot >= kBarSlot && slot - kBarSlot < kWin) {
+              const int x = slot - kBarSlot;
+              if (first_copy(x) < first_copy(x + 1)) issue(wn_, first_copy(x));
+            }
+            if (g == 7 && par == 1) acc[g][j] = mma(fx, fb[par][j], acc[g][j]);
+            else acc[g][j] = mma(fa[g], fb[par][j], acc[g][j]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      wc = wn_;
+#pragma unroll
+      for (int x = 0; x < kX; ++x) a_cur[x] = a_nxt[x];
+      sa = sa1;
+    }
+  }
+  mfma_drain();
+#pragma unroll
+  for (int i = 0; i < NTM; ++i)
+#pragma unroll
+    for (int j = 0; j < NTN; ++j) asm volatile("" : "+a"(acc[i][j]));
+  clock_mark(clock_ptr<Params>(), kClockLoopEnd, wave);
+
+  __builtin_amdgcn_s_waitcnt(0);
+  const int elane = lane_id_fresh();
+  if (p.c_vec16_ok) {
+    __syncthreads();
+    store_c_lds<KIND, NTN>(p, Cb, acc,
+                           (__attribute__((address_space(3))) uint8_t *)smem + wave * 32768,
+                           m0 + wm * kWaveTile, n0 + wn * S::WN, elane);
+  } else {
+    store_c<KIND, NTN>(p, Cb, acc, m0 + wm * kWaveTile, n0 + wn * S::WN, elane);
+  }
+  clock_mark(clock_ptr<Params>(), kClockEnd, wave);
+}
+
+template __global__ void gemm_tn_ring_kernel<kF16, 8, true>(Params);
+template __global__ void gemm_tn_ring_kernel<kF16, 7, true>(Params);
+template __global__ void gemm_tn_ring_kernel<kF8, 8, true>(Params);
+template __global__ void gemm_tn_ring_kernel<kF8, 7, true>(Params);
+template __global__ void gemm_tn_ring_kernel<kF16, 8, false>(Params);
+template __global__ void gemm_tn_ring_kernel<kF16, 7, false>(Params);
+template __global__ void gemm_tn_ring_kernel<kF8, 8, false>(Params);
+template __global__ void gemm_tn_ring_kernel<kF8, 7, false>(Params);
+
 template __global__ void gemm_tn_kernel<kF16, 8, false, false, false>(Params);
 template __global__ void gemm_tn_kernel<kF16, 7, false, false, false>(Params);
 template __global__ void gemm_tn_kernel<kF8, 8, false, false, false>(Params);
@@ -1862,6 +2168,12 @@ __global__ __launch_bounds__(kPpThreads, 1) void gemm_tn_pp_kernel(Params p) {
 // Kernel configuration of a problem (the codes are the C ABI's
 // gemm_tn_config values).
 enum { kCfg256 = 0, kCfg224 = 1, kCfgMid = 2, kCfgSkinny = 3, kCfgPingPong = 4 };
+// DG_GEMM_RING = 0 in the environment makes TN calls take gemm_tn_kernel's two
+// [A | B] stages instead of gemm_tn_ring_kernel (measurement only).
+static bool ring_env() {
+  const char *r = getenv("DG_GEMM_RING");
+  return !(r && r[0] == '0');
+}
 struct Config {
   int kind;
 };
@@ -2012,13 +2324,18 @@ static int launch_cfg(const Problem &pr, Config cfg, hipStream_t stream) {
     hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
                        stream, p);
   else {
-    // Whole K-steps take the kernel with fixed copy offsets.
+    // The 3 + 2 ring; whole K-steps take the form with fixed copy offsets.
     const bool kf = pr.K % T::kstep == 0;
     typedef void (*kernel_t)(Params);
-    const kernel_t k = ntn == 8 ? (kf ? gemm_tn_kernel<KIND, 8, false, false, true>
-                                      : gemm_tn_kernel<KIND, 8, false, false, false>)
-                                : (kf ? gemm_tn_kernel<KIND, 7, false, false, true>
-                                      : gemm_tn_kernel<KIND, 7, false, false, false>);
+    const kernel_t k =
+        ring_env() ? (ntn == 8 ? (kf ? gemm_tn_ring_kernel<KIND, 8, true>
+                                     : gemm_tn_ring_kernel<KIND, 8, false>)
+                               : (kf ? gemm_tn_ring_kernel<KIND, 7, true>
+                                     : gemm_tn_ring_kernel<KIND, 7, false>))
+                   : ntn == 8 ? (kf ? gemm_tn_kernel<KIND, 8, false, false, true>
+                                    : gemm_tn_kernel<KIND, 8, false, false, false>)
+                              : (kf ? gemm_tn_kernel<KIND, 7, false, false, true>
+                                    : gemm_tn_kernel<KIND, 7, false, false, false>);
     hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   }
   return hipGetLastError() == hipSuccess ? DG_OK : DG_ERR_HIP;

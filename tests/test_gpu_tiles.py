@@ -48,6 +48,21 @@ def test_forced_tile_exact(force, tile, code, kind, M, N, K):
     assert_exact(kind, got, reference(kind, x, M, N, K))
 
 
+@pytest.mark.parametrize("tile", ["256", "224"])
+@pytest.mark.parametrize("kind,M,N,K", [("f16",) + s for s in SHAPES16[3:]] +
+                         [("f8",) + s for s in SHAPES8[3:]])
+def test_two_stage_tn_kernel_exact(monkeypatch, tile, kind, M, N, K):
+    """The TN calls' former 256-row kernel (two [A | B] LDS stages), kept for
+    measurement behind DG_GEMM_RING=0: same shapes, same bits as the oracle."""
+    monkeypatch.setenv("DG_GEMM_TILE", tile)
+    monkeypatch.setenv("DG_GEMM_RING", "0")
+    print("two-stage tn %s %s %dx%dx%d" % (tile, kind, M, N, K), flush=True)
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=M * 5 + N + K)
+    got, canary = run_gemm(kind, x, M, N, K)
+    assert canary
+    assert_exact(kind, got, reference(kind, x, M, N, K))
+
+
 @pytest.mark.parametrize("tile,code", FORCED)
 @pytest.mark.parametrize("kind", ["f16", "f8"])
 def test_forced_tile_padding_and_odd_ldc(force, tile, code, kind):

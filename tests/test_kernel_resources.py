@@ -22,10 +22,10 @@ def rows():
 
 def test_every_kernel_reported(rows):
     names = {r["kernel"] for r in rows}
-    for want in ("gemm_tn_kernel<0, 8, false, false, true>",
-                 "gemm_tn_kernel<1, 8, false, false, true>",
-                 "gemm_tn_kernel<0, 8, false, false, false>",
-                 "gemm_tn_kernel<1, 8, false, false, false>",
+    for want in ("gemm_tn_ring_kernel<0, 8, true>", "gemm_tn_ring_kernel<1, 8, true>",
+                 "gemm_tn_ring_kernel<0, 7, false>", "gemm_tn_ring_kernel<1, 7, false>",
+                 "gemm_tn_kernel<0, 8, false, false, true>",
+                 "gemm_tn_kernel<1, 8, true, false, false>",
                  "gemm_tn_skinny_kernel<0>", "gemm_tn_mid_kernel<0, false, false, false, 2>",
                  "gemm_tn_mid_kernel<0, false, false, false, 4>",
                  "gemm_tn_mid_kernel<1, false, false, true, 4>",
@@ -42,10 +42,13 @@ def test_no_scratch_anywhere(rows):
 
 
 def test_big_tiles_hold_accumulators_in_agprs(rows):
+    """256-row tiles: accumulators in AGPRs at one wave per SIMD; two [A | B]
+    stages (128 KiB), or the TN kernel's three A and two B strips (160 KiB)."""
     for r in rows:
-        if "gemm_tn_kernel<" in r["kernel"]:
+        if "gemm_tn_kernel<" in r["kernel"] or "gemm_tn_ring_kernel<" in r["kernel"]:
             assert int(r["AGPRs"]) >= 224 and r["Occupancy [waves/SIMD]"] == "1", r
-            assert int(r["LDS Size [bytes/block]"]) == 131072, r
+            lds = 163840 if "ring" in r["kernel"] else 131072
+            assert int(r["LDS Size [bytes/block]"]) == lds, r
 
 
 def test_mid_kernel_rings_fit_their_occupancy(rows):
