@@ -57,3 +57,46 @@ def test_ring_normal_data_matches_two_stage_kernel(monkeypatch, kind):
     two, canary = run_gemm(kind, x, M, N, K)
     assert canary
     assert np.array_equal(ring, two)
+
+
+def _draw(n=48, seed=4242):
+    """Seeded TN shapes with whole K-steps (the ring kernel's fixed-offset
+    form), ragged M and N, padded leading dimensions and ldc, the tile width
+    chosen or forced."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = "f16" if i % 2 == 0 else "f8"
+        vec = 8 if kind == "f16" else 16
+        big = rng.random() < 0.5
+        M = int(rng.integers(200, 3000)) if big else int(rng.integers(1, 900))
+        N = int(rng.integers(200, 3000)) if big else int(rng.integers(1, 900))
+        steps = int(rng.integers(3, 40))
+        while M * N * steps * KSTEP[kind] > 3e9:
+            steps = max(3, steps // 2)
+            if steps == 3:
+                break
+        out.append({"kind": kind, "M": M, "N": N, "K": steps * KSTEP[kind],
+                    "pad_a": int(rng.integers(0, 3)) * vec, "pad_b": int(rng.integers(0, 3)) * vec,
+                    "ldc_pad": int(rng.choice([0, 0, 1, 8])),
+                    "tile": rng.choice([None, None, "256", "224"]), "seed": 7000 + i})
+    return out
+
+
+RANDOM = _draw()
+
+
+@pytest.mark.parametrize("c", RANDOM, ids=["%s-%dx%dx%d-%s" % (c["kind"], c["M"], c["N"], c["K"],
+                                                             c["tile"] or "auto") for c in RANDOM])
+def test_ring_random_whole_steps_exact(monkeypatch, c):
+    monkeypatch.delenv("DG_GEMM_RING", raising=False)
+    monkeypatch.delenv("DG_GEMM_TILE", raising=False)
+    if c["tile"]:
+        monkeypatch.setenv("DG_GEMM_TILE", str(c["tile"]))
+    kind, M, N, K = c["kind"], c["M"], c["N"], c["K"]
+    print("ring random %s %dx%dx%d tile %s" % (kind, M, N, K, c["tile"]), flush=True)
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=c["seed"])
+    got, canary = run_gemm(kind, x, M, N, K, lda=K + c["pad_a"], ldb=K + c["pad_b"],
+                           ldc=M + c["ldc_pad"])
+    assert canary
+    assert_exact(kind, got, reference(kind, x, M, N, K))
