@@ -86,8 +86,10 @@ def kernel_name(w):
         per = (nk + splits - 1) // splits if nk else 0
         ranges = (nk + per - 1) // per if per else 0
         blocks = tiles128(M, N) * (ranges if split else batch)
-        return "gemm_tn_mid_kernel<%d, false, false, %s, %d>" % (
-            kind, "true" if split else "false", dg.mid_stages(blocks, per if split else nk))
+        # Whole K-steps (K a multiple of the K-step) take the fixed-offset form.
+        return "gemm_tn_mid_kernel<%d, false, false, %s, %d, %s>" % (
+            kind, "true" if split else "false", dg.mid_stages(blocks, per if split else nk),
+            "true" if K % kstep == 0 else "false")
 
     if layout != "TN":
         amn = "true" if layout[0] == "N" else "false"
@@ -95,7 +97,7 @@ def kernel_name(w):
         cfg_of = dg.f8_config if w.kind == "f8" else dg.f16_config
         if cfg_of(layout[0], layout[1], w.M, w.N, w.K) == 2:
             nk = (w.K + kstep - 1) // kstep
-            return "gemm_tn_mid_kernel<%d, %s, %s, false, %d>" % (
+            return "gemm_tn_mid_kernel<%d, %s, %s, false, %d, false>" % (
                 kind, amn, bmn, dg.mid_stages(tiles128(w.M, w.N), nk))
         return "gemm_tn_kernel<%d, 8, %s, %s, false>" % (kind, amn, bmn)
     fp8 = w.kind == "f8"

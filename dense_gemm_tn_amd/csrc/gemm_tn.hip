@@ -157,6 +157,18 @@ __device__ __forceinline__ float4_t_v mma(const int8_t_v &a, const int8_t_v &b, 
 __device__ __forceinline__ void mfma_drain() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
+// The products tied in place in AGPRs but with no memory clobber, so the
+// compiler still places the LDS reads between them (the 128 x 128 kernel's
+// fixed-offset form, where the builtin's accumulators get renamed across the
+// loop's back edge).  The same wait states apply before other reads.
+__device__ __forceinline__ float4_t_v mma_t(const half8_t &a, const half8_t &b, float4_t_v c) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  return c;
+}
+__device__ __forceinline__ float4_t_v mma_t(const int8_t_v &a, const int8_t_v &b, float4_t_v c) {
+  asm volatile("v_mfma_f32_16x16x128_f8f6f4 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  return c;
+}
 // The same products with the accumulators left to the compiler (the 128 x 128
 // and skinny-K kernels, whose few accumulators need no pinning).
 __device__ __forceinline__ float4_t_v mma_c(const half8_t &a, const half8_t &b,
@@ -1678,10 +1690,16 @@ __device__ __forceinline__ void mid_copy(const uint8_t *base, int64_t ld_b, int6
 // covers the wait: copies run three steps ahead, so a step whose operands
 // come from HBM (a round trip several times the 512 MFMA cycles of a step)
 // does not stall the products.
-template <int KIND, bool AMN, bool BMN, bool SPLIT = false, int STAGES = 2>
+// KF (TN only): this block's K range is a whole number of K-steps, so every
+// step's copies use the same lane offsets (formed once), steps past the range
+// get an empty descriptor instead of out-of-range lane offsets, and every step
+// issues its copies unconditionally: the loop's copy addressing and its waits
+// then take no vector ALU instructions and no branches.
+template <int KIND, bool AMN, bool BMN, bool SPLIT = false, int STAGES = 2, bool KF = false>
 __global__ __launch_bounds__(kThreads, STAGES == 2 ? 2 : 1) void gemm_tn_mid_kernel(Params p) {
   typedef Traits<KIND> T;
   static_assert(!SPLIT || (!AMN && !BMN), "split-K partials are TN only");
+  static_assert(!KF || (!AMN && !BMN), "whole K-steps: TN only");
   static_assert(STAGES == 2 || STAGES == 4, "a ring of 2 or 4 stages");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * 2 * kMidStrip];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -1749,6 +1767,31 @@ __global__ __launch_bounds__(kThreads, STAGES == 2 ? 2 : 1) void gemm_tn_mid_ker
     mid_copy<KIND, BMN, AMN || BMN>(Bb, p.ldb_b, Kx, rec_b, voff_b, qs_b, kchunk, opb, t,
                                     st + kMidStrip);
   };
+  // Whole K-steps: fixed lane offsets (the empty asm statements keep them in
+  // registers), one descriptor pair per step, empty past the range.
+  uint32_t cva[4], cvb[4];
+  if constexpr (KF) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      cva[q] = voff_a + (uint32_t)q * qs_a;
+      cvb[q] = voff_b + (uint32_t)q * qs_b;
+      asm volatile("" : "+v"(cva[q]));
+      asm volatile("" : "+v"(cvb[q]));
+    }
+  }
+  const int nk32 = (int)nk;
+  auto copy_step_kf = [&](int t) {
+    const bool inside = t < nk32;
+    const uint32_t kb = inside ? (uint32_t)t * (uint32_t)(T::kstep * T::es) : 0u;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Ab + kb, inside ? rec_a - kb : 0u);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bb + kb, inside ? rec_b - kb : 0u);
+    lds_u8 *st = (lds_u8 *)smem + (t & (STAGES - 1)) * 2 * kMidStrip + wave * 1024;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lds_copy16(ra, (lds_void_t *)(st + q * 4096), cva[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      lds_copy16(rb, (lds_void_t *)(st + kMidStrip + q * 4096), cvb[q]);
+  };
 
   // Fragments.  K-major: lane l reads row l % 16 of a 16-row tile; fp16 takes
   // chunk 4s + g of sub-step s, fp8 chunks g and g + 4 (g = l / 16), as in the
@@ -1798,9 +1841,14 @@ __global__ __launch_bounds__(kThreads, STAGES == 2 ? 2 : 1) void gemm_tn_mid_ker
 
   // Steps 0 .. STAGES - 2 ahead of the loop; step t + STAGES - 1 goes into the
   // stage step t - 1 used, right after the barrier that ends its reads.
+  if constexpr (KF) {
 #pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t)
-    if (t < nk) copy_step(t);
+    for (int t = 0; t < STAGES - 1; ++t) copy_step_kf(t);
+  } else {
+#pragma unroll
+    for (int t = 0; t < STAGES - 1; ++t)
+      if (t < nk) copy_step(t);
+  }
   for (int64_t t = 0; t < nk; ++t) {
     // This wave's copies of step t have landed (loads complete in order; the
     // copies of the at most STAGES - 2 steps issued after it may still run,
@@ -1808,7 +1856,9 @@ __global__ __launch_bounds__(kThreads, STAGES == 2 ? 2 : 1) void gemm_tn_mid_ker
     // are done; after the barrier every wave's are.  A plain barrier:
     // __syncthreads() would also wait for the later steps' copies.
     const int64_t later = nk - 1 - t;
-    if (STAGES == 2 || later <= 0)
+    if constexpr (KF)   // every step issued its eight copies, past the range too
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 * (STAGES - 2)) & 0xF0FF);
+    else if (STAGES == 2 || later <= 0)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & 0xF0FF);
     else if (later == 1)
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(8) & 0xF0FF);
@@ -1817,7 +1867,10 @@ __global__ __launch_bounds__(kThreads, STAGES == 2 ? 2 : 1) void gemm_tn_mid_ker
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (t + STAGES - 1 < nk) copy_step(t + STAGES - 1);
+    if constexpr (KF)
+      copy_step_kf((int)t + STAGES - 1);
+    else if (t + STAGES - 1 < nk)
+      copy_step(t + STAGES - 1);
     lds_cptr st = (lds_cptr)smem + (t & (STAGES - 1)) * 2 * kMidStrip;
 #pragma unroll
     for (int s = 0; s < T::subs; ++s) {
@@ -1836,10 +1889,22 @@ __global__ __launch_bounds__(kThreads, STAGES == 2 ? 2 : 1) void gemm_tn_mid_ker
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mma_c(fa[i], fb[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = KF ? mma_t(fa[i], fb[j], acc[i][j]) : mma_c(fa[i], fb[j], acc[i][j]);
     }
   }
 
+  // The copies issued past the range (KF) still write the LDS: they land
+  // before the block may end.  The products' wait states pass before the
+  // epilogue reads the accumulators, every one tied to that wait.
+  if constexpr (KF) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    mfma_drain();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+  }
   // Lane (rl, grp) of tile (i, j) holds C rows 16i + 4 grp .. +3 of column
   // 16j + rl of the wave's 64 x 64 block.
   const int64_t mb = m0 + wm * 64 + 4 * grp, nb = n0 + wn * 64 + rl;
@@ -2317,12 +2382,18 @@ static int launch_cfg(const Problem &pr, Config cfg, hipStream_t stream) {
   else if (pp)
     hipLaunchKernelGGL(gemm_tn_pp_kernel<KIND>, dim3((unsigned)blocks), dim3(kPpThreads), 0,
                        stream, p);
-  else if (mid && mid_deep_ring(blocks, (pr.K + T::kstep - 1) / T::kstep))
-    hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false, false, 4>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, p);
-  else if (mid)
-    hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false>), dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, p);
+  else if (mid) {
+    // Whole K-steps take the form with fixed copy offsets.
+    typedef void (*kernel_t)(Params);
+    const bool kf = pr.K % T::kstep == 0;
+    const kernel_t k =
+        mid_deep_ring(blocks, (pr.K + T::kstep - 1) / T::kstep)
+            ? (kf ? gemm_tn_mid_kernel<KIND, false, false, false, 4, true>
+                  : gemm_tn_mid_kernel<KIND, false, false, false, 4, false>)
+            : (kf ? gemm_tn_mid_kernel<KIND, false, false, false, 2, true>
+                  : gemm_tn_mid_kernel<KIND, false, false, false, 2, false>);
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  }
   else {
     // The 3 + 2 ring; whole K-steps take the form with fixed copy offsets.
     const bool kf = pr.K % T::kstep == 0;
@@ -2483,12 +2554,18 @@ static int launch_splitk(const Problem &pr, int64_t splits, void *ws, int64_t ws
   p.W = (float *)ws;
   p.ldw = ldw;
   p.clk = clock_slot(blocks);
-  if (mid_deep_ring(blocks, per))
-    hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false, true, 4>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm_tn_mid_kernel<KIND, false, false, true>), dim3((unsigned)blocks),
-                       dim3(kThreads), 0, stream, p);
+  {
+    // Whole K-steps in every range (K a multiple of the step) take the form
+    // with fixed copy offsets.
+    typedef void (*kernel_t)(Params);
+    const bool kf = pr.K % T::kstep == 0;
+    const kernel_t k = mid_deep_ring(blocks, per)
+                           ? (kf ? gemm_tn_mid_kernel<KIND, false, false, true, 4, true>
+                                 : gemm_tn_mid_kernel<KIND, false, false, true, 4, false>)
+                           : (kf ? gemm_tn_mid_kernel<KIND, false, false, true, 2, true>
+                                 : gemm_tn_mid_kernel<KIND, false, false, true, 2, false>);
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  }
   if (hipGetLastError() != hipSuccess) return DG_ERR_HIP;
   p.clk = nullptr;
   hipLaunchKernelGGL(gemm_splitk_reduce_kernel<KIND>, dim3((unsigned)rblocks), dim3(kThreads), 0,

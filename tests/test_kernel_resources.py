@@ -26,9 +26,10 @@ def test_every_kernel_reported(rows):
                  "gemm_tn_ring_kernel<0, 7, false>", "gemm_tn_ring_kernel<1, 7, false>",
                  "gemm_tn_kernel<0, 8, false, false, true>",
                  "gemm_tn_kernel<1, 8, true, false, false>",
-                 "gemm_tn_skinny_kernel<0>", "gemm_tn_mid_kernel<0, false, false, false, 2>",
-                 "gemm_tn_mid_kernel<0, false, false, false, 4>",
-                 "gemm_tn_mid_kernel<1, false, false, true, 4>",
+                 "gemm_tn_skinny_kernel<0>", "gemm_tn_mid_kernel<0, false, false, false, 2, false>",
+                 "gemm_tn_mid_kernel<0, false, false, false, 4, true>",
+                 "gemm_tn_mid_kernel<1, false, false, true, 4, true>",
+                 "gemm_tn_mid_kernel<1, false, false, true, 2, true>",
                  "gemm_splitk_reduce_kernel<0>", "attention_fwd_kernel"):
         assert any(want in n for n in names), want
     assert len(rows) >= 31
@@ -53,11 +54,12 @@ def test_big_tiles_hold_accumulators_in_agprs(rows):
 
 def test_mid_kernel_rings_fit_their_occupancy(rows):
     """The 128 x 128 kernel: two-stage ring (64 KiB) at two blocks per CU, the
-    four-stage ring (128 KiB) for grids of one block per CU."""
+    four-stage ring (128 KiB) for grids of one block per CU; both in the
+    general form and in the fixed-offset form for whole K-steps."""
     seen = set()
     for r in rows:
         if "gemm_tn_mid_kernel<" in r["kernel"]:
-            stages = r["kernel"].split(",")[-1].split(">")[0].strip()
+            stages = r["kernel"].split("<")[1].split(",")[4].strip()
             lds = int(r["LDS Size [bytes/block]"])
             assert (stages, lds) in (("2", 65536), ("4", 131072)), r
             if stages == "2":
