@@ -110,9 +110,14 @@ def test_selector_sends_2048_cube_to_128_tiles(monkeypatch):
 # with at least eight K-steps): step counts at and just past the floor, so the
 # loop's last three steps take each of its waits (no, one, two later steps in
 # flight), with a K tail inside the last step; and one count below the floor
-# (the two-stage ring).  fp16 K-steps are 64 elements, fp8 128.
+# (the two-stage ring).  fp16 K-steps are 64 elements, fp8 128.  The same
+# counts with whole K-steps (no tail) run the fixed-offset form of both rings,
+# whose copies past the last step read an empty descriptor; 1 and 2 steps put
+# those copies in the prologue.
 RING = [("f16", 300, 260, 64 * n - 8) for n in (7, 8, 9, 10, 11, 33)] + \
-       [("f8", 257, 300, 128 * n - 16) for n in (7, 8, 9, 10, 21)]
+       [("f8", 257, 300, 128 * n - 16) for n in (7, 8, 9, 10, 21)] + \
+       [("f16", 300, 260, 64 * n) for n in (1, 2, 7, 8, 9, 10, 33)] + \
+       [("f8", 257, 300, 128 * n) for n in (1, 7, 8, 9, 10)]
 
 
 @pytest.mark.parametrize("kind,M,N,K", RING)
