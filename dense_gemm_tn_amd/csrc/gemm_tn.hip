@@ -55,6 +55,8 @@
 //   LDS ring, for grids the 256-wide tiles cannot fill; on grids of at most
 //   one block per CU (and at least eight K-steps) one block per CU with a
 //   four-stage ring, whose copies run three steps ahead of the products.
+//   With whole K-steps (TN) both rings take a fixed-offset form like the
+//   256-row kernel's, with the products accumulating in place in AGPRs.
 //
 // Split-K (gemm_f16_tn_splitk, gemm_f8_tn_splitk): for few output tiles and a
 //   long K, the 128 x 128 kernel with SPLIT multiplies one K range per block
