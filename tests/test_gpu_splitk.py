@@ -174,11 +174,17 @@ def test_splitk_chooser_doubled_configuration(kind, M, N, K):
 
 # Split ranges of 8 to 11 K-steps on a grid of one block per CU (the partial
 # kernel's four-stage ring), the last range short, and 7 (two-stage ring).
+# 57 K-steps in 8 splits: seven ranges of 8 and a last range of one step, whose
+# block issues copies three steps past its range before its only step (whole
+# K-steps: the fixed-offset form; with a K tail: the general form).
 @pytest.mark.parametrize("kind,M,N,K,splits", [("f16", 300, 200, 64 * 8 * 6 - 40, 6),
                                                ("f16", 256, 256, 64 * 9 * 5, 5),
                                                ("f16", 130, 250, 64 * 10 * 4 + 64 * 3, 5),
                                                ("f16", 256, 128, 64 * 7 * 8, 8),
-                                               ("f8", 256, 200, 128 * 11 * 3 - 16, 3)])
+                                               ("f8", 256, 200, 128 * 11 * 3 - 16, 3),
+                                               ("f16", 256, 256, 64 * 57, 8),
+                                               ("f16", 250, 256, 64 * 57 - 24, 8),
+                                               ("f8", 256, 200, 128 * 57, 8)])
 def test_splitk_ring_ranges_exact(kind, M, N, K, splits):
     print("splitk ring %s %dx%dx%d splits %d" % (kind, M, N, K, splits), flush=True)
     x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=M + N + K)
