@@ -16,7 +16,8 @@ import pytest
 import dense_gemm_tn_amd as dg
 import oracle
 from dense_gemm_tn_amd import inputs
-from test_gpu_parity import assert_exact, normwise_error, reference, run_gemm, F16_TOL
+from test_gpu_parity import (BF16_TOL, F16_TOL, assert_exact, normwise_error, reference,
+                             run_gemm)
 
 pytestmark = pytest.mark.gpu
 
@@ -83,6 +84,31 @@ def test_forced_tile_normal_data(force, tile):
     got, canary = run_gemm("f16", x, M, N, K)
     assert canary
     assert normwise_error("f16", got, reference("f16", x, M, N, K)) <= F16_TOL
+
+
+# The 128 x 128 kernel on N(0,1) data, every element against the oracle: both
+# rings (7 K-steps: two stages; 12 or more on a 20-block grid: four), whole
+# K-steps (the fixed-offset form) and K tails (the general form), fp16 and
+# fp8; a second run must give the same bits.
+MID_NORMAL = [("f16", 520, 390, 64 * 7), ("f16", 520, 390, 64 * 24),
+              ("f16", 520, 390, 64 * 24 - 40), ("f8", 520, 390, 128 * 5),
+              ("f8", 520, 390, 128 * 12), ("f8", 520, 390, 128 * 12 - 16)]
+
+
+@pytest.mark.parametrize("kind,M,N,K", MID_NORMAL)
+def test_mid_kernel_normal_data_both_forms(force, kind, M, N, K):
+    force("128")
+    ks = 64 if kind == "f16" else 128
+    nk = -(-K // ks)
+    print("mid normal %s %dx%dx%d (%d steps, ring %d)" % (kind, M, N, K, nk,
+          dg.mid_stages(-(-M // 128) * -(-N // 128), nk)), flush=True)
+    x = inputs.make_shape(kind, M, N, K, dist="normal", seed=M + K)
+    got, canary = run_gemm(kind, x, M, N, K)
+    assert canary
+    tol = F16_TOL if kind == "f16" else BF16_TOL
+    assert normwise_error(kind, got, reference(kind, x, M, N, K)) <= tol
+    again, _ = run_gemm(kind, x, M, N, K)
+    assert np.array_equal(got, again)
 
 
 def test_selector_sends_2048_cube_to_128_tiles(monkeypatch):
