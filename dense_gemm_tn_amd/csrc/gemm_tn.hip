@@ -2610,10 +2610,16 @@ static void *scratch_ptr() {
 // block per CU (never a second round), doubled to two blocks per CU when the
 // one-block-per-CU ranges are 4 * kSplitMinSteps K-steps or longer (so the
 // doubled ranges keep at least 2 * kSplitMinSteps; the second block hides the
-// first one's waits), each split keeping at least kSplitMinSteps K-steps; 1
-// when the tiles alone fill half the CUs or K is short.  (Measured on 512^2 x
-// 32768, 256^2 x 65536, 1024^2 x 16384, 1024 x 512 x 16384 and 768^2 x 8192:
-// within 3 % of the best count of a sweep.)
+// first one's waits), each split keeping at least kSplitMinSteps K-steps.
+// (Measured on 512^2 x 32768, 256^2 x 65536, 1024^2 x 16384, 1024 x 512 x
+// 16384 and 768^2 x 8192: within 3 % of the best count of a sweep.)  Grids of
+// more than half and fewer than all CUs' worth of tiles leave CUs idle
+// unsplit, and no split count spreads them evenly: they take the count that
+// fits two blocks per CU in one round when the busiest CU's block-steps drop
+// to at most 0.8 of the unsplit K-steps, else 1 (measured: 1536^2 x 4096,
+// 144 tiles, S = 3 33.4 vs 37.5 us; 1536^2 x 8192 53.4 vs 74.7; 1792^2 x 4096,
+// 196 tiles, stays unsplit: S = 2 40.1 vs 37.8).  1 for a full grid or a
+// short K.
 constexpr int64_t kSplitMinSteps = 16;
 static int64_t choose_splits(int es, int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 1;
@@ -2621,7 +2627,14 @@ static int64_t choose_splits(int es, int64_t M, int64_t N, int64_t K) {
   const int64_t nk = (K + kstep - 1) / kstep;
   const int64_t tiles = ((M + kMidTile - 1) / kMidTile) * ((N + kMidTile - 1) / kMidTile);
   const int64_t cus = cu_count();
-  if (2 * tiles >= cus) return 1;
+  if (tiles >= cus) return 1;
+  if (2 * tiles > cus) {
+    int64_t s2 = 2 * cus / tiles;
+    if (s2 > nk / kSplitMinSteps) s2 = nk / kSplitMinSteps;
+    if (s2 < 2) return 1;
+    const int64_t busiest = ((tiles * s2 + cus - 1) / cus) * ((nk + s2 - 1) / s2);
+    return 5 * busiest <= 4 * nk ? s2 : 1;
+  }
   int64_t s = cus / tiles;
   if (s >= 1 && nk / s >= 4 * kSplitMinSteps) s *= 2;
   const int64_t by_k = nk / kSplitMinSteps;

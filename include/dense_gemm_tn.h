@@ -429,8 +429,11 @@ int64_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t splits);
  * splits of the 128 x 128 tiles as fit one block per compute unit, doubled to
  * two per compute unit when those one-per-unit ranges are 64 K-steps or longer
  * (the doubled ranges then keep at least 32), each keeping at least 16 K-steps
- * and at most 64 splits; 1 when the tiles alone fill half the compute units.
- * -1 for negative sizes. */
+ * and at most 64 splits.  Between half and all of the compute units' worth of
+ * tiles: the count that fits two blocks per unit in one round, when the
+ * busiest unit's block-steps drop to at most 0.8 of the unsplit K-steps, else
+ * 1.  1 for a grid of at least one tile per compute unit.  -1 for negative
+ * sizes. */
 int64_t gemm_splitk_choose(int fp8, int64_t M, int64_t N, int64_t K);
 
 #ifdef __cplusplus

@@ -387,6 +387,19 @@ def test_splitk_choose_doubling_rule():
     assert dg.splitk_choose(256, 256, 65536) == 64
 
 
+def test_splitk_choose_medium_grids():
+    # Between half and all of 256 CUs' worth of 128 x 128 tiles: two blocks per
+    # CU in one round when that cuts the busiest CU's block-steps to <= 0.8 of
+    # the unsplit K-steps.
+    assert dg.splitk_choose(2048, 1024, 4096) == 2              # 128 tiles: one block per CU
+    assert dg.splitk_choose(1536, 1536, 4096) == 3              # 144 tiles: 2 x 22 <= 0.8 x 64
+    assert dg.splitk_choose(1536, 1536, 8192) == 3
+    assert dg.splitk_choose(1536, 1536, 8192, fp8=True) == 3    # 64 fp8 steps
+    assert dg.splitk_choose(1792, 1792, 4096) == 1              # 196 tiles: S = 2 gives 2 x 32
+    assert dg.splitk_choose(1536, 1536, 2048) == 1              # 32 steps: S <= 2, no gain
+    assert dg.splitk_choose(2048, 2048, 4096) == 1              # 256 tiles: full grid
+
+
 # ------------------------------------------------- tensor helpers (no launches)
 
 torch = pytest.importorskip("torch")

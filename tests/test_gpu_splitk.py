@@ -172,6 +172,29 @@ def test_splitk_chooser_doubled_configuration(kind, M, N, K):
     assert np.array_equal(g, want), "%d mismatches" % int((g != want).sum())
 
 
+@pytest.mark.parametrize("kind,M,N,K", [("f16", 1536, 1536, 4096), ("f16", 1530, 1500, 4096 - 24),
+                                        ("f16", 2048, 1024, 4096), ("f8", 1536, 1536, 8192)])
+def test_splitk_chooser_medium_grid(kind, M, N, K):
+    """The chooser's medium-grid branch (more than half of the CUs' worth of
+    128 x 128 tiles, fewer than all): the count it suggests, two blocks per CU
+    in one round (or one per CU at exactly half), +-1 data exact against the
+    oracle, canaries around C and past the workspace."""
+    splits = dg.splitk_choose(M, N, K, fp8=(kind == "f8"))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tiles = -(-M // 128) * -(-N // 128)
+    print("splitk medium grid %s %dx%dx%d tiles %d splits %d" % (kind, M, N, K, tiles, splits),
+          flush=True)
+    if cus == 256:
+        assert splits == (2 if 2 * tiles == cus else 3)
+    x = inputs.make_shape(kind, M, N, K, dist="pm1", seed=29)
+    got, canary, ws_ok, _ = run(kind, x, M, N, K, splits)
+    assert canary and ws_ok
+    ref = oracle.gemm_tn(x["A"], x["B"], fmt_in(kind), M, N, K)
+    want = oracle.decode(oracle.encode(ref, fmt_out(kind)), fmt_out(kind))
+    g = oracle.decode(got, fmt_out(kind))
+    assert np.array_equal(g, want), "%d mismatches" % int((g != want).sum())
+
+
 # Split ranges of 8 to 11 K-steps on a grid of one block per CU (the partial
 # kernel's four-stage ring), the last range short, and 7 (two-stage ring).
 # 57 K-steps in 8 splits: seven ranges of 8 and a last range of one step, whose
