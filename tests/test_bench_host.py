@@ -77,6 +77,33 @@ def test_every_workload_names_its_kernel(name):
     assert bench.kernel_name(inputs.WORKLOADS[name])
 
 
+# The instantiation each workload's launch dispatches on a 256-CU part (the
+# library's selector, ring depth and whole-K-step choice), as the kernel traces
+# under profiles/ recorded it; every one is a kernel the build compiles.
+DISPATCHED = {
+    "f16_4096": "gemm_tn_ring_kernel<0, 8, true>",
+    "f8_8192": "gemm_tn_ring_kernel<1, 8, true>",
+    "f16_1920x13900x4096": "gemm_tn_ring_kernel<0, 7, true>",
+    "qkt_64x4096x4096x128": "gemm_tn_skinny_kernel<0>",
+    "f16_256_pm1": "gemm_tn_mid_kernel<0, false, false, false, 2, true>",
+    "f16_2048": "gemm_tn_mid_kernel<0, false, false, false, 4, true>",
+    "f16_512x512x32768": "gemm_tn_mid_kernel<0, false, false, false, 4, true>",
+    "f16_512x512x32768_splitk": "gemm_tn_mid_kernel<0, false, false, true, 4, true>",
+    "f16_nn_4096": "gemm_tn_kernel<0, 8, true, false, false>",
+    "f8_nt_8192": "gemm_tn_kernel<1, 8, true, true, false>",
+}
+
+
+@pytest.mark.parametrize("name", sorted(DISPATCHED))
+def test_kernel_names_match_dispatch(name):
+    import os
+
+    assert bench.kernel_name(inputs.WORKLOADS[name]) == DISPATCHED[name]
+    report = open(os.path.join(os.path.dirname(bench.__file__), "profiles",
+                               "kernel_resources.md")).read()
+    assert "dg::%s(dg::Params)" % DISPATCHED[name] in report
+
+
 def test_default_list_starts_with_the_five_configurations():
     five = ("f16_4096", "f8_8192", "f16_256_pm1", "f16_1920x13900x4096", "qkt_64x4096x4096x128")
     assert bench.DEFAULT_WORKLOADS[:5] == five
